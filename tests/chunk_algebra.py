@@ -1,0 +1,143 @@
+"""Chunked (UT/WY) form of the gated delta rule, evaluated on the CPU.
+
+Test helper, not the oracle: it states the chunk algebra the GPU kernels
+implement so that it can be checked against the sequential oracle to 1e-12,
+and it emulates the rounding of candidate MFMA operand plans.
+
+Within a chunk of C tokens entering with state S0 (dv x dk), with raw q, k
+rows, rk_i = 1/sqrt(|k_i|^2 + eps) (1 without L2 norm), rq likewise,
+gamma = inclusive cumsum of g over the chunk and b = exp(gamma):
+    L_ij  = beta_i exp(gamma_i - gamma_j) rk_i rk_j (k_i . k_j)     j < i
+    T     = (I + L)^-1                         (forward substitution)
+    Tb    = T diag(beta)
+    X     = V - diag(b rk) K S0^T              (error against the entering state)
+    U     = Tb X                               (the per-token delta-rule writes)
+    P_ij  = scale exp(gamma_i - gamma_j) rq_i rk_j (q_i . k_j)       j <= i
+    O     = scale diag(b rq) Q S0^T + P U
+    S_C   = b_C S0 + U^T diag(exp(gamma_C - gamma) rk) K
+U solves u_i = beta_i (v_i - a_i S_{i-1} k^_i) token by token, which is the
+delta rule written with the decayed entering state.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _round_f32(x):
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+
+
+def _bf16(x):
+    x = np.asarray(x, np.float64).astype(np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    bias = np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return ((u + bias) & np.uint64(0xFFFF0000)).astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def split_hi_lo(x):
+    """fp32 value -> (hi, lo) bf16 pair with hi + lo ~ x to ~2^-17 relative."""
+    x = _round_f32(x)
+    hi = _bf16(x)
+    lo = _bf16(x - hi)
+    return hi, lo
+
+
+class Plan:
+    """How each contraction's operands are represented.
+
+    exact : float64 throughout (the algebra check)
+    f32   : fp32 operands and fp32 rounding of stored intermediates
+    bf16x3: raw bf16 q/k/v single, derived operands as bf16 hi+lo pairs
+            (hi*hi + hi*lo + lo*hi for derived x derived, hi*raw + lo*raw for
+            derived x raw); fp32 stored intermediates and fp32 state
+    bf16  : derived operands rounded to a single bf16
+    """
+
+    def __init__(self, name: str):
+        assert name in ("exact", "f32", "bf16x3", "bf16")
+        self.name = name
+
+    def store(self, x):
+        return x if self.name == "exact" else _round_f32(x)
+
+    def mm(self, a, b, a_derived: bool, b_derived: bool, subscripts: str):
+        e = lambda x, y: np.einsum(subscripts, x, y)
+        if self.name in ("exact", "f32"):
+            return self.store(e(a, b))
+        if self.name == "bf16":
+            a1 = _bf16(a) if a_derived else a
+            b1 = _bf16(b) if b_derived else b
+            return _round_f32(e(a1, b1))
+        ah, al = split_hi_lo(a) if a_derived else (a, None)
+        bh, bl = split_hi_lo(b) if b_derived else (b, None)
+        r = e(ah, bh)
+        if bl is not None:
+            r = r + e(ah, bl)
+        if al is not None:
+            r = r + e(al, bh)
+        return _round_f32(r)
+
+
+def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_state=None,
+                             cu_seqlens=None, use_qk_l2norm=True, l2_eps=1e-6,
+                             plan: str = "exact"):
+    """Same contract as the oracle's gated_delta_rule, evaluated chunk by chunk.
+    Chunks restart at every sequence start; the last chunk may be partial."""
+    P = Plan(plan)
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    g = np.asarray(g, np.float64)
+    beta = np.asarray(beta, np.float64)
+    t_total, hqk, dk = q.shape
+    hv, dv = v.shape[1:]
+    grp = hv // hqk
+    cu = np.array([0, t_total]) if cu_seqlens is None else np.asarray(cu_seqlens, np.int64)
+    n = len(cu) - 1
+    S0 = np.zeros((n, hv, dv, dk)) if initial_state is None else np.asarray(initial_state, np.float64)
+    o = np.zeros((t_total, hv, dv))
+    final = np.zeros((n, hv, dv, dk))
+    hq = np.arange(hv) // grp
+    for s in range(n):
+        S = P.store(S0[s].copy())                               # [Hv, dv, dk]
+        for c0 in range(cu[s], cu[s + 1], chunk):
+            c1 = min(c0 + chunk, cu[s + 1])
+            C = c1 - c0
+            K = k[c0:c1][:, hq].transpose(1, 0, 2)              # [Hv, C, dk] raw
+            Q = q[c0:c1][:, hq].transpose(1, 0, 2)
+            V = v[c0:c1].transpose(1, 0, 2)                     # [Hv, C, dv]
+            bt = beta[c0:c1].T                                  # [Hv, C]
+            if use_qk_l2norm:
+                rk = 1.0 / np.sqrt(np.sum(K * K, -1) + l2_eps)
+                rq = 1.0 / np.sqrt(np.sum(Q * Q, -1) + l2_eps)
+            else:
+                rk = np.ones(K.shape[:2])
+                rq = np.ones(Q.shape[:2])
+            gam = np.cumsum(g[c0:c1].T, axis=1)                 # [Hv, C]
+            b = np.exp(gam)
+            diff = gam[:, :, None] - gam[:, None, :]
+            strict = np.tril(np.ones((C, C), bool), -1)
+            incl = np.tril(np.ones((C, C), bool), 0)
+            gam_s = np.where(strict, np.exp(np.where(strict, diff, 0.0)), 0.0)
+            gam_i = np.where(incl, np.exp(np.where(incl, diff, 0.0)), 0.0)
+            GK = np.einsum("hid,hjd->hij", K, K)                # raw x raw, exact products
+            GQ = np.einsum("hid,hjd->hij", Q, K)
+            L = P.store(bt[:, :, None] * gam_s * rk[:, :, None] * rk[:, None, :] * GK)
+            T = np.zeros_like(L)
+            eye = np.eye(C)
+            for i in range(C):                                  # forward substitution
+                T[:, i] = eye[i] - np.einsum("hj,hjc->hc", L[:, i, :i], T[:, :i])
+            T = P.store(T)
+            Tb = P.store(T * bt[:, None, :])
+            Pm = P.store(scale * gam_i * rq[:, :, None] * rk[:, None, :] * GQ)
+            KS = P.mm(K, S, False, True, "hcd,hvd->hcv")        # K S^T  [Hv, C, dv]
+            QS = P.mm(Q, S, False, True, "hcd,hvd->hcv")
+            X = P.store(V - (b * rk)[:, :, None] * KS)
+            U = P.mm(Tb, X, True, True, "hij,hjv->hiv")
+            O = scale * (b * rq)[:, :, None] * QS + P.mm(Pm, U, True, True, "hij,hjv->hiv")
+            o[c0:c1] = O.transpose(1, 0, 2)
+            dec = np.exp(gam[:, -1:] - gam) * rk                # [Hv, C]
+            Ud = P.store(U * dec[:, :, None])
+            S = P.store(b[:, -1][:, None, None] * S + P.mm(Ud, K, True, False, "hcv,hcd->hvd"))
+        final[s] = S
+    return o, final

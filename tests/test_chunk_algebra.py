@@ -1,0 +1,48 @@
+"""The chunked (UT/WY) algebra the GPU kernels implement equals the
+sequential oracle (invariant: chunked form == sequential recurrence)."""
+import numpy as np
+import pytest
+
+from chunk_algebra import chunked_gated_delta_rule
+from oracle import gdn_ref as R
+
+
+def _case(rng, lengths, hqk=2, hv=4, dk=8, dv=6, strong_decay=True):
+    T = int(sum(lengths))
+    q = rng.standard_normal((T, hqk, dk))
+    k = rng.standard_normal((T, hqk, dk))
+    v = rng.standard_normal((T, hv, dv))
+    if strong_decay:   # model-like: g = -exp(A) softplus(n), reaching about -50
+        a = rng.uniform(0, np.log(16), hv)
+        g = -np.exp(a)[None] * np.logaddexp(0, rng.standard_normal((T, hv)))
+    else:
+        g = -rng.uniform(0.0, 0.1, (T, hv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((T, hv))))
+    S0 = rng.standard_normal((len(lengths), hv, dv, dk)) * 0.5
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    return q, k, v, g, beta, S0, cu
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 16, 64, 200])
+@pytest.mark.parametrize("strong", [True, False])
+def test_chunked_equals_sequential(chunk, strong):
+    rng = np.random.default_rng(100 + chunk)
+    lengths = [37, 0, 130, 1, 64]
+    q, k, v, g, beta, S0, cu = _case(rng, lengths, strong_decay=strong)
+    o_ref, f_ref = R.gated_delta_rule(q, k, v, g, beta, scale=0.8, initial_state=S0, cu_seqlens=cu)
+    o, f = chunked_gated_delta_rule(q, k, v, g, beta, chunk=chunk, scale=0.8, initial_state=S0,
+                                    cu_seqlens=cu)
+    scale_o = np.sqrt(np.mean(o_ref ** 2))
+    assert np.max(np.abs(o - o_ref)) <= 1e-12 * max(1.0, scale_o)
+    assert np.max(np.abs(f - f_ref)) <= 1e-12
+    np.testing.assert_array_equal(f[1], S0[1])
+
+
+def test_chunked_without_l2norm():
+    rng = np.random.default_rng(5)
+    q, k, v, g, beta, S0, cu = _case(rng, [50], strong_decay=False)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q *= 0.3
+    o_ref, f_ref = R.gated_delta_rule(q, k, v, g, beta, initial_state=S0, use_qk_l2norm=False)
+    o, f = chunked_gated_delta_rule(q, k, v, g, beta, chunk=16, initial_state=S0, use_qk_l2norm=False)
+    assert np.max(np.abs(o - o_ref)) < 1e-12 and np.max(np.abs(f - f_ref)) < 1e-12
