@@ -1,0 +1,247 @@
+// C ABI of the GDN mixer library: argument validation on the host, then the
+// launchers.  Every check runs before any launch, so a rejected call writes
+// nothing; no path here reads device memory, allocates or synchronises.
+#include <stdint.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "../../include/gdn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+struct Range {
+  const void* p;
+  uint64_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool all_aligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+
+// An output range must not overlap any of the given ranges.
+bool disjoint(const Range& out, std::initializer_list<Range> others) {
+  for (const Range& r : others)
+    if (overlap(out, r)) return false;
+  return true;
+}
+
+int dt_bytes(gdn_dtype dt) { return dt == GDN_BF16 ? 2 : 4; }
+bool dt_valid(gdn_dtype dt) { return dt == GDN_BF16 || dt == GDN_F32; }
+
+// Byte extent of `rows` rows of `width` elements with a row stride (elements).
+uint64_t strided_bytes(int64_t rows, int64_t stride, int64_t width, int eb) {
+  if (rows <= 0) return 0;
+  return static_cast<uint64_t>((rows - 1) * stride + width) * eb;
+}
+
+gdn_status finish(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int32_t>(e);
+    return GDN_ERR_HIP;
+  }
+  return GDN_OK;
+}
+
+// Shared checks of the q/k/v/g/beta arguments of the recurrence entry points.
+gdn_status check_qkv(const void* q, const void* k, const void* v, int64_t& q_stride, int64_t& k_stride,
+                     int64_t& v_stride, gdn_dtype dt, const float* g, const float* beta, int32_t h_qk,
+                     int32_t h_v, int32_t d_k, int32_t d_v) {
+  if (!q || !k || !v || !g || !beta) return GDN_ERR_NULL;
+  if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0 || h_v % h_qk != 0) return GDN_ERR_INVALID;
+  if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
+  if (q_stride == 0) q_stride = static_cast<int64_t>(h_qk) * d_k;
+  if (k_stride == 0) k_stride = static_cast<int64_t>(h_qk) * d_k;
+  if (v_stride == 0) v_stride = static_cast<int64_t>(h_v) * d_v;
+  if (q_stride < static_cast<int64_t>(h_qk) * d_k || k_stride < static_cast<int64_t>(h_qk) * d_k ||
+      v_stride < static_cast<int64_t>(h_v) * d_v)
+    return GDN_ERR_INVALID;
+  if (q_stride % 8 || k_stride % 8 || v_stride % 8) return GDN_ERR_ALIGN;
+  if (!all_aligned({q, k, v, g, beta})) return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_version(void) { return "gdn-mi355x 0.1.0 (gfx950)"; }
+
+int32_t gdn_last_hip_error(void) { return g_last_hip_error; }
+
+const char* gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+    case GDN_ERR_INVALID: return "GDN_ERR_INVALID: invalid size, stride or head grouping";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: head dims, chunk or dtype not supported";
+    case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: pointer or stride not 16-byte aligned";
+    case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps another buffer";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: kernel launch failed";
+    default: return "unknown gdn_status";
+  }
+}
+
+gdn_status gdn_conv1d_fwd(const void* x, gdn_dtype dt, const void* w, int32_t channels, const int32_t* cu_seqlens,
+                          int32_t n_seq, int64_t t_total, void* conv_state, int32_t n_slots,
+                          const int32_t* state_slots, void* y, void* stream) {
+  if (n_seq < 0 || t_total < 0 || channels <= 0 || n_slots < 0) return GDN_ERR_INVALID;
+  if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
+  if (channels % 8) return GDN_ERR_INVALID;
+  if (n_seq == 0) return GDN_OK;
+  if (!x && t_total > 0) return GDN_ERR_NULL;
+  if (!y && t_total > 0) return GDN_ERR_NULL;
+  if (!w || !conv_state) return GDN_ERR_NULL;
+  if (!cu_seqlens && t_total != n_seq) return GDN_ERR_INVALID;
+  if (!state_slots && n_slots < n_seq) return GDN_ERR_INVALID;
+  if (!all_aligned({x, w, conv_state, y, cu_seqlens, state_slots})) return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const Range rx{x, static_cast<uint64_t>(t_total) * channels * eb};
+  const Range ry{y, static_cast<uint64_t>(t_total) * channels * eb};
+  const Range rw{w, static_cast<uint64_t>(channels) * 4 * eb};
+  const Range rs{conv_state, static_cast<uint64_t>(n_slots) * 3 * channels * eb};
+  const Range rcu{cu_seqlens, cu_seqlens ? static_cast<uint64_t>(n_seq + 1) * 4 : 0};
+  const Range rsl{state_slots, state_slots ? static_cast<uint64_t>(n_seq) * 4 : 0};
+  if (!disjoint(ry, {rx, rw, rs, rcu, rsl}) || !disjoint(rs, {rx, rw, rcu, rsl})) return GDN_ERR_ALIAS;
+  return finish(gdn::launch_conv1d(x, dt, w, channels, cu_seqlens, n_seq, t_total, conv_state, state_slots, y,
+                                   stream));
+}
+
+gdn_status gdn_chunk_fwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t chunk,
+                                        int32_t n_seq, int64_t t_total, gdn_dtype dt, int32_t with_norm,
+                                        size_t* bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  if (h_qk <= 0 || h_v <= 0 || h_v % h_qk != 0 || n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
+  if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
+  const bool ok = (d_k == 128 && d_v == 128 && chunk == 64) || (dt == GDN_F32 && d_k == 16 && d_v == 16 && chunk == 16);
+  if (!ok) return GDN_ERR_UNSUPPORTED;
+  *bytes = gdn::chunk_ws_bytes(h_v, d_v, chunk, n_seq, t_total, with_norm);
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                         int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                         int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                         int32_t chunk, const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                         const float* initial_state, float* final_state, void* o, gdn_dtype o_dt, const void* z,
+                         const float* norm_w, float norm_eps, void* workspace, size_t ws_bytes, void* stream) {
+  if (n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
+  if (n_seq == 0) return GDN_OK;
+  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, g, beta, h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (!o || !workspace) return !o ? GDN_ERR_NULL : GDN_ERR_WORKSPACE;
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!cu_seqlens && n_seq != 1) return GDN_ERR_NULL;
+  if (!dt_valid(o_dt)) return GDN_ERR_UNSUPPORTED;
+  size_t need = 0;
+  st = gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_total, dt, z != nullptr, &need);
+  if (st != GDN_OK) return st;
+  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (!all_aligned({o, z, norm_w, initial_state, final_state, workspace, cu_seqlens})) return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const uint64_t state_bytes = static_cast<uint64_t>(n_seq) * h_v * d_v * d_k * 4;
+  const Range rq{q, strided_bytes(t_total, q_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rk{k, strided_bytes(t_total, k_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rv{v, strided_bytes(t_total, v_stride, static_cast<int64_t>(h_v) * d_v, eb)};
+  const Range rg{g, static_cast<uint64_t>(t_total) * h_v * 4};
+  const Range rb{beta, static_cast<uint64_t>(t_total) * h_v * 4};
+  const Range ro{o, static_cast<uint64_t>(t_total) * h_v * d_v * dt_bytes(o_dt)};
+  const Range rz{z, z ? static_cast<uint64_t>(t_total) * h_v * d_v * eb : 0};
+  const Range rw{norm_w, z ? static_cast<uint64_t>(d_v) * 4 : 0};
+  const Range ri{initial_state, initial_state ? state_bytes : 0};
+  const Range rf{final_state, final_state ? state_bytes : 0};
+  const Range rws{workspace, need};
+  const Range rcu{cu_seqlens, cu_seqlens ? static_cast<uint64_t>(n_seq + 1) * 4 : 0};
+  if (!disjoint(ro, {rq, rk, rv, rg, rb, rz, rw, ri, rf, rws, rcu})) return GDN_ERR_ALIAS;
+  if (!disjoint(rws, {rq, rk, rv, rg, rb, rz, rw, ri, rf, rcu})) return GDN_ERR_ALIAS;
+  if (!disjoint(rf, {rq, rk, rv, rg, rb, rz, rw, rcu})) return GDN_ERR_ALIAS;
+  if (initial_state && final_state && initial_state != final_state && overlap(ri, rf)) return GDN_ERR_ALIAS;
+
+  gdn::ChunkArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride;
+  a.dt = dt; a.g = g; a.beta = beta; a.scale = scale;
+  a.use_l2 = use_qk_l2norm != 0; a.l2_eps = l2_eps;
+  a.h_qk = h_qk; a.h_v = h_v; a.d = d_k; a.chunk = chunk;
+  a.cu = cu_seqlens; a.n_seq = n_seq; a.t_total = t_total;
+  a.init = initial_state; a.fin = final_state;
+  a.o = o; a.o_dt = o_dt; a.z = z; a.norm_w = norm_w; a.norm_eps = norm_eps;
+  a.workspace = workspace; a.stream = stream;
+  return finish(gdn::launch_chunk_fwd(a));
+}
+
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                              int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                              int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k,
+                              int32_t d_v, int32_t n_req, float* state, int32_t n_slots,
+                              const int32_t* state_slots, void* o, gdn_dtype o_dt, const void* z,
+                              const float* norm_w, float norm_eps, void* stream) {
+  if (n_req < 0 || n_slots < 0) return GDN_ERR_INVALID;
+  if (n_req == 0) return GDN_OK;
+  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, g, beta, h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  if (!state || !o) return GDN_ERR_NULL;
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!dt_valid(o_dt)) return GDN_ERR_UNSUPPORTED;
+  if (!((d_k == 128 && d_v == 128) || (d_k == 16 && d_v == 16))) return GDN_ERR_UNSUPPORTED;
+  if (!state_slots && n_slots < n_req) return GDN_ERR_INVALID;
+  if (!all_aligned({state, o, z, norm_w, state_slots})) return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const Range rq{q, strided_bytes(n_req, q_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rk{k, strided_bytes(n_req, k_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rv{v, strided_bytes(n_req, v_stride, static_cast<int64_t>(h_v) * d_v, eb)};
+  const Range rg{g, static_cast<uint64_t>(n_req) * h_v * 4};
+  const Range rb{beta, static_cast<uint64_t>(n_req) * h_v * 4};
+  const Range rs{state, static_cast<uint64_t>(n_slots) * h_v * d_v * d_k * 4};
+  const Range ro{o, static_cast<uint64_t>(n_req) * h_v * d_v * dt_bytes(o_dt)};
+  const Range rz{z, z ? static_cast<uint64_t>(n_req) * h_v * d_v * eb : 0};
+  const Range rw{norm_w, z ? static_cast<uint64_t>(d_v) * 4 : 0};
+  const Range rsl{state_slots, state_slots ? static_cast<uint64_t>(n_req) * 4 : 0};
+  if (!disjoint(ro, {rq, rk, rv, rg, rb, rs, rz, rw, rsl})) return GDN_ERR_ALIAS;
+  if (!disjoint(rs, {rq, rk, rv, rg, rb, rz, rw, rsl})) return GDN_ERR_ALIAS;
+
+  gdn::StepArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride;
+  a.dt = dt; a.g = g; a.beta = beta; a.scale = scale;
+  a.use_l2 = use_qk_l2norm != 0; a.l2_eps = l2_eps;
+  a.h_qk = h_qk; a.h_v = h_v; a.d = d_k; a.n_req = n_req;
+  a.state = state; a.slots = state_slots;
+  a.o = o; a.o_dt = o_dt; a.z = z; a.norm_w = norm_w; a.norm_eps = norm_eps;
+  a.stream = stream;
+  return finish(gdn::launch_recurrent_step(a));
+}
+
+gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w, float eps,
+                             int64_t rows, int32_t d, void* y, gdn_dtype y_dt, void* stream) {
+  if (rows < 0) return GDN_ERR_INVALID;
+  if (!dt_valid(x_dt) || !dt_valid(z_dt) || !dt_valid(y_dt)) return GDN_ERR_UNSUPPORTED;
+  if (d != 16 && d != 128) return GDN_ERR_UNSUPPORTED;
+  if (rows == 0) return GDN_OK;
+  if (!x || !z || !w || !y) return GDN_ERR_NULL;
+  if (!all_aligned({x, z, w, y})) return GDN_ERR_ALIGN;
+  const Range rx{x, static_cast<uint64_t>(rows) * d * dt_bytes(x_dt)};
+  const Range rz{z, static_cast<uint64_t>(rows) * d * dt_bytes(z_dt)};
+  const Range rw{w, static_cast<uint64_t>(d) * 4};
+  const Range ry{y, static_cast<uint64_t>(rows) * d * dt_bytes(y_dt)};
+  const bool in_place = (y == x && y_dt == x_dt);
+  if (!in_place && overlap(ry, rx)) return GDN_ERR_ALIAS;
+  if (!disjoint(ry, {rz, rw})) return GDN_ERR_ALIAS;
+  return finish(gdn::launch_gated_rmsnorm(x, x_dt, z, z_dt, w, eps, rows, d, y, y_dt, stream));
+}
+
+}  // extern "C"

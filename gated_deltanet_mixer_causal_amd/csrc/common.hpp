@@ -1,0 +1,124 @@
+// Device helpers shared by the GDN kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---- scalar conversions --------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ __bf16 f32_to_bf16(float f) { return static_cast<__bf16>(f); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// fp32 value -> bf16 pair (hi, lo) with hi + lo == x to about 2^-17 relative.
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(x);
+  lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// ---- element traits for I/O dtypes ----------------------------------------
+
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const T* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+  // 8 consecutive elements (16 bytes) -> float[8]
+  __device__ __forceinline__ static void load8(const T* p, float* out) {
+    const uint4 r = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store8(T* p, const float* in) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16_bits(in[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(in[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+struct F32 {
+  using T = float;
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load(const T* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = v; }
+  __device__ __forceinline__ static void load8(const T* p, float* out) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+  __device__ __forceinline__ static void store8(T* p, const float* in) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(in[0], in[1], in[2], in[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(in[4], in[5], in[6], in[7]);
+  }
+};
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
+  return v;
+}
+
+// Sequence of a token-block slot.  Block j of sequence s (blocks of `blk`
+// tokens restarting at each sequence start) is given slot
+//     floor(cu[s] / blk) + s + j,
+// which is strictly increasing over (s, j) and stays below
+// ceil(t_total / blk) + n_seq, so a grid of that many blocks covers every
+// block with no host-side knowledge of the lengths.  Returns false for an
+// idle slot.
+__device__ __forceinline__ int64_t seq_start(const int32_t* cu, int s, int64_t t_total) {
+  return cu ? static_cast<int64_t>(cu[s]) : (s == 0 ? 0 : t_total);
+}
+
+// cu == nullptr means a single sequence of t_total tokens.
+__device__ __forceinline__ bool locate_block(const int32_t* cu, int n_seq, int64_t t_total, int blk,
+                                             int64_t slot, int& seq, int64_t& t0, int& len) {
+  // largest s in [0, n_seq) with floor(cu[s]/blk) + s <= slot
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq_start(cu, mid, t_total) / blk + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int64_t start = seq_start(cu, lo, t_total), end = seq_start(cu, lo + 1, t_total);
+  const int64_t j = slot - (start / blk + lo);
+  if (j < 0) return false;
+  t0 = start + j * blk;
+  if (t0 >= end) return false;
+  seq = lo;
+  len = static_cast<int>(end - t0 < blk ? end - t0 : blk);
+  return true;
+}
+
+__host__ __device__ constexpr int64_t block_slots(int64_t t_total, int n_seq, int blk) {
+  return (t_total + blk - 1) / blk + n_seq;
+}
+
+}  // namespace gdn

@@ -1,0 +1,166 @@
+// Causal depthwise conv1d of width 4 + SiLU over packed sequences (gfx950).
+//
+// Output token t of sequence s is SiLU(sum_i w[c][i] * padded[t - start + i][c])
+// where padded = [history(3 raw inputs, oldest first); x_s]; the history is
+// then replaced by the last three rows of padded (haskell-infer-demo README,
+// "Architecture", width-4 causal-conv1d; Flare core-design, short-convolution
+// paragraph and its prepared-interface list: raw projected QKV, dilation 1,
+// SiLU, caller-owned raw-input history, slot mapping, inactive lanes).
+//
+// Prefill: one workgroup per (block of 32 tokens of one sequence, 2048
+// channels); each thread owns 8 adjacent channels (one 16-byte vector per
+// token for bf16) and slides a 3-token window down its block, so every input
+// row is read once plus a 3-row halo.  Blocks never straddle sequences
+// (slots from common.hpp), which keeps the history reads inside the first
+// block of each sequence: that block alone reads the old history and writes
+// the new one, so the in-place update needs no second pass.
+// Decode (one token per sequence): one thread per (sequence, 8 channels).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+constexpr int kConvBT = 32;            // tokens per prefill block (>= 3)
+constexpr int kConvThreads = 256;
+constexpr int kConvCh = kConvThreads * 8;
+
+template <class E>
+__device__ __forceinline__ void load_taps(const typename E::T* w, int c0, float (&wt)[4][8]) {
+  float tmp[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) E::load8(w + static_cast<int64_t>(c0) * 4 + 8 * i, tmp + 8 * i);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wt[i][c] = tmp[4 * c + i];
+}
+
+__device__ __forceinline__ void conv_out(const float (&wt)[4][8], const float (&w0)[8], const float (&w1)[8],
+                                         const float (&w2)[8], const float (&cur)[8], float (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float acc = wt[0][c] * w0[c] + wt[1][c] * w1[c] + wt[2][c] * w2[c] + wt[3][c] * cur[c];
+    out[c] = silu(acc);
+  }
+}
+
+template <class E>
+__global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
+    const typename E::T* __restrict__ x, const typename E::T* __restrict__ w, int channels,
+    const int32_t* __restrict__ cu, int n_seq, int64_t t_total, typename E::T* __restrict__ state,
+    const int32_t* __restrict__ slots, typename E::T* __restrict__ y) {
+  using T = typename E::T;
+  const int c0 = (blockIdx.y * kConvThreads + threadIdx.x) * 8;
+  if (c0 >= channels) return;
+  int seq, len;
+  int64_t t0;
+  if (!locate_block(cu, n_seq, t_total, kConvBT, blockIdx.x, seq, t0, len)) return;
+  const int slot = slots ? slots[seq] : seq;
+  if (slot < 0) return;
+  const int64_t start = cu[seq];
+  const int64_t p0 = t0 - start;
+  const int64_t ld = channels;
+
+  float wt[4][8];
+  load_taps<E>(w, c0, wt);
+  T* hist = state + static_cast<int64_t>(slot) * 3 * ld + c0;
+
+  float h0[8], h1[8], h2[8];   // raw inputs at local positions p0-3, p0-2, p0-1
+  {
+    float* hs[3] = {h0, h1, h2};
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int64_t lp = p0 - 3 + r;
+      if (lp >= 0) E::load8(x + (start + lp) * ld + c0, hs[r]);
+      else E::load8(hist + (3 + lp) * ld, hs[r]);
+    }
+  }
+  float old0[8], old1[8], old2[8];   // the history as read, for the first block's update
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { old0[c] = h0[c]; old1[c] = h1[c]; old2[c] = h2[c]; }
+
+  for (int t = 0; t < len; ++t) {
+    float cur[8], out[8];
+    E::load8(x + (t0 + t) * ld + c0, cur);
+    conv_out(wt, h0, h1, h2, cur, out);
+    E::store8(y + (t0 + t) * ld + c0, out);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { h0[c] = h1[c]; h1[c] = h2[c]; h2[c] = cur[c]; }
+  }
+
+  if (p0 == 0) {
+    // new history row r = padded[L + r] with padded = [old history; x_s]
+    const int64_t L = cu[seq + 1] - start;
+    const float* olds[3] = {old0, old1, old2};
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const int64_t idx = L + r;
+      float row[8];
+      if (idx < 3) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) row[c] = olds[idx][c];
+      } else {
+        E::load8(x + (start + idx - 3) * ld + c0, row);
+      }
+      E::store8(hist + r * ld, row);
+    }
+  }
+}
+
+template <class E>
+__global__ __launch_bounds__(kConvThreads) void k_conv1d_step(
+    const typename E::T* __restrict__ x, const typename E::T* __restrict__ w, int channels, int n_seq,
+    typename E::T* __restrict__ state, const int32_t* __restrict__ slots, typename E::T* __restrict__ y) {
+  using T = typename E::T;
+  const int groups = channels / 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x;
+  const int64_t s = gid / groups;
+  if (s >= n_seq) return;
+  const int c0 = static_cast<int>(gid % groups) * 8;
+  const int slot = slots ? slots[s] : static_cast<int>(s);
+  if (slot < 0) return;
+  const int64_t ld = channels;
+  float wt[4][8];
+  load_taps<E>(w, c0, wt);
+  T* hist = state + static_cast<int64_t>(slot) * 3 * ld + c0;
+  float h0[8], h1[8], h2[8], cur[8], out[8];
+  E::load8(hist, h0);
+  E::load8(hist + ld, h1);
+  E::load8(hist + 2 * ld, h2);
+  E::load8(x + s * ld + c0, cur);
+  conv_out(wt, h0, h1, h2, cur, out);
+  E::store8(y + s * ld + c0, out);
+  E::store8(hist, h1);
+  E::store8(hist + ld, h2);
+  E::store8(hist + 2 * ld, cur);
+}
+
+template <class E>
+static hipError_t run_conv(const void* x, const void* w, int channels, const int32_t* cu, int n_seq,
+                           int64_t t_total, void* state, const int32_t* slots, void* y, hipStream_t st) {
+  using T = typename E::T;
+  if (cu) {
+    const int64_t nblk = block_slots(t_total, n_seq, kConvBT);
+    dim3 grid(static_cast<unsigned>(nblk), (channels + kConvCh - 1) / kConvCh);
+    hipLaunchKernelGGL((k_conv1d_prefill<E>), grid, dim3(kConvThreads), 0, st, static_cast<const T*>(x),
+                       static_cast<const T*>(w), channels, cu, n_seq, t_total, static_cast<T*>(state), slots,
+                       static_cast<T*>(y));
+  } else {
+    const int64_t threads = static_cast<int64_t>(n_seq) * (channels / 8);
+    const unsigned blocks = static_cast<unsigned>((threads + kConvThreads - 1) / kConvThreads);
+    hipLaunchKernelGGL((k_conv1d_step<E>), dim3(blocks), dim3(kConvThreads), 0, st, static_cast<const T*>(x),
+                       static_cast<const T*>(w), channels, n_seq, static_cast<T*>(state), slots,
+                       static_cast<T*>(y));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv1d(const void* x, gdn_dtype dt, const void* w, int channels, const int32_t* cu,
+                         int n_seq, int64_t t_total, void* state, const int32_t* slots, void* y,
+                         void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == GDN_BF16) return run_conv<BF16>(x, w, channels, cu, n_seq, t_total, state, slots, y, st);
+  return run_conv<F32>(x, w, channels, cu, n_seq, t_total, state, slots, y, st);
+}
+
+}  // namespace gdn

@@ -1,0 +1,64 @@
+// Internal launchers behind the C ABI (host side).  Arguments reaching these
+// functions have been validated by the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+struct ChunkArgs {
+  const void *q, *k, *v;
+  int64_t q_stride, k_stride, v_stride;
+  gdn_dtype dt;
+  const float *g, *beta;
+  float scale;
+  int use_l2;
+  float l2_eps;
+  int h_qk, h_v, d, chunk;
+  const int32_t* cu;
+  int n_seq;
+  int64_t t_total;
+  const float* init;
+  float* fin;
+  void* o;
+  gdn_dtype o_dt;
+  const void* z;
+  const float* norm_w;
+  float norm_eps;
+  void* workspace;
+  void* stream;
+};
+
+struct StepArgs {
+  const void *q, *k, *v;
+  int64_t q_stride, k_stride, v_stride;
+  gdn_dtype dt;
+  const float *g, *beta;
+  float scale;
+  int use_l2;
+  float l2_eps;
+  int h_qk, h_v, d, n_req;
+  float* state;
+  const int32_t* slots;
+  void* o;
+  gdn_dtype o_dt;
+  const void* z;
+  const float* norm_w;
+  float norm_eps;
+  void* stream;
+};
+
+size_t chunk_ws_bytes(int h_v, int d, int chunk, int n_seq, int64_t t_total, int with_norm);
+hipError_t launch_chunk_fwd(const ChunkArgs& a);
+hipError_t launch_recurrent_step(const StepArgs& a);
+hipError_t launch_conv1d(const void* x, gdn_dtype dt, const void* w, int channels, const int32_t* cu,
+                         int n_seq, int64_t t_total, void* state, const int32_t* slots, void* y,
+                         void* stream);
+hipError_t launch_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w,
+                                float eps, int64_t rows, int d, void* y, gdn_dtype y_dt, void* stream);
+
+}  // namespace gdn

@@ -1,0 +1,175 @@
+// Recurrent decode step of the gated delta rule (gfx950).
+//
+// One token per request; per (request, v-head) the fp32 state S (d_v x d_k)
+// is read once, updated and written once:
+//     a = exp(g),  e_i = v_i - a (S k^)_i,  S <- a S + beta e k^^T,
+//     o_i = scale (S_new q^)_i = scale (a (S q^)_i + beta e_i (k^ . q^))
+// which is the rule S_t = a S (I - beta k k^T) + beta v k^T, o_t = scale S_t q_t
+// (haskell-infer-demo README, "Architecture"/fla_gdn.cu recurrent decode;
+// FP32 recurrent state: Flare core-design, Qwen defaults table).
+//
+// The step is bound by HBM: 2 x d_v x d_k x 4 bytes of state per (request,
+// head) against ~4 flops per state element.  One workgroup per (request,
+// head); a state row of d_k floats is split over d_k/8 lanes as two 16-byte
+// vectors at columns 4l and d_k/2 + 4l, so the lanes of a row read 2 x 256
+// contiguous bytes; every thread issues all its state loads before any use,
+// keeping 64 KiB per workgroup in flight.  Both row dot products (S k^ and
+// S q^) come from the same registers, reduced across the row's lanes.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+template <class E>
+__device__ __forceinline__ void load4(const typename E::T* p, float* out);
+template <>
+__device__ __forceinline__ void load4<BF16>(const uint16_t* p, float* out) {
+  const uint2 r = *reinterpret_cast<const uint2*>(p);
+  out[0] = __uint_as_float(r.x << 16);
+  out[1] = __uint_as_float(r.x & 0xffff0000u);
+  out[2] = __uint_as_float(r.y << 16);
+  out[3] = __uint_as_float(r.y & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void load4<F32>(const float* p, float* out) {
+  const float4 r = *reinterpret_cast<const float4*>(p);
+  out[0] = r.x; out[1] = r.y; out[2] = r.z; out[3] = r.w;
+}
+
+template <class E, class EO, int D, int NT>
+__global__ __launch_bounds__(NT) void k_recurrent_step(
+    const typename E::T* __restrict__ q, const typename E::T* __restrict__ k, const typename E::T* __restrict__ v,
+    int64_t q_stride, int64_t k_stride, int64_t v_stride, const float* __restrict__ g,
+    const float* __restrict__ beta, float scale, int use_l2, float l2_eps, int h_qk, int h_v,
+    float* __restrict__ state, const int32_t* __restrict__ slots, typename EO::T* __restrict__ o,
+    const typename E::T* __restrict__ z, const float* __restrict__ norm_w, float norm_eps) {
+  constexpr int TPR = D / 8;                 // lanes per state row
+  constexpr int RPP = NT / TPR;              // rows per pass
+  constexpr int PASSES = (D + RPP - 1) / RPP;
+  static_assert(TPR <= 64 && NT % 64 == 0, "row lanes within a wave");
+
+  const int r = blockIdx.x / h_v, h = blockIdx.x % h_v;
+  const int slot = slots ? slots[r] : r;
+  if (slot < 0) return;
+  const int hq = h / (h_v / h_qk);
+  const int tid = threadIdx.x, l = tid % TPR, rg = tid / TPR;
+  const int ca = 4 * l, cb = D / 2 + 4 * l;
+
+  float* S = state + (static_cast<int64_t>(slot) * h_v + h) * D * D;
+  float4 sa[PASSES], sb[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = rg + p * RPP;
+    if (row < D) {
+      sa[p] = *reinterpret_cast<const float4*>(S + row * D + ca);
+      sb[p] = *reinterpret_cast<const float4*>(S + row * D + cb);
+    }
+  }
+
+  float kk[8], qq[8];
+  load4<E>(k + r * k_stride + hq * D + ca, kk);
+  load4<E>(k + r * k_stride + hq * D + cb, kk + 4);
+  load4<E>(q + r * q_stride + hq * D + ca, qq);
+  load4<E>(q + r * q_stride + hq * D + cb, qq + 4);
+  float sk = 0.f, sq = 0.f, kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
+  sk = group_sum<TPR>(sk);
+  sq = group_sum<TPR>(sq);
+  kq = group_sum<TPR>(kq);
+  const float rk = use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f;
+  const float rq = use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { kk[i] *= rk; qq[i] *= rq; }
+  kq *= rk * rq;
+  const float alpha = __expf(g[static_cast<int64_t>(r) * h_v + h]);
+  const float bt = beta[static_cast<int64_t>(r) * h_v + h];
+
+  float orow[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = rg + p * RPP;
+    float dk = sa[p].x * kk[0] + sa[p].y * kk[1] + sa[p].z * kk[2] + sa[p].w * kk[3] +
+               sb[p].x * kk[4] + sb[p].y * kk[5] + sb[p].z * kk[6] + sb[p].w * kk[7];
+    float dq = sa[p].x * qq[0] + sa[p].y * qq[1] + sa[p].z * qq[2] + sa[p].w * qq[3] +
+               sb[p].x * qq[4] + sb[p].y * qq[5] + sb[p].z * qq[6] + sb[p].w * qq[7];
+    dk = group_sum<TPR>(dk);
+    dq = group_sum<TPR>(dq);
+    if (row < D) {
+      const float vi = E::load(v, r * v_stride + h * D + row);
+      const float e = vi - alpha * dk;
+      const float be = bt * e;
+      orow[p] = scale * (alpha * dq + be * kq);
+      float4 na, nb;
+      na.x = alpha * sa[p].x + be * kk[0]; na.y = alpha * sa[p].y + be * kk[1];
+      na.z = alpha * sa[p].z + be * kk[2]; na.w = alpha * sa[p].w + be * kk[3];
+      nb.x = alpha * sb[p].x + be * kk[4]; nb.y = alpha * sb[p].y + be * kk[5];
+      nb.z = alpha * sb[p].z + be * kk[6]; nb.w = alpha * sb[p].w + be * kk[7];
+      *reinterpret_cast<float4*>(S + row * D + ca) = na;
+      *reinterpret_cast<float4*>(S + row * D + cb) = nb;
+    }
+  }
+
+  const int64_t obase = (static_cast<int64_t>(r) * h_v + h) * D;
+  if (!z) {
+    if (l == 0) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int row = rg + p * RPP;
+        if (row < D) EO::store(o, obase + row, orow[p]);
+      }
+    }
+    return;
+  }
+  // fused gated RMSNorm over the head's d_v outputs
+  __shared__ float so[D];
+  __shared__ float sred[NT / 64];
+  if (l == 0) {
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = rg + p * RPP;
+      if (row < D) so[row] = orow[p];
+    }
+  }
+  __syncthreads();
+  const float ov = tid < D ? so[tid] : 0.f;
+  float ss = group_sum<64>(ov * ov);
+  if ((tid & 63) == 0) sred[tid >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) tot += sred[w];
+  if (tid < D) {
+    const float rr = 1.0f / sqrtf(tot * (1.0f / D) + norm_eps);
+    const float zv = E::load(z, obase + tid);
+    EO::store(o, obase + tid, ov * rr * norm_w[tid] * silu(zv));
+  }
+}
+
+template <class E, class EO>
+static hipError_t run_step(const StepArgs& a) {
+  using T = typename E::T;
+  using TO = typename EO::T;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.n_req) * a.h_v);
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const T* z = static_cast<const T*>(a.z);
+  if (a.d == 128)
+    hipLaunchKernelGGL((k_recurrent_step<E, EO, 128, 256>), dim3(blocks), dim3(256), 0, st, q, k, v, a.q_stride,
+                       a.k_stride, a.v_stride, a.g, a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.state,
+                       a.slots, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
+  else
+    hipLaunchKernelGGL((k_recurrent_step<E, EO, 16, 64>), dim3(blocks), dim3(64), 0, st, q, k, v, a.q_stride,
+                       a.k_stride, a.v_stride, a.g, a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.state,
+                       a.slots, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_recurrent_step(const StepArgs& a) {
+  if (a.dt == GDN_BF16) return a.o_dt == GDN_BF16 ? run_step<BF16, BF16>(a) : run_step<BF16, F32>(a);
+  return a.o_dt == GDN_BF16 ? run_step<F32, BF16>(a) : run_step<F32, F32>(a);
+}
+
+}  // namespace gdn

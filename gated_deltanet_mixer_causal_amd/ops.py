@@ -1,0 +1,118 @@
+"""Torch-facing binding of the GDN mixer C ABI (argument marshalling only).
+
+Each function has the name of the C entry point it calls and passes the
+tensors' device pointers, sizes and the current HIP stream straight through;
+every step of the mixer runs in libgdn.so's kernels.  Tensors must live on
+the GPU; outputs are written in place into the tensors passed in.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.bfloat16: L.GDN_BF16, torch.float32: L.GDN_F32}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32") from None
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _rows_view(t: torch.Tensor, name: str) -> int:
+    """Token stride of a [T, H, d] view whose last two dims are dense."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be a [T, H, d] view with dense heads (got strides {t.stride()})")
+    return t.stride(0)
+
+
+def gdn_conv1d_fwd(x, w, conv_state, y, *, cu_seqlens=None, state_slots=None, n_seq=None, stream=None):
+    """Width-4 causal conv1d + SiLU.  x, y [T, Ch]; w [Ch, 4]; conv_state [slots, 3, Ch].
+    With cu_seqlens None every row of x is its own sequence (decode)."""
+    t_total, ch = x.shape
+    if n_seq is None:
+        n_seq = (cu_seqlens.numel() - 1) if cu_seqlens is not None else t_total
+    st = L.load().gdn_conv1d_fwd(_ptr(x), _dt(x), _ptr(w), ch, _ptr(cu_seqlens), n_seq, t_total,
+                                 _ptr(conv_state), conv_state.shape[0], _ptr(state_slots), _ptr(y),
+                                 _stream(stream))
+    L.check("gdn_conv1d_fwd", st)
+    return y
+
+
+def gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_total, dtype, with_norm) -> int:
+    out = ctypes.c_size_t(0)
+    st = L.load().gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_total,
+                                               _DT[dtype], int(bool(with_norm)), ctypes.byref(out))
+    L.check("gdn_chunk_fwd_workspace_size", st)
+    return out.value
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, o, *, chunk, scale=1.0, use_qk_l2norm=True, l2_eps=1e-6,
+                  cu_seqlens=None, initial_state=None, final_state=None, z=None, norm_w=None,
+                  norm_eps=1e-6, workspace=None, stream=None):
+    """Chunked gated delta rule.  q, k [T, Hqk, dk]; v [T, Hv, dv] (token-strided views
+    allowed); g, beta [T, Hv] fp32; o [T, Hv, dv]; states [N, Hv, dv, dk] fp32."""
+    t_total, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n_seq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
+    if workspace is None:
+        nbytes = gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_total, q.dtype, z is not None)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.load().gdn_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(g), _ptr(beta), float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, chunk, _ptr(cu_seqlens), n_seq, t_total,
+        _ptr(initial_state), _ptr(final_state), _ptr(o), _dt(o),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(workspace), workspace.numel(), _stream(stream))
+    L.check("gdn_chunk_fwd", st)
+    return o
+
+
+def gdn_recurrent_step(q, k, v, g, beta, state, o, *, scale=1.0, use_qk_l2norm=True, l2_eps=1e-6,
+                       state_slots=None, z=None, norm_w=None, norm_eps=1e-6, stream=None):
+    """One decode token per request.  q, k [N, Hqk, dk]; v [N, Hv, dv]; g, beta [N, Hv];
+    state [slots, Hv, dv, dk] fp32 updated in place; o [N, Hv, dv]."""
+    n_req, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    st = L.load().gdn_recurrent_step(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(g), _ptr(beta), float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, n_req, _ptr(state), state.shape[0], _ptr(state_slots), _ptr(o), _dt(o),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _stream(stream))
+    L.check("gdn_recurrent_step", st)
+    return o
+
+
+def gdn_gated_rmsnorm(x, z, w, y, *, eps=1e-6, stream=None):
+    """y = x / sqrt(mean(x^2) + eps) * w * SiLU(z) over the last dim (16 or 128)."""
+    d = x.shape[-1]
+    rows = x.numel() // d
+    st = L.load().gdn_gated_rmsnorm(_ptr(x), _dt(x), _ptr(z), _dt(z), _ptr(w), float(eps), rows, d,
+                                    _ptr(y), _dt(y), _stream(stream))
+    L.check("gdn_gated_rmsnorm", st)
+    return y
+
+
+def qkv_views(y_conv: torch.Tensor, h_qk: int, d_k: int, h_v: int, d_v: int):
+    """q, k, v views of a conv output [T, Ch] (channels q | k | v), no copies."""
+    t = y_conv.shape[0]
+    nq = h_qk * d_k
+    ch = y_conv.shape[1]
+    q = y_conv.as_strided((t, h_qk, d_k), (ch, d_k, 1), y_conv.storage_offset())
+    k = y_conv.as_strided((t, h_qk, d_k), (ch, d_k, 1), y_conv.storage_offset() + nq)
+    v = y_conv.as_strided((t, h_v, d_v), (ch, d_v, 1), y_conv.storage_offset() + 2 * nq)
+    return q, k, v

@@ -1,0 +1,226 @@
+/*
+ * gdn.h -- Gated DeltaNet causal mixer for AMD Instinct MI355X (gfx950).
+ *
+ * The mixer is the linear-attention block that hybrid Qwen-style models run
+ * in 48 of their 64 layers: a width-4 causal conv1d with SiLU over the
+ * projected q|k|v channels, the gated delta rule, and a gated RMSNorm
+ * (haskell-infer-demo README, "Highlights", hybrid-architecture bullet, and
+ * "Architecture", kernels gdn_conv.cu, fla_gdn.cu and gdn_norm.cu).
+ *
+ * Gated delta rule, per sequence and v-head, with state S (d_v x d_k, fp32):
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,   o_t = scale S_t q_t,
+ * a_t = exp(g_t), k_t and q_t L2-normalised when use_qk_l2norm is set.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer unless marked (host).  The caller owns
+ *     every buffer.  The library allocates nothing, keeps no pointer after a
+ *     call returns, never synchronises and never copies device data to the
+ *     host.  All work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream).
+ *   - Sizes are element counts.  Device buffers must be 16-byte aligned.
+ *   - Arguments are checked on the host before anything is launched; a call
+ *     that returns an error status has written nothing.
+ *   - Sequence boundaries (cu_seqlens) and state slots are device data and are
+ *     never read on the host: their contents are the caller's guarantee
+ *     (cu_seqlens non-decreasing, cu_seqlens[0] = 0, cu_seqlens[n_seq] =
+ *     t_total; active slots in range and unique).  This follows the prepared
+ *     short-convolution interface of the Flare core-design page (packed
+ *     prefill and single-token decode, caller-owned state, explicit slot
+ *     mapping, inactive lanes that write no state, no CPU sequence-length
+ *     extraction).
+ *   - A negative state slot marks an inactive lane: nothing is read for it
+ *     and nothing is written, neither state nor output rows.
+ *   - Device faults surface at the caller's next synchronisation.
+ *   - The library is thread-safe across streams; it holds no global mutable
+ *     state other than a thread-local last HIP error.
+ *
+ * Layouts (row-major, last index fastest)
+ *   conv input/output x, y   [t_total, channels], channels ordered q | k | v
+ *   conv weights w           [channels, 4], w[c][3] multiplies the current token
+ *   conv state               [slots, 3, channels], oldest token first (raw inputs)
+ *   q, k                     [t_total, h_qk, d_k] with a token stride (elements)
+ *   v                        [t_total, h_v, d_v] with a token stride (elements)
+ *   g, beta                  [t_total, h_v] fp32 (log-decay and write strength)
+ *   recurrent state          [slots or n_seq, h_v, d_v, d_k] fp32 (S k = v orientation)
+ *   o, z, y                  [t_total, h_v, d_v] dense
+ *   v-head h reads q/k head h / (h_v / h_qk).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gdn_status;
+#define GDN_OK 0
+#define GDN_ERR_NULL 1        /* a required pointer is NULL */
+#define GDN_ERR_INVALID 2     /* negative size, h_v % h_qk != 0, bad stride, t_total != n_seq in decode */
+#define GDN_ERR_UNSUPPORTED 3 /* head dims / chunk / dtype combination not built */
+#define GDN_ERR_ALIGN 4       /* a device pointer or stride breaks 16-byte alignment */
+#define GDN_ERR_ALIAS 5       /* an output overlaps an input or another output */
+#define GDN_ERR_WORKSPACE 6   /* workspace NULL or smaller than gdn_chunk_fwd_workspace_size */
+#define GDN_ERR_HIP 7         /* a launch failed; see gdn_last_hip_error() */
+
+typedef int32_t gdn_dtype;
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/*
+ * gdn_conv1d_fwd -- causal depthwise conv1d of width 4, then SiLU.
+ * (haskell-infer-demo README, "Architecture": native causal-conv1d of width 4;
+ *  Flare core-design, short-convolution paragraph: raw projected QKV, dilation
+ *  1, SiLU, raw input history; the speculative snapshot paragraph: three-token
+ *  GDN convolution windows.)
+ *
+ * For sequence s (tokens cu_seqlens[s] .. cu_seqlens[s+1]-1 of x) with history
+ * H = conv_state[slot(s)] (3 raw inputs, oldest first), the padded input is
+ * [H; x_s] and output token t is
+ *     y[t][c] = SiLU( sum_{i=0..3} w[c][i] * padded[t - start + i][c] ),
+ * accumulated in fp32 and rounded once to dt.  Afterwards conv_state[slot(s)]
+ * holds the last three rows of the padded input (a sequence shorter than 3
+ * shifts its tokens in; a zero-length sequence leaves it bit-identical).
+ *
+ *   x           [t_total, channels] of dt (read)
+ *   dt          GDN_BF16 or GDN_F32; w, conv_state and y use the same dtype
+ *   w           [channels, 4] (read)
+ *   channels    > 0, multiple of 8
+ *   cu_seqlens  [n_seq + 1] int32, or NULL for decode: exactly one token per
+ *               sequence, which requires t_total == n_seq
+ *   conv_state  [n_slots, 3, channels], read and updated in place
+ *   n_slots     number of rows of conv_state (>= n_seq when state_slots is NULL)
+ *   state_slots [n_seq] int32 slot per sequence in [0, n_slots), NULL = identity
+ *               (slot s); negative = inactive lane (its y rows and state untouched)
+ *   y           [t_total, channels] (written); must not overlap x, w or conv_state
+ * n_seq == 0 is a no-op.
+ */
+gdn_status gdn_conv1d_fwd(const void* x, gdn_dtype dt, const void* w, int32_t channels,
+                          const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                          void* conv_state, int32_t n_slots, const int32_t* state_slots, void* y,
+                          void* stream);
+
+/*
+ * gdn_chunk_fwd -- chunked prefill of the gated delta rule over packed sequences.
+ * (Recurrence: the formula at the top of this header.  Chunked prefill and
+ *  recurrent decode as in haskell-infer-demo README, "Architecture", fla_gdn.cu.
+ *  FP32 recurrent state and BF16 intermediates, chunks relative to each call:
+ *  Flare core-design, GDN numerics paragraph and Qwen defaults table.  Final
+ *  state at the exact consumed length: Flare core-design, checkpoint endpoints
+ *  "not rounded to token groups".)
+ *
+ * Chunks of `chunk` tokens restart at every sequence start.  Within a chunk the
+ * kernels use the UT/WY form (intra-chunk triangular solve, then contractions
+ * with the fp32 state on the matrix cores); a call boundary that is a multiple
+ * of `chunk` leaves results bit-identical to one longer call.
+ *
+ *   q, k        [t_total, h_qk, d_k] of dt, token stride q_stride / k_stride
+ *   v           [t_total, h_v, d_v] of dt, token stride v_stride
+ *               (strides in elements; 0 = dense; multiples of 8)
+ *   dt          GDN_BF16 (bf16 operands on the matrix cores, derived operands as
+ *               bf16 hi+lo pairs, fp32 accumulation) or GDN_F32 (fp32 matrix cores)
+ *   g, beta     [t_total, h_v] fp32: a_t = exp(g_t), write strength beta_t
+ *   scale       output scale (1 for the plain rule; models often use d_k^-1/2)
+ *   use_qk_l2norm  nonzero: q and k are replaced by x / sqrt(sum x^2 + l2_eps)
+ *   (h_qk, h_v) h_v % h_qk == 0; (d_k, d_v, chunk): (128,128,64) for both
+ *               dtypes, (16,16,16) for GDN_F32
+ *   g           must be finite here (the chunk form takes differences of its
+ *               running sums); a hard reset (g = -inf) is exact in gdn_recurrent_step
+ *   cu_seqlens  [n_seq + 1] int32; NULL allowed only when n_seq == 1
+ *   initial_state [n_seq, h_v, d_v, d_k] fp32 or NULL (zeros)
+ *   final_state [n_seq, h_v, d_v, d_k] fp32 or NULL (not wanted); may equal
+ *               initial_state exactly (updated in place), no partial overlap.
+ *               final_state[s] is the state after exactly len(s) tokens.
+ *   o           [t_total, h_v, d_v] of o_dt (GDN_F32 or GDN_BF16): the outputs,
+ *               or with z != NULL the gated RMSNorm of the outputs (epilogue)
+ *   z           NULL, or [t_total, h_v, d_v] of dt: gate of the gated RMSNorm
+ *               y = o / sqrt(mean_dv(o^2) + norm_eps) * norm_w * SiLU(z)
+ *   norm_w      [d_v] fp32, required when z != NULL
+ *   workspace   device scratch of ws_bytes >= gdn_chunk_fwd_workspace_size(...);
+ *               its contents need no initialisation and are not preserved
+ * n_seq == 0 is a no-op.  Zero-length sequences are legal: their final state
+ * equals their initial state (or zeros).
+ */
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
+                         int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                         const float* g, const float* beta, float scale,
+                         int32_t use_qk_l2norm, float l2_eps,
+                         int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t chunk,
+                         const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                         const float* initial_state, float* final_state,
+                         void* o, gdn_dtype o_dt,
+                         const void* z, const float* norm_w, float norm_eps,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd_workspace_size -- (host) bytes of workspace gdn_chunk_fwd needs.
+ * An upper bound computed from capacities only (n_seq and t_total), so one
+ * allocation serves every call with the same or smaller capacities.
+ * with_norm: nonzero if the call will pass z.  Writes *bytes on success.
+ */
+gdn_status gdn_chunk_fwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                                        int32_t chunk, int32_t n_seq, int64_t t_total,
+                                        gdn_dtype dt, int32_t with_norm, size_t* bytes /* host */);
+
+/*
+ * gdn_recurrent_step -- one decode token per request, state updated in place.
+ * (The recurrence at the top of this header applied to a single token; upstream
+ *  recurrent decode: haskell-infer-demo README, "Architecture", fla_gdn.cu;
+ *  FP32 recurrent state: Flare core-design, Qwen defaults table.)
+ *
+ * Each (request, v-head) state of d_v x d_k fp32 is streamed once through
+ * registers: read, decayed, corrected by the delta rule, used for the output
+ * and written back.
+ *
+ *   q, k, v, strides, dt, g, beta, scale, use_qk_l2norm, l2_eps, h_qk, h_v,
+ *   d_k, d_v: as gdn_chunk_fwd with t_total = n_req; (d_k, d_v) in {(16,16), (128,128)}
+ *   state       [n_slots, h_v, d_v, d_k] fp32, read and written in place
+ *   n_slots     number of state entries (>= n_req when state_slots is NULL)
+ *   state_slots [n_req] int32 slot per request in [0, n_slots), NULL = identity;
+ *               negative = inactive lane (reads nothing, writes nothing, o rows
+ *               untouched)
+ *   o           [n_req, h_v, d_v] of o_dt; with z != NULL the gated RMSNorm output
+ *   z, norm_w, norm_eps: as gdn_chunk_fwd
+ * n_req == 0 is a no-op.
+ */
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
+                              int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                              const float* g, const float* beta, float scale,
+                              int32_t use_qk_l2norm, float l2_eps,
+                              int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t n_req,
+                              float* state, int32_t n_slots, const int32_t* state_slots,
+                              void* o, gdn_dtype o_dt,
+                              const void* z, const float* norm_w, float norm_eps, void* stream);
+
+/*
+ * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * w * SiLU(z), per row of d.
+ * (The gated RMSNorm of the GDN layers: haskell-infer-demo README,
+ *  "Highlights", hybrid-architecture bullet, and "Architecture", gdn_norm.cu;
+ *  distinct from the GemmaRMSNorm of flashinfer_norm.cu.)
+ *
+ *   x   [rows, d] of x_dt (GDN_F32 or GDN_BF16)
+ *   z   [rows, d] of z_dt
+ *   w   [d] fp32
+ *   y   [rows, d] of y_dt; may equal x exactly when x_dt == y_dt (in place)
+ *   d in {16, 128}.  rows == 0 is a no-op.
+ */
+gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt,
+                             const float* w, float eps, int64_t rows, int32_t d,
+                             void* y, gdn_dtype y_dt, void* stream);
+
+/* (host) Name of a status code; never NULL. */
+const char* gdn_status_string(gdn_status status);
+
+/* (host) hipError_t of the last failed launch on this thread (0 if none). */
+int32_t gdn_last_hip_error(void);
+
+/* (host) Library version string. */
+const char* gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

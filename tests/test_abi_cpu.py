@@ -1,0 +1,155 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/gdn.h declares, and rejects invalid calls before launching anything.
+
+No call here reaches a kernel: every one is rejected by host validation
+(device pointers are fake integers that are never dereferenced) or is a
+documented no-op, so this runs without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_mixer_causal_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_\w+)\s*\(", text)))
+
+
+def test_header_functions_exported(lib):
+    names = _declared()
+    assert set(names) == set(L.PROTOTYPES), names
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.gdn_status_string(s).decode().startswith(L.STATUS_NAMES[s])
+    assert b"unknown" in lib.gdn_status_string(99)
+    assert lib.gdn_last_hip_error() == 0
+    assert b"gfx950" in lib.gdn_version()
+
+
+A = 0x10000000  # fake, 16-byte aligned device addresses spaced far apart
+
+
+def _addr(i):
+    return A * (i + 1)
+
+
+def conv(lib, **kw):
+    a = dict(x=_addr(0), dt=L.GDN_BF16, w=_addr(1), ch=1024, cu=_addr(2), n=2, t=10, st=_addr(3), ns=2,
+             sl=None, y=_addr(4))
+    a.update(kw)
+    return lib.gdn_conv1d_fwd(a["x"], a["dt"], a["w"], a["ch"], a["cu"], a["n"], a["t"], a["st"], a["ns"],
+                              a["sl"], a["y"], None)
+
+
+def test_conv_validation(lib):
+    assert conv(lib, n=0) == L.GDN_OK                       # no-op
+    assert conv(lib, n=-1) == L.GDN_ERR_INVALID
+    assert conv(lib, ch=12) == L.GDN_ERR_INVALID             # not a multiple of 8
+    assert conv(lib, dt=5) == L.GDN_ERR_UNSUPPORTED
+    assert conv(lib, w=None) == L.GDN_ERR_NULL
+    assert conv(lib, st=None) == L.GDN_ERR_NULL
+    assert conv(lib, cu=None, t=3, n=2) == L.GDN_ERR_INVALID  # decode needs t_total == n_seq
+    assert conv(lib, ns=1) == L.GDN_ERR_INVALID              # identity slots need n_slots >= n_seq
+    assert conv(lib, x=_addr(0) + 4) == L.GDN_ERR_ALIGN
+    assert conv(lib, y=_addr(0) + 16) == L.GDN_ERR_ALIAS     # y overlaps x
+    assert conv(lib, st=_addr(4) + 32) == L.GDN_ERR_ALIAS    # state overlaps y
+
+
+def chunk(lib, **kw):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), qs=0, ks=0, vs=0, dt=L.GDN_BF16, g=_addr(3), b=_addr(4),
+             hq=2, hv=4, dk=128, dv=128, c=64, cu=_addr(5), n=1, t=100, init=None, fin=_addr(6), o=_addr(7),
+             odt=L.GDN_F32, z=None, nw=None, ws=_addr(8), wsb=1 << 26)
+    a.update(kw)
+    return lib.gdn_chunk_fwd(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["dt"], a["g"], a["b"], 1.0, 1,
+                             1e-6, a["hq"], a["hv"], a["dk"], a["dv"], a["c"], a["cu"], a["n"], a["t"], a["init"],
+                             a["fin"], a["o"], a["odt"], a["z"], a["nw"], 1e-6, a["ws"], a["wsb"], None)
+
+
+def test_chunk_validation(lib):
+    assert chunk(lib, n=0) == L.GDN_OK
+    assert chunk(lib, t=-1) == L.GDN_ERR_INVALID
+    assert chunk(lib, q=None) == L.GDN_ERR_NULL
+    assert chunk(lib, o=None) == L.GDN_ERR_NULL
+    assert chunk(lib, ws=None) == L.GDN_ERR_WORKSPACE
+    assert chunk(lib, wsb=1024) == L.GDN_ERR_WORKSPACE
+    assert chunk(lib, hv=3) == L.GDN_ERR_INVALID             # h_v % h_qk
+    assert chunk(lib, dk=64, dv=64) == L.GDN_ERR_UNSUPPORTED
+    assert chunk(lib, c=32) == L.GDN_ERR_UNSUPPORTED
+    assert chunk(lib, dk=16, dv=16, c=16) == L.GDN_ERR_UNSUPPORTED   # bf16 needs the 128/64 shape
+    assert chunk(lib, odt=9) == L.GDN_ERR_UNSUPPORTED
+    assert chunk(lib, qs=100) == L.GDN_ERR_INVALID           # stride below a row
+    assert chunk(lib, qs=260) == L.GDN_ERR_ALIGN             # stride not a multiple of 8
+    assert chunk(lib, g=_addr(3) + 8) == L.GDN_ERR_ALIGN
+    assert chunk(lib, z=_addr(9)) == L.GDN_ERR_NULL          # z without norm weight
+    assert chunk(lib, cu=None, n=2) == L.GDN_ERR_NULL        # NULL cu_seqlens only for one sequence
+    assert chunk(lib, o=_addr(0) + 4096) == L.GDN_ERR_ALIAS  # o overlaps q
+    assert chunk(lib, fin=_addr(8) + 256) == L.GDN_ERR_ALIAS  # final state inside the workspace
+    assert chunk(lib, init=_addr(6) + 64) == L.GDN_ERR_ALIAS  # partial overlap of the states
+
+
+def test_chunk_workspace_size(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0
+    slots = 4096 // 64 + 1
+    expect = 2 * slots * 32 * 64 * 64 * 4 + slots * 32 * 4 * 64 * 4
+    assert out.value == expect
+    assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 1, ctypes.byref(out)) == 0
+    assert out.value == expect + 4096 * 32 * 128 * 4
+    assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, None) == L.GDN_ERR_NULL
+    assert lib.gdn_chunk_fwd_workspace_size(16, 32, 64, 64, 64, 1, 4096, L.GDN_BF16, 0,
+                                            ctypes.byref(out)) == L.GDN_ERR_UNSUPPORTED
+
+
+def step(lib, **kw):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dt=L.GDN_BF16, g=_addr(3), b=_addr(4), hq=2, hv=4, d=128,
+             n=3, st=_addr(5), ns=3, sl=None, o=_addr(6), odt=L.GDN_F32, z=None, nw=None)
+    a.update(kw)
+    return lib.gdn_recurrent_step(a["q"], a["k"], a["v"], 0, 0, 0, a["dt"], a["g"], a["b"], 1.0, 1, 1e-6,
+                                  a["hq"], a["hv"], a["d"], a["d"], a["n"], a["st"], a["ns"], a["sl"], a["o"],
+                                  a["odt"], a["z"], a["nw"], 1e-6, None)
+
+
+def test_recurrent_validation(lib):
+    assert step(lib, n=0) == L.GDN_OK
+    assert step(lib, n=-2) == L.GDN_ERR_INVALID
+    assert step(lib, st=None) == L.GDN_ERR_NULL
+    assert step(lib, d=64) == L.GDN_ERR_UNSUPPORTED
+    assert step(lib, ns=2) == L.GDN_ERR_INVALID
+    assert step(lib, o=_addr(5) + 1024) == L.GDN_ERR_ALIAS    # o inside the state
+    assert step(lib, st=_addr(4) + 16) == L.GDN_ERR_ALIAS     # state overlaps beta
+    assert step(lib, o=_addr(6) + 8) == L.GDN_ERR_ALIGN
+
+
+def norm(lib, **kw):
+    a = dict(x=_addr(0), xdt=L.GDN_F32, z=_addr(1), zdt=L.GDN_BF16, w=_addr(2), rows=10, d=128, y=_addr(3),
+             ydt=L.GDN_F32)
+    a.update(kw)
+    return lib.gdn_gated_rmsnorm(a["x"], a["xdt"], a["z"], a["zdt"], a["w"], 1e-6, a["rows"], a["d"], a["y"],
+                                 a["ydt"], None)
+
+
+def test_norm_validation(lib):
+    assert norm(lib, rows=0) == L.GDN_OK
+    assert norm(lib, rows=-1) == L.GDN_ERR_INVALID
+    assert norm(lib, d=64) == L.GDN_ERR_UNSUPPORTED
+    assert norm(lib, z=None) == L.GDN_ERR_NULL
+    assert norm(lib, y=_addr(0) + 16) == L.GDN_ERR_ALIAS      # partial overlap with x
+    assert norm(lib, y=_addr(1)) == L.GDN_ERR_ALIAS           # y over z
+    assert norm(lib, w=_addr(2) + 4) == L.GDN_ERR_ALIGN
