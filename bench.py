@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the GDN mixer hot path on one MI355X.
+
+Prefill (the headline `value`): one step is the whole prefill mixer over one
+synthetic batch of the hybrid model's GDN shape -- B=1, T=4096, 16 q/k heads,
+32 v heads, d=128, chunk 64, bf16: gdn_conv1d_fwd (width-4 conv + SiLU) then
+gdn_chunk_fwd (chunked gated delta rule, fp32 state) with the fused gated
+RMSNorm epilogue writing bf16.  value = tokens/s.
+
+Decode (reported beside it): one step is the decode mixer for 64 requests,
+one token each -- gdn_conv1d_fwd in decode mode then gdn_recurrent_step with
+the fused norm -- on per-request fp32 states of 32 x 128 x 128; reported as
+state GB/s (2 x state bytes per step) and steps/s.
+
+Both legs rotate over `--sets` independent copies of their buffers (as the
+GDN layers of a model would), so the working set exceeds the 256 MB Infinity
+Cache and the numbers are HBM-cold.  Inputs are resident in HBM before the
+timed region starts.  Timing: W warmup steps, then K steps bracketed by
+torch.cuda.synchronize() and HIP events on the stream the kernels run on.
+
+Roofline of the dominant entry point gdn_chunk_fwd (prep + scan kernels):
+algorithmic flops of the chunked method, 139,648 per token per v-head
+(4.469 MFLOP per token), over its event-timed average duration, against the
+dense bf16 matrix-core peak.  The CPU baseline times the float64 oracle on a
+bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorithmic)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=4, help="independent buffer sets rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per gdn_chunk_fwd call {'fetch': B, 'write': B}")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup, torch):
+    """Run fn(i) warmup times, then `steps` times between events; returns ms per step."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def prefill_leg(args, torch, np, ops, I):
+    lay = I.MODEL_LAYOUT
+    d = I.model_prefill_inputs()
+    T = d["x"].shape[0]
+    dev = "cuda:0"
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(dev)
+
+    ws_bytes = ops.gdn_chunk_fwd_workspace_size(lay.h_qk, lay.h_v, lay.d_k, lay.d_v, lay.chunk, 1, T,
+                                                torch.bfloat16, True)
+    sets = []
+    x0 = up(d["x"], torch.bfloat16)
+    for _ in range(args.sets):
+        s = dict(x=x0.clone(), w=up(d["conv_w"], torch.bfloat16), tail=up(d["tail"], torch.bfloat16),
+                 cu=torch.from_numpy(d["cu_seqlens"]).to(dev), g=up(d["g"]), beta=up(d["beta"]),
+                 z=up(d["z"], torch.bfloat16), nw=up(d["norm_w"]),
+                 state=torch.zeros((1, lay.h_v, lay.d_v, lay.d_k), device=dev),
+                 y_conv=torch.empty((T, lay.channels), dtype=torch.bfloat16, device=dev),
+                 y=torch.empty((T, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev),
+                 o=torch.empty((T, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev),
+                 ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev))
+        s["q"], s["k"], s["v"] = ops.qkv_views(s["y_conv"], lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+        sets.append(s)
+    del x0
+
+    def step(i):
+        s = sets[i % len(sets)]
+        ops.gdn_conv1d_fwd(s["x"], s["w"], s["tail"], s["y_conv"], cu_seqlens=s["cu"])
+        ops.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["y"], chunk=lay.chunk, cu_seqlens=s["cu"],
+                          initial_state=None, final_state=s["state"], z=s["z"], norm_w=s["nw"],
+                          workspace=s["ws"])
+
+    def chunk_only(i):
+        s = sets[i % len(sets)]
+        ops.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["o"], chunk=lay.chunk, cu_seqlens=s["cu"],
+                          final_state=s["state"], workspace=s["ws"])
+
+    ms, wall = timed(step, args.steps, args.warmup, torch)
+    ms_chunk, _ = timed(chunk_only, args.steps, args.warmup, torch)
+    return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, layout=lay)
+
+
+def decode_leg(args, torch, np, ops, I):
+    lay = I.MODEL_LAYOUT
+    n_req = 64
+    dev = "cuda:0"
+    d = I.decode_inputs(2, lay, n_req, 8)
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(dev)
+
+    state0 = up(d["state"])
+    sets = []
+    for _ in range(args.sets):
+        s = dict(state=state0.clone(), tail=up(d["tail"], torch.bfloat16), w=up(d["conv_w"], torch.bfloat16),
+                 nw=up(d["norm_w"]), y_conv=torch.empty((n_req, lay.channels), dtype=torch.bfloat16, device=dev),
+                 o=torch.empty((n_req, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev))
+        s["q"], s["k"], s["v"] = ops.qkv_views(s["y_conv"], lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+        sets.append(s)
+    del state0
+    steps_in = [dict(x=up(d["x"][t], torch.bfloat16), g=up(d["g"][t]), beta=up(d["beta"][t]),
+                     z=up(d["z"][t], torch.bfloat16)) for t in range(d["x"].shape[0])]
+
+    def step(i):
+        s = sets[i % len(sets)]
+        inp = steps_in[i % len(steps_in)]
+        ops.gdn_conv1d_fwd(inp["x"], s["w"], s["tail"], s["y_conv"])
+        ops.gdn_recurrent_step(s["q"], s["k"], s["v"], inp["g"], inp["beta"], s["state"], s["o"], z=inp["z"],
+                               norm_w=s["nw"])
+
+    def rec_only(i):
+        s = sets[i % len(sets)]
+        inp = steps_in[i % len(steps_in)]
+        ops.gdn_recurrent_step(s["q"], s["k"], s["v"], inp["g"], inp["beta"], s["state"], s["o"])
+
+    ms, wall = timed(step, args.steps, args.warmup, torch)
+    ms_rec, _ = timed(rec_only, args.steps, args.warmup, torch)
+    state_bytes = n_req * lay.h_v * lay.d_v * lay.d_k * 4
+    # per request: q, k, v, z (bf16), g, beta (fp32), o (bf16)
+    small = n_req * (2 * lay.h_qk * lay.d_k * 2 + lay.h_v * lay.d_v * 2 + 2 * lay.h_v * 4 + lay.h_v * lay.d_v * 2)
+    return dict(ms=ms, wall=wall, ms_rec=ms_rec, n_req=n_req, state_bytes=state_bytes, small=small)
+
+
+def cpu_baseline(np, I, R):
+    """Float64 oracle (conv -> gated delta rule -> gated norm) on the whole
+    prefill workload (4096 tokens, all 32 v-heads), single thread."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    lay = I.MODEL_LAYOUT
+    d = I.model_prefill_inputs()
+    n = 4096
+    import contextlib
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        t0 = time.perf_counter()
+        R.mixer_prefill(d["x"][:n], d["conv_w"], d["tail"], d["state"], d["beta"][:n], d["g"][:n], d["z"][:n],
+                        d["norm_w"], [0, n], h_qk=lay.h_qk, h_v=lay.h_v, d_k=lay.d_k, d_v=lay.d_v,
+                        bf16_boundary=True)
+        dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"the whole B=1 T={n} prefill mixer (conv, recurrence, norm), all 32 v-heads, float64, 1 thread "
+                       f"({dt:.1f} s)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the mixer runs on one GPU with no sharding).", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    from gated_deltanet_mixer_causal_amd import ops
+    from harness import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ops.L.load()
+    pf = prefill_leg(args, torch, np, ops, I)
+    T = pf["T"]
+    lay = pf["layout"]
+    tok_s = T / (pf["ms"] * 1e-3)
+    flop = FLOP_PER_TOKEN_HEAD * lay.h_v * T
+    chunk_tflops = flop / (pf["ms_chunk"] * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        tr = json.load(open(args.traffic))
+        traffic = tr.get("fetch", 0) + tr.get("write", 0)
+    out = {
+        "metric": "GDN prefill tokens/s (% MFMA peak) + decode state GB/s (% HBM peak)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GDN mixer prefill: conv1d+SiLU -> chunked gated delta rule -> gated RMSNorm; "
+                               "B=1 T=4096, 16 q/k heads, 32 v heads, d=128, chunk 64, bf16 in/out, fp32 state",
+                   "global_batch": 1, "seq_len": T, "parallelism": "none (1 GPU)",
+                   "buffer_sets_rotated": args.sets},
+        "roofline": {"kernel": "gdn_chunk_fwd (k_chunk_prep + k_chunk_scan)", "bound": "mfma",
+                     "achieved": round(chunk_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(chunk_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "avg_launch_ms": round(pf["ms_chunk"], 4),
+                     "algorithmic_flop_per_launch": flop},
+    }
+    if not args.no_decode:
+        dc = decode_leg(args, torch, np, ops, I)
+        gbs = 2 * dc["state_bytes"] / (dc["ms_rec"] * 1e-3) / 1e9
+        alg = 2 * dc["state_bytes"] + dc["small"]
+        out["decode"] = {
+            "workload": "64 requests x 1 token, same head layout, fp32 state 32x128x128 per request",
+            "state_GB_per_s": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "mixer_steps_per_s": round(1e3 / dc["ms"], 1),
+            "ms_per_mixer_step": round(dc["ms"], 4),
+            "roofline": {"kernel": "gdn_recurrent_step", "bound": "hbm",
+                         "achieved": round(alg / (dc["ms_rec"] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(alg / (dc["ms_rec"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "traffic": None, "avg_launch_ms": round(dc["ms_rec"], 4),
+                         "algorithmic_bytes_per_launch": alg},
+        }
+    if not args.no_cpu_baseline:
+        from oracle import gdn_ref as R
+        out["cpu_baseline"] = cpu_baseline(np, I, R)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

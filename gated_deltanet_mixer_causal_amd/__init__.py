@@ -5,6 +5,8 @@ include/gdn.h); `ops` marshals torch tensors into it.  Import of this package
 does not load the library; the first call does, and fails loudly if it has
 not been built.
 """
+import importlib
+
 from ._lib import GdnError, load  # noqa: F401
 
 __all__ = ["GdnError", "load", "ops"]
@@ -12,6 +14,5 @@ __all__ = ["GdnError", "load", "ops"]
 
 def __getattr__(name):
     if name == "ops":
-        from . import ops
-        return ops
+        return importlib.import_module(__name__ + ".ops")
     raise AttributeError(name)

@@ -36,16 +36,37 @@ def note(msg):
     sys.stdout.flush()
 
 
-def bf16_ulp_check(got, ref_rounded, ref_exact, max_frac=1e-3):
+def conv_abs_sum(x, w, tail, cu):
+    """sum_i |w[c, i] * padded[t + i, c]| per output element: the scale of the
+    fp32 rounding error of the 4-tap sum (its condition)."""
+    x = np.abs(np.asarray(x, np.float64))
+    w = np.abs(np.asarray(w, np.float64))
+    tail = np.abs(np.asarray(tail, np.float64))
+    out = np.zeros_like(x)
+    for s in range(len(cu) - 1):
+        xs = x[cu[s]:cu[s + 1]]
+        p = np.concatenate([tail[s], xs])
+        for i in range(4):
+            out[cu[s]:cu[s + 1]] += w[:, i][None] * p[i:i + xs.shape[0]]
+    return out
+
+
+def bf16_ulp_check(got, ref_rounded, ref_exact, max_frac=1e-3, abs_sum=None):
     """bf16 outputs: every element equals the oracle's bf16 rounding or an
-    adjacent bf16 value (the rounding decision taken on fp32 vs float64 sums),
-    and such one-ulp disagreements are rare."""
+    adjacent bf16 value (the rounding decision taken on an fp32 sum instead of
+    a float64 one), and such disagreements are rare.  With `abs_sum` (the
+    condition of the fp32 sum, see conv_abs_sum) the allowance adds the fp32
+    accumulation error bound 8 * 2^-24 * abs_sum * max|SiLU'| for outputs
+    that come from cancelling sums."""
     got = np.asarray(got, np.float64)
     ref_rounded = np.asarray(ref_rounded, np.float64)
     diff = np.abs(got - ref_rounded)
     mant, expo = np.frexp(np.maximum(np.abs(ref_exact), 1e-30))
     ulp = np.ldexp(1.0, expo - 8)
-    assert np.all(diff <= ulp * 1.0000001), f"max diff/ulp {np.max(diff / ulp):.3f}"
+    allow = ulp * 1.0000001
+    if abs_sum is not None:
+        allow = allow + 8 * 2.0 ** -24 * 1.1 * np.asarray(abs_sum, np.float64)
+    assert np.all(diff <= allow), f"max diff/allowance {np.max(diff / allow):.3f}"
     frac = float(np.mean(diff > 0))
     assert frac <= max_frac, f"one-ulp disagreements {frac:.2e}"
     return frac
