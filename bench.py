@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent buffer sets rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="before the timed legs, copy 256 MiB device-to-device once (a plain copy of known "
+                         "size that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per gdn_chunk_fwd call {'fetch': B, 'write': B}")
     return ap.parse_args()
@@ -192,6 +195,12 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ops.L.load()
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     pf = prefill_leg(args, torch, np, ops, I)
     T = pf["T"]
     lay = pf["layout"]

@@ -129,7 +129,7 @@ gdn_status gdn_chunk_fwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, 
   if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
   const bool ok = (d_k == 128 && d_v == 128 && chunk == 64) || (dt == GDN_F32 && d_k == 16 && d_v == 16 && chunk == 16);
   if (!ok) return GDN_ERR_UNSUPPORTED;
-  *bytes = gdn::chunk_ws_bytes(h_v, d_v, chunk, n_seq, t_total, with_norm);
+  *bytes = gdn::chunk_ws_bytes(dt, h_qk, h_v, d_v, chunk, n_seq, t_total, with_norm);
   return GDN_OK;
 }
 

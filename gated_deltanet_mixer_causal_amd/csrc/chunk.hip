@@ -18,16 +18,26 @@
 // U solves u_i = beta_i (v_i - a_i S_{i-1} k^_i) for every token of the chunk.
 //
 // Two kernels:
-//   k_chunk_prep  one workgroup per (chunk, q/k head): the Gram matrices K K^T
+//   k_chunk_prep  one workgroup per (chunk, v-head): the Gram matrices K K^T
 //                 and Q K^T on the matrix cores (raw operands, exact products),
-//                 then per v-head of the group the decay scalars, L, P and the
-//                 unit-lower-triangular solve (16x16 diagonal blocks by forward
-//                 substitution in registers, off-diagonal blocks by fp32 MFMA).
-//                 Writes Tb, P and the per-token scalars to the workspace.
+//                 the decay scalars, L, P and the unit-lower-triangular solve
+//                 (16x16 diagonal blocks by forward substitution in registers,
+//                 off-diagonal blocks by fp32 MFMA).  It writes Tb, P (split
+//                 into bf16 hi/lo) and K^T in matrix-core fragment order.
 //   k_chunk_scan  one workgroup per (sequence, v-head, 16-wide d_v tile),
 //                 walking the sequence's chunks in order with its slice of the
-//                 state held in fp32 registers; every contraction with the state
-//                 or a derived operand runs on the matrix cores.
+//                 state in fp32 registers; every contraction with the state or
+//                 a derived operand runs on the matrix cores.
+//
+// Data movement of the scan.  Every chunk operand the scan reads (K, Q, Tb,
+// P, K^T) is a matrix-core A operand that exactly one wave uses: wave w owns
+// token rows 16w..16w+15 of K, Q, Tb and P and the d_k rows 16(w + 4j) of
+// K^T.  So each wave loads its fragments straight from memory into the
+// registers the MFMAs read -- nothing is staged through LDS -- and issues the
+// next chunk's loads for a register set as soon as the current chunk's MFMAs
+// have consumed it, giving every load a full chunk step of latency.  Only the
+// B operands every wave needs (the state S, X, U and the decayed U) pass
+// through LDS, three barriers per chunk.
 //
 // Operand precision (policy PolBF16): raw bf16 q/k/v are exact single bf16
 // operands; derived operands (S, X, U, Tb, P) are bf16 hi+lo pairs and a
@@ -46,37 +56,34 @@ __device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Operands in LDS are "k-contiguous": A as [m][k] and B as [n][k].  A 16x16
-// tile product accumulates acc[i] += sum_k A[4g+i][k] * B[r][k] -- the
-// matrix-core output layout: lane (r = lane%16, g = lane/16) holds column r,
-// rows 4g..4g+3.
+// Matrix-core operand conventions.  One 16 x 16 x KSTEP product takes per
+// lane (r = lane % 16, g = lane / 16) an A fragment: row r, k elements
+// g*FE .. g*FE+FE-1 of the k-step, and a B fragment: column r, the same k
+// elements; it accumulates acc[i] += A[4g+i][.] B[.][r] (output row 4g+i,
+// column r).  Operands in LDS are stored k-contiguous: A as [m][k], B as [n][k].
 struct PolBF16 {
   using In = BF16;
   using Elem = __bf16;
+  using Frag = bf16x8;
   static constexpr int KSTEP = 32;
+  static constexpr int FE = 8;        // elements per lane per fragment
   static constexpr int PAD = 8;
-  static constexpr int NSPLIT = 2;   // hi and lo arrays
+  static constexpr int NSPLIT = 2;    // hi and lo arrays
 
-  template <bool ALO, bool BLO>
-  __device__ __forceinline__ static void mma(floatx4& acc, const Elem* a_hi, const Elem* a_lo, int lda,
-                                             const Elem* b_hi, const Elem* b_lo, int ldb, int nks) {
+  __device__ __forceinline__ static floatx4 mma(Frag a, Frag b, floatx4 c) { return mfma_bf16(a, b, c); }
+  __device__ __forceinline__ static Frag ld(const Elem* p) { return *reinterpret_cast<const Frag*>(p); }
+  __device__ __forceinline__ static Frag ld_in(const uint16_t* p) { return *reinterpret_cast<const Frag*>(p); }
+
+  // acc += A B over nks k-steps, both operands in LDS (raw, no lo parts)
+  __device__ __forceinline__ static void mma_lds(floatx4& acc, const Elem* a, int lda, const Elem* b, int ldb,
+                                                 int nks) {
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     for (int ks = 0; ks < nks; ++ks) {
-      const int off = ks * 32 + 8 * g;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(a_hi + r * lda + off);
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(b_hi + r * ldb + off);
-      acc = mfma_bf16(ah, bh, acc);
-      if constexpr (ALO) {
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(a_lo + r * lda + off);
-        acc = mfma_bf16(al, bh, acc);
-      }
-      if constexpr (BLO) {
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(b_lo + r * ldb + off);
-        acc = mfma_bf16(ah, bl, acc);
-      }
+      const int off = ks * KSTEP + g * FE;
+      acc = mma(ld(a + r * lda + off), ld(b + r * ldb + off), acc);
     }
   }
-  // Split store of 4 consecutive values.
+  // Split store of 4 consecutive values into LDS hi and lo arrays.
   __device__ __forceinline__ static void put4(Elem* hi, Elem* lo, int idx, const float* v) {
     bf16x4 h, l;
 #pragma unroll
@@ -89,10 +96,30 @@ struct PolBF16 {
     *reinterpret_cast<bf16x4*>(hi + idx) = h;
     *reinterpret_cast<bf16x4*>(lo + idx) = l;
   }
-  __device__ __forceinline__ static void put_raw(Elem* p, int idx, float v) { p[idx] = f32_to_bf16(v); }
+  // One fragment (FE values) split into hi and lo, stored to memory.
+  __device__ __forceinline__ static void store_split(Elem* hi, Elem* lo, const float* v) {
+    Frag h, l;
+#pragma unroll
+    for (int i = 0; i < FE; ++i) {
+      __bf16 a, b;
+      split_bf16(v[i], a, b);
+      h[i] = a;
+      l[i] = b;
+    }
+    *reinterpret_cast<Frag*>(hi) = h;
+    *reinterpret_cast<Frag*>(lo) = l;
+  }
+  // FE raw elements gathered from LDS with a stride, stored as one fragment.
+  __device__ __forceinline__ static void gather(Elem* dst, const Elem* src, int stride) {
+    Frag h;
+#pragma unroll
+    for (int i = 0; i < FE; ++i) h[i] = src[i * stride];
+    *reinterpret_cast<Frag*>(dst) = h;
+  }
   // 8 consecutive raw input elements: copy bits to LDS, return values.
   __device__ __forceinline__ static void stage8(Elem* dst, const uint16_t* src, bool valid, float* f) {
-    uint4 r = valid ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+    uint4 r = *reinterpret_cast<const uint4*>(src);   // src is always a readable row
+    if (!valid) r = make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(dst) = r;
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
@@ -106,26 +133,35 @@ struct PolBF16 {
 struct PolF32 {
   using In = F32;
   using Elem = float;
+  using Frag = float;
   static constexpr int KSTEP = 4;
+  static constexpr int FE = 1;
   static constexpr int PAD = 4;
-  static constexpr int NSPLIT = 1;   // fp32 operands need no lo part
+  static constexpr int NSPLIT = 1;    // fp32 operands need no lo part
 
-  template <bool ALO, bool BLO>
-  __device__ __forceinline__ static void mma(floatx4& acc, const Elem* a_hi, const Elem*, int lda,
-                                             const Elem* b_hi, const Elem*, int ldb, int nks) {
+  __device__ __forceinline__ static floatx4 mma(Frag a, Frag b, floatx4 c) { return mfma_f32(a, b, c); }
+  __device__ __forceinline__ static Frag ld(const Elem* p) { return *p; }
+  __device__ __forceinline__ static Frag ld_in(const float* p) { return *p; }
+  __device__ __forceinline__ static void mma_lds(floatx4& acc, const Elem* a, int lda, const Elem* b, int ldb,
+                                                 int nks) {
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     for (int ks = 0; ks < nks; ++ks) {
-      const int off = ks * 4 + g;
-      acc = mfma_f32(a_hi[r * lda + off], b_hi[r * ldb + off], acc);
+      const int off = ks * KSTEP + g;
+      acc = mma(a[r * lda + off], b[r * ldb + off], acc);
     }
   }
   __device__ __forceinline__ static void put4(Elem* hi, Elem*, int idx, const float* v) {
     *reinterpret_cast<float4*>(hi + idx) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  __device__ __forceinline__ static void put_raw(Elem* p, int idx, float v) { p[idx] = v; }
+  __device__ __forceinline__ static void store_split(Elem* hi, Elem*, const float* v) { *hi = v[0]; }
+  __device__ __forceinline__ static void gather(Elem* dst, const Elem* src, int) { *dst = *src; }
   __device__ __forceinline__ static void stage8(Elem* dst, const float* src, bool valid, float* f) {
-    float4 a = valid ? reinterpret_cast<const float4*>(src)[0] : make_float4(0, 0, 0, 0);
-    float4 b = valid ? reinterpret_cast<const float4*>(src)[1] : make_float4(0, 0, 0, 0);
+    float4 a = reinterpret_cast<const float4*>(src)[0];   // src is always a readable row
+    float4 b = reinterpret_cast<const float4*>(src)[1];
+    if (!valid) {
+      a = make_float4(0, 0, 0, 0);
+      b = make_float4(0, 0, 0, 0);
+    }
     reinterpret_cast<float4*>(dst)[0] = a;
     reinterpret_cast<float4*>(dst)[1] = b;
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
@@ -133,15 +169,63 @@ struct PolF32 {
   }
 };
 
-// Workspace regions, indexed by (chunk slot, v-head).
+__device__ __forceinline__ uint32_t to_u32(uint16_t x) { return x; }
+__device__ __forceinline__ uint32_t to_u32(float x) { return __float_as_uint(x); }
+template <class In>
+__device__ __forceinline__ float from_u32(uint32_t x);
+template <>
+__device__ __forceinline__ float from_u32<BF16>(uint32_t x) { return __uint_as_float(x << 16); }
+template <>
+__device__ __forceinline__ float from_u32<F32>(uint32_t x) { return __uint_as_float(x); }
+
+// Workspace, all indexed by chunk slot (see locate_block):
+//   kt [slots][h_qk][D*C]          K^T fragments: blocks (dk tile mt, k-step ks)
+//   tb [slots][h_v][NSPLIT*C*C]    Tb fragments:  blocks (token tile mt, k-step ks, hi|lo)
+//   p  [slots][h_v][NSPLIT*C*C]    P fragments:   same order
+//   sc [slots][h_v][4][C] fp32     b rk | scale b rq | exp(gamma_C - gamma) rk | b_C
+// A fragment block is 64 lanes x FE elements, lane l holding row l % 16 and
+// k elements (l / 16) * FE .. + FE - 1 of its k-step, so one wave reads a
+// block with one contiguous 16-byte load per lane (bf16).
 struct ChunkWs {
-  float* tb;   // [slots][h_v][C][C]  T diag(beta), row-major
-  float* p;    // [slots][h_v][C][C]  P (scale folded in), row-major
-  float* sc;   // [slots][h_v][4][C]  b rk | scale b rq | exp(gamma_C - gamma) rk | b_C
+  void* kt;
+  void* tb;
+  void* p;
+  float* sc;
+};
+
+template <class Pol, int D, int C>
+struct WsLayout {
+  using Elem = typename Pol::Elem;
+  static constexpr int NKS_C = C / Pol::KSTEP;
+  static constexpr int BLK = 64 * Pol::FE;                            // elements per fragment block
+  static constexpr int64_t kt_elems = (int64_t)D * C;                 // per (slot, qk head)
+  static constexpr int64_t op_elems = (int64_t)Pol::NSPLIT * C * C;   // per (slot, v head)
+  // offset of block (mt, ks, split) of a Tb/P region, and of block (mt, ks) of a K^T region
+  __host__ __device__ static constexpr int op_block(int mt, int ks, int split) {
+    return ((mt * NKS_C + ks) * Pol::NSPLIT + split) * BLK;
+  }
+  __host__ __device__ static constexpr int kt_block(int mt, int ks) { return (mt * NKS_C + ks) * BLK; }
+  static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+  static size_t bytes(int64_t slots, int h_qk, int h_v) {
+    return al(sizeof(Elem) * slots * h_qk * kt_elems) + 2 * al(sizeof(Elem) * slots * h_v * op_elems) +
+           al(sizeof(float) * slots * h_v * 4 * C);
+  }
+  static ChunkWs carve(void* base, int64_t slots, int h_qk, int h_v) {
+    char* b = static_cast<char*>(base);
+    ChunkWs w;
+    w.kt = b;
+    b += al(sizeof(Elem) * slots * h_qk * kt_elems);
+    w.tb = b;
+    b += al(sizeof(Elem) * slots * h_v * op_elems);
+    w.p = b;
+    b += al(sizeof(Elem) * slots * h_v * op_elems);
+    w.sc = reinterpret_cast<float*>(b);
+    return w;
+  }
 };
 
 // ---------------------------------------------------------------------------
-// k_chunk_prep
+// k_chunk_prep: one workgroup per (chunk slot, v-head)
 // ---------------------------------------------------------------------------
 template <class Pol, int D, int C>
 __global__ __launch_bounds__(256) void k_chunk_prep(
@@ -150,24 +234,34 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     float scale, int use_l2, float l2_eps, int h_qk, int h_v,
     const int32_t* __restrict__ cu, int n_seq, int64_t t_total, ChunkWs ws) {
   using Elem = typename Pol::Elem;
+  using W = WsLayout<Pol, D, C>;
   constexpr int LDK = D + Pol::PAD;
   constexpr int LDC = C + 4;
   constexpr int NT = C / 16;
+  constexpr int FE = Pol::FE;
+  constexpr int NKS_C = C / Pol::KSTEP;
+  constexpr int KQ_BYTES = 2 * C * LDK * (int)sizeof(Elem);
+  constexpr int LT_BYTES = 2 * C * LDC * 4;
   static_assert(C % 16 == 0 && D % 16 == 0 && C <= 64, "tile shape");
-  static_assert(D % Pol::KSTEP == 0, "k-steps must tile D");
+  static_assert(D % Pol::KSTEP == 0 && C % Pol::KSTEP == 0, "k-steps must tile D and C");
 
-  __shared__ __attribute__((aligned(16))) Elem sK[C * LDK];
-  __shared__ __attribute__((aligned(16))) Elem sQ[C * LDK];
-  __shared__ float sGK[C * LDC], sGQ[C * LDC], sL[C * LDC], sT[C * LDC];
+  // K/Q rows during the Gram phase, then L and T (overlaid).
+  __shared__ __attribute__((aligned(16))) char smem[KQ_BYTES > LT_BYTES ? KQ_BYTES : LT_BYTES];
+  __shared__ float sGK[C * LDC], sGQ[C * LDC];
   __shared__ float s_rk[C], s_rq[C], s_gam[C], s_beta[C];
+  Elem* sK = reinterpret_cast<Elem*>(smem);
+  Elem* sQ = sK + C * LDK;
+  float* sL = reinterpret_cast<float*>(smem);
+  float* sT = sL + C * LDC;
 
   int seq, len;
   int64_t t0;
   if (!locate_block(cu, n_seq, t_total, C, blockIdx.x, seq, t0, len)) return;
-  const int hq = blockIdx.y;
+  const int h = blockIdx.y;
+  const int grp = h_v / h_qk;
+  const int hq = h / grp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int grp = h_v / h_qk;
 
   // 1. raw K, Q rows of the chunk into LDS (zero beyond len) and their L2 scales
   {
@@ -175,7 +269,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
     for (int r0 = 0; r0 < C; r0 += RPP) {
       const int row = r0 + tid / TPR, c8 = (tid % TPR) * 8;
       float kv[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < C) {
+      if (RPP <= C || row < C) {
         const bool valid = row < len;
         const int64_t tok = t0 + (valid ? row : 0);
         Pol::stage8(sK + row * LDK + c8, k + tok * k_stride + (int64_t)hq * D + c8, valid, kv);
@@ -186,7 +280,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
       for (int i = 0; i < 8; ++i) { sk += kv[i] * kv[i]; sq += qv[i] * qv[i]; }
       sk = group_sum<TPR>(sk);
       sq = group_sum<TPR>(sq);
-      if (row < C && tid % TPR == 0) {
+      if ((RPP <= C || row < C) && tid % TPR == 0) {
         const bool valid = row < len;
         s_rk[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f);
         s_rq[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f);
@@ -205,117 +299,139 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
       while ((ti + 1) * (ti + 2) / 2 <= idx) ++ti;
       const int tj = idx - ti * (ti + 1) / 2;
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      Pol::template mma<false, false>(acc, (isq ? sQ : sK) + ti * 16 * LDK, nullptr, LDK,
-                                      sK + tj * 16 * LDK, nullptr, LDK, D / Pol::KSTEP);
+      Pol::mma_lds(acc, (isq ? sQ : sK) + ti * 16 * LDK, LDK, sK + tj * 16 * LDK, LDK, D / Pol::KSTEP);
       float* dst = isq ? sGQ : sGK;
 #pragma unroll
       for (int i = 0; i < 4; ++i) dst[(16 * ti + 4 * g4 + i) * LDC + 16 * tj + r16] = acc[i];
     }
   }
+  // 3. the first v-head of a q/k head writes K^T of the chunk as fragments:
+  //    block (mt, ks), lane l: K[token ks*KSTEP + (l/16)*FE + e][dk 16 mt + l%16]
+  if (h % grp == 0) {
+    Elem* kt = static_cast<Elem*>(ws.kt) + ((int64_t)blockIdx.x * h_qk + hq) * W::kt_elems;
+    for (int f = tid; f < (D / 16) * NKS_C * 64; f += 256) {
+      const int l = f & 63, blk = f >> 6;
+      const int mt = blk / NKS_C, ks = blk % NKS_C;
+      const int dk = 16 * mt + (l & 15), tok0 = ks * Pol::KSTEP + (l >> 4) * FE;
+      Pol::gather(kt + W::kt_block(mt, ks) + l * FE, sK + tok0 * LDK + dk, LDK);
+    }
+  }
+  const int64_t unit = (int64_t)blockIdx.x * h_v + h;
+
+  // 4. decay: inclusive prefix sum of g over the chunk (padded tokens add 0)
+  if (wave == 0) {
+    float gv = 0.f, bv = 0.f;
+    if (lane < len) {
+      gv = g[(t0 + lane) * h_v + h];
+      bv = beta[(t0 + lane) * h_v + h];
+    }
+    float gam = gv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(gam, off, 64);
+      if (lane >= off) gam += o;
+    }
+    const float glast = __shfl(gam, C - 1, 64);
+    if (lane < C) {
+      float* sc_out = ws.sc + unit * (4 * C);
+      s_gam[lane] = gam;
+      s_beta[lane] = bv;
+      const float b = __expf(gam);
+      sc_out[lane] = b * s_rk[lane];
+      sc_out[C + lane] = scale * b * s_rq[lane];
+      sc_out[2 * C + lane] = __expf(glast - gam) * s_rk[lane];
+      sc_out[3 * C + lane] = __expf(glast);
+    }
+  }
+  __syncthreads();   // K/Q no longer read: L and T may overlay them
+
+  // 5. L (strictly lower) into LDS; P (lower incl. diagonal) to the workspace
+  //    as split fragments.  The decay is only formed for j <= i (masked
+  //    before the exponential).
+  for (int e = tid; e < C * C; e += 256) {
+    const int i = e / C, j = e % C;
+    float lv = 0.f;
+    if (j < i) lv = s_beta[i] * __expf(s_gam[i] - s_gam[j]) * s_rk[i] * s_rk[j] * sGK[i * LDC + j];
+    sL[i * LDC + j] = lv;
+  }
+  {
+    Elem* pb = static_cast<Elem*>(ws.p) + unit * W::op_elems;
+    for (int f = tid; f < NT * NKS_C * 64; f += 256) {
+      const int l = f & 63, blk = f >> 6;
+      const int mt = blk / NKS_C, ks = blk % NKS_C;
+      const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
+      float pv[FE];
+#pragma unroll
+      for (int e = 0; e < FE; ++e) {
+        const int j = j0 + e;
+        pv[e] = (j <= i) ? scale * __expf(s_gam[i] - s_gam[j]) * s_rq[i] * s_rk[j] * sGQ[i * LDC + j] : 0.f;
+      }
+      Pol::store_split(pb + W::op_block(mt, ks, 0) + l * FE, pb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
+                       pv);
+    }
+  }
   __syncthreads();
 
-  for (int gi = 0; gi < grp; ++gi) {
-    const int h = hq * grp + gi;
-    const int64_t unit = (int64_t)blockIdx.x * h_v + h;
-    float* sc_out = ws.sc + unit * (4 * C);
-
-    // 3. decay: inclusive prefix sum of g over the chunk (padded tokens add 0)
-    if (wave == 0) {
-      float gv = 0.f, bv = 0.f;
-      if (lane < len) {
-        gv = g[(t0 + lane) * h_v + h];
-        bv = beta[(t0 + lane) * h_v + h];
-      }
-      float gam = gv;
+  // 6. T = (I + L)^-1.  Diagonal 16x16 blocks: lane 16b + c owns column c of
+  //    block b and runs forward substitution T_i = e_i - sum_{j<i} L_ij T_j.
+  if (wave == 0 && lane < 16 * NT) {
+    const int b = lane >> 4, c = lane & 15, base = 16 * b;
+    float tcol[16];
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(gam, off, 64);
-        if (lane >= off) gam += o;
-      }
-      const float glast = __shfl(gam, C - 1, 64);
-      if (lane < C) {
-        s_gam[lane] = gam;
-        s_beta[lane] = bv;
-        const float b = __expf(gam);
-        sc_out[lane] = b * s_rk[lane];
-        sc_out[C + lane] = scale * b * s_rq[lane];
-        sc_out[2 * C + lane] = __expf(glast - gam) * s_rk[lane];
-        sc_out[3 * C + lane] = __expf(glast);
-      }
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < i; ++j) acc -= sL[(base + i) * LDC + base + j] * tcol[j];
+      tcol[i] = acc;
     }
-    __syncthreads();
-
-    // 4. L (strictly lower) into LDS; P (lower incl. diagonal) to the workspace.
-    //    The decay is only formed for j <= i (masked before the exponential).
-    {
-      float* p_out = ws.p + unit * (C * C);
-      for (int e = tid; e < C * C; e += 256) {
-        const int i = e / C, j = e % C;
-        float lv = 0.f, pv = 0.f;
-        if (j <= i) {
-          const float dec = __expf(s_gam[i] - s_gam[j]);
-          pv = scale * dec * s_rq[i] * s_rk[j] * sGQ[i * LDC + j];
-          if (j < i) lv = s_beta[i] * dec * s_rk[i] * s_rk[j] * sGK[i * LDC + j];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + c] = tcol[i];
+  }
+  __syncthreads();
+  //    Off-diagonal blocks by block diagonals d = bi - bj:
+  //    T_{bi,bj} = -T_{bi,bi} * sum_{kb=bj}^{bi-1} L_{bi,kb} T_{kb,bj}   (fp32 MFMA)
+  for (int d = 1; d < NT; ++d) {
+    for (int bi = d + wave; bi < NT; bi += 4) {
+      const int bj = bi - d;
+      floatx4 w = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = bj; kb < bi; ++kb) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int kk = 4 * ks + g4;
+          w = mfma_f32(sL[(16 * bi + r16) * LDC + 16 * kb + kk], sT[(16 * kb + kk) * LDC + 16 * bj + r16], w);
         }
-        sL[i * LDC + j] = lv;
-        p_out[e] = pv;
       }
+      // w holds W[4g+i][r16]; use it as the B operand with k = 4g + step
+      floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) t = mfma_f32(sT[(16 * bi + r16) * LDC + 16 * bi + 4 * g4 + s], w[s], t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * g4 + i) * LDC + 16 * bj + r16] = -t[i];
     }
     __syncthreads();
+  }
 
-    // 5. T = (I + L)^-1.  Diagonal 16x16 blocks: lane 16b + c owns column c of
-    //    block b and runs forward substitution T_i = e_i - sum_{j<i} L_ij T_j.
-    if (wave == 0 && lane < 16 * NT) {
-      const int b = lane >> 4, c = lane & 15, base = 16 * b;
-      float tcol[16];
+  // 7. Tb = T diag(beta) (zero above the diagonal) as split fragments
+  {
+    Elem* tb = static_cast<Elem*>(ws.tb) + unit * W::op_elems;
+    for (int f = tid; f < NT * NKS_C * 64; f += 256) {
+      const int l = f & 63, blk = f >> 6;
+      const int mt = blk / NKS_C, ks = blk % NKS_C;
+      const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
+      float tv[FE];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float acc = (i == c) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < i; ++j) acc -= sL[(base + i) * LDC + base + j] * tcol[j];
-        tcol[i] = acc;
+      for (int e = 0; e < FE; ++e) {
+        const int j = j0 + e;
+        tv[e] = (j <= i) ? sT[i * LDC + j] * s_beta[j] : 0.f;
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + c] = tcol[i];
+      Pol::store_split(tb + W::op_block(mt, ks, 0) + l * FE, tb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
+                       tv);
     }
-    __syncthreads();
-    //    Off-diagonal blocks by block diagonals d = bi - bj:
-    //    T_{bi,bj} = -T_{bi,bi} * sum_{kb=bj}^{bi-1} L_{bi,kb} T_{kb,bj}   (fp32 MFMA)
-    for (int d = 1; d < NT; ++d) {
-      for (int bi = d + wave; bi < NT; bi += 4) {
-        const int bj = bi - d;
-        floatx4 w = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = bj; kb < bi; ++kb) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int kk = 4 * ks + g4;
-            w = mfma_f32(sL[(16 * bi + r16) * LDC + 16 * kb + kk], sT[(16 * kb + kk) * LDC + 16 * bj + r16], w);
-          }
-        }
-        // w holds W[4g+i][r16]; use it as the B operand with k = 4g + step
-        floatx4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) t = mfma_f32(sT[(16 * bi + r16) * LDC + 16 * bi + 4 * g4 + s], w[s], t);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * g4 + i) * LDC + 16 * bj + r16] = -t[i];
-      }
-      __syncthreads();
-    }
-
-    // 6. Tb = T diag(beta) (zero above the diagonal) to the workspace
-    {
-      float* tb_out = ws.tb + unit * (C * C);
-      for (int e = tid; e < C * C; e += 256) {
-        const int i = e / C, j = e % C;
-        tb_out[e] = (j <= i) ? sT[i * LDC + j] * s_beta[j] : 0.f;
-      }
-    }
-    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// k_chunk_scan
+// k_chunk_scan: one workgroup per (sequence, v-head, 16-wide d_v tile)
 // ---------------------------------------------------------------------------
 template <class Pol, class EO, int D, int C>
 __global__ __launch_bounds__(256) void k_chunk_scan(
@@ -326,26 +442,33 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     typename EO::T* __restrict__ o, ChunkWs ws, int64_t n_blocks) {
   using Elem = typename Pol::Elem;
   using In = typename Pol::In;
+  using Frag = typename Pol::Frag;
+  using W = WsLayout<Pol, D, C>;
   constexpr int BV = 16;
   constexpr int NTILE = D / BV;
-  constexpr int LDK = D + Pol::PAD;    // rows of d_k elements
-  constexpr int LDT = C + Pol::PAD;    // rows of C token elements
-  constexpr int NMT = C / 16;          // token m-tiles (one per wave)
+  constexpr int LDK = D + Pol::PAD;    // LDS rows of d_k elements
+  constexpr int LDT = C + Pol::PAD;    // LDS rows of C token elements
+  constexpr int NMT = C / 16;          // token tiles (one per wave)
   constexpr int NST = D / 16;          // d_k tiles of the state
   constexpr int SPW = (NST + 3) / 4;   // state tiles per wave
+  constexpr int NSP = Pol::NSPLIT;
+  constexpr int FE = Pol::FE;
+  constexpr int KS = Pol::KSTEP;
+  constexpr int NKS_D = D / KS;        // k-steps over d_k
+  constexpr int NKS_C = C / KS;        // k-steps over the chunk's tokens
+  constexpr bool kAllWaves = NMT == 4;         // every wave owns a token tile
+  constexpr bool kAllTiles = NST % 4 == 0;     // every wave owns SPW state tiles
   static_assert(NMT <= 4, "one token tile per wave");
-  static_assert(C % Pol::KSTEP == 0 && D % Pol::KSTEP == 0, "k-steps must tile C and D");
+  static_assert(C % KS == 0 && D % KS == 0, "k-steps must tile C and D");
 
-  __shared__ __attribute__((aligned(16))) Elem sK[C * LDK];
-  __shared__ __attribute__((aligned(16))) Elem sQ[C * LDK];
-  __shared__ __attribute__((aligned(16))) Elem sKt[D * LDT];
-  __shared__ __attribute__((aligned(16))) Elem sTb[Pol::NSPLIT][C * LDT];
-  __shared__ __attribute__((aligned(16))) Elem sP[Pol::NSPLIT][C * LDT];
-  __shared__ __attribute__((aligned(16))) Elem sX[Pol::NSPLIT][BV * LDT];
-  __shared__ __attribute__((aligned(16))) Elem sU[Pol::NSPLIT][BV * LDT];
-  __shared__ __attribute__((aligned(16))) Elem sU2[Pol::NSPLIT][BV * LDT];
-  __shared__ __attribute__((aligned(16))) Elem sS[Pol::NSPLIT][BV * LDK];
-  __shared__ float s_c1[C], s_c2[C], s_c3[C], s_bc;
+  __shared__ __attribute__((aligned(16))) Elem sX[NSP * BV * LDT];
+  __shared__ __attribute__((aligned(16))) Elem sU[NSP * BV * LDT];
+  __shared__ __attribute__((aligned(16))) Elem sU2[NSP * BV * LDT];
+  __shared__ __attribute__((aligned(16))) Elem sS[NSP * BV * LDK];
+  Elem* const sX_lo = sX + (NSP - 1) * BV * LDT;
+  Elem* const sU_lo = sU + (NSP - 1) * BV * LDT;
+  Elem* const sU2_lo = sU2 + (NSP - 1) * BV * LDT;
+  Elem* const sS_lo = sS + (NSP - 1) * BV * LDK;
 
   // XCD-aware order: the dispatcher places block b on XCD b % 8, so give each
   // XCD a contiguous range of logical ids; the d_v tiles of one head then
@@ -362,6 +485,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
+  const bool tok_wave = kAllWaves || wave < NMT;
 
   // fp32 master state: tiles mt = wave + 4 j of S^T (rows d_k, columns d_v):
   // lane holds S[dv0 + r16][16 mt + 4 g4 + i].
@@ -371,125 +495,213 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   for (int j = 0; j < SPW; ++j) {
     const int mt = wave + 4 * j;
     Sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (mt < NST) {
+    if (kAllTiles || mt < NST) {
       if (init) {
         const float4 v4 = *reinterpret_cast<const float4*>(init + srow * D + 16 * mt + 4 * g4);
         Sacc[j] = floatx4{v4.x, v4.y, v4.z, v4.w};
       }
       const float tmp[4] = {Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]};
-      Pol::put4(sS[0], sS[Pol::NSPLIT - 1], r16 * LDK + 16 * mt + 4 * g4, tmp);
+      Pol::put4(sS, sS_lo, r16 * LDK + 16 * mt + 4 * g4, tmp);
     }
   }
 
   const int64_t start = seq_start(cu, s, t_total), end = seq_start(cu, s + 1, t_total);
   const int64_t nchunks = (end - start + C - 1) / C;
   const int64_t slot0 = start / C + s;
+  const int mrow = 16 * wave + r16;               // this lane's A-fragment row
+  const int orow0 = 16 * wave + 4 * g4;           // this lane's first output row
+
+  // This wave's operand fragments for one chunk (registers).  Rows of K, Q
+  // and V past the chunk's end re-read a valid row: their scalars (b rk,
+  // scale b rq, exp(.) rk) and their Tb rows and columns are exactly zero, so
+  // they contribute nothing and only need to be finite.
+  Frag kf[NKS_D], qf[NKS_D];             // K, Q rows of the token tile
+  Frag tbh[NKS_C], tbl[NKS_C];           // Tb rows (hi, lo)
+  Frag ph[NKS_C], pl[NKS_C];             // P rows (hi, lo)
+  Frag ktf[SPW][NKS_C];                  // K^T rows of the state tiles
+  float4 c1v = {0.f, 0.f, 0.f, 0.f}, c2v = c1v, c3v = c1v;   // b rk, scale b rq, exp(.) rk of 4 output rows
+  float bcv = 0.f;                       // b_C
+  uint32_t vraw[4] = {0u, 0u, 0u, 0u};   // raw V of the 4 output rows
+  int vlen = 0;
+  const int nks_w = (16 * wave + 16 + KS - 1) / KS;   // k-steps reaching this tile's last row
+
+#define GDN_LOAD_KQ(jj)                                                                                 \
+  do {                                                                                                 \
+    const int64_t t0_ = start + (jj) * C;                                                              \
+    const int len_ = static_cast<int>(end - t0_ < C ? end - t0_ : C);                                  \
+    if (tok_wave) {                                                                                    \
+      const int64_t row_ = t0_ + (mrow < len_ ? mrow : len_ - 1);                                      \
+      const typename In::T* kp_ = k + row_ * k_stride + (int64_t)hq * D + g4 * FE;                    \
+      const typename In::T* qp_ = q + row_ * q_stride + (int64_t)hq * D + g4 * FE;                    \
+      _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_D; ++ks_) {                                        \
+        kf[ks_] = Pol::ld_in(kp_ + ks_ * KS);                                                          \
+        qf[ks_] = Pol::ld_in(qp_ + ks_ * KS);                                                          \
+      }                                                                                                \
+      const float* sc_ = ws.sc + ((slot0 + (jj)) * h_v + h) * (4 * C);                                \
+      c1v = *reinterpret_cast<const float4*>(sc_ + orow0);                                             \
+      c2v = *reinterpret_cast<const float4*>(sc_ + C + orow0);                                         \
+      c3v = *reinterpret_cast<const float4*>(sc_ + 2 * C + orow0);                                     \
+      _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                               \
+        const int r_ = orow0 + i_;                                                                     \
+        vraw[i_] = to_u32(v[(t0_ + (r_ < len_ ? r_ : len_ - 1)) * v_stride + (int64_t)h * D + dv0 + r16]); \
+      }                                                                                                \
+      vlen = len_;                                                                                     \
+    }                                                                                                  \
+    bcv = ws.sc[((slot0 + (jj)) * h_v + h) * (4 * C) + 3 * C];                                         \
+  } while (0)
+#define GDN_LOAD_TB(jj)                                                                                \
+  do {                                                                                                 \
+    if (tok_wave) {                                                                                    \
+      const Elem* tb_ = static_cast<const Elem*>(ws.tb) + ((slot0 + (jj)) * h_v + h) * W::op_elems + lane * FE; \
+      _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_C; ++ks_) {                                        \
+        if (ks_ < nks_w) {                                                                             \
+          tbh[ks_] = Pol::ld(tb_ + W::op_block(wave, ks_, 0));                                         \
+          tbl[ks_] = Pol::ld(tb_ + W::op_block(wave, ks_, NSP - 1));                                   \
+        }                                                                                              \
+      }                                                                                                \
+    }                                                                                                  \
+  } while (0)
+#define GDN_LOAD_PKT(jj)                                                                               \
+  do {                                                                                                 \
+    if (tok_wave) {                                                                                    \
+      const Elem* p_ = static_cast<const Elem*>(ws.p) + ((slot0 + (jj)) * h_v + h) * W::op_elems + lane * FE; \
+      _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_C; ++ks_) {                                        \
+        if (ks_ < nks_w) {                                                                             \
+          ph[ks_] = Pol::ld(p_ + W::op_block(wave, ks_, 0));                                           \
+          pl[ks_] = Pol::ld(p_ + W::op_block(wave, ks_, NSP - 1));                                     \
+        }                                                                                              \
+      }                                                                                                \
+    }                                                                                                  \
+    const Elem* kt_ = static_cast<const Elem*>(ws.kt) + ((slot0 + (jj)) * h_qk + hq) * W::kt_elems + lane * FE; \
+    _Pragma("unroll") for (int j_ = 0; j_ < SPW; ++j_) {                                               \
+      if (kAllTiles || wave + 4 * j_ < NST) {                                                          \
+        _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_C; ++ks_)                                        \
+            ktf[j_][ks_] = Pol::ld(kt_ + W::kt_block(wave + 4 * j_, ks_));                             \
+      }                                                                                                \
+    }                                                                                                  \
+  } while (0)
+
+  if (nchunks > 0) {
+    GDN_LOAD_KQ(0);
+    GDN_LOAD_TB(0);
+    GDN_LOAD_PKT(0);
+  }
+  __syncthreads();
 
   for (int64_t j = 0; j < nchunks; ++j) {
     const int64_t t0 = start + j * C;
     const int len = static_cast<int>(end - t0 < C ? end - t0 : C);
-    const int64_t unit = (slot0 + j) * h_v + h;
+    // the chunk whose operands are fetched during this step (the last step
+    // re-reads its own chunk, so every load is unconditional)
+    const int64_t jn = j + 1 < nchunks ? j + 1 : j;
 
-    // ---- stage the chunk's operands ----
-    {
-      constexpr int TPR = D / 8, RPP = 256 / TPR;
-      for (int r0 = 0; r0 < C; r0 += RPP) {
-        const int row = r0 + tid / TPR, c8 = (tid % TPR) * 8;
-        if (row < C) {
-          const bool valid = row < len;
-          const int64_t tok = t0 + (valid ? row : 0);
-          float kv[8], qv[8];
-          Pol::stage8(sK + row * LDK + c8, k + tok * k_stride + (int64_t)hq * D + c8, valid, kv);
-          Pol::stage8(sQ + row * LDK + c8, q + tok * q_stride + (int64_t)hq * D + c8, valid, qv);
+    // ---- A: K S^T and Q S^T for token tile `wave`; X = V - diag(b rk) K S^T ----
+    floatx4 Oacc = {0.f, 0.f, 0.f, 0.f};
+    const float4 c3 = c3v;
+    const float bc = bcv;
+    if (tok_wave) {
+      floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) Pol::put_raw(sKt, (c8 + i) * LDT + row, kv[i]);
+      for (int ks = 0; ks < NKS_D; ++ks) {
+        const int off = r16 * LDK + ks * KS + g4 * FE;
+        const Frag shi = Pol::ld(sS + off);
+        ak = Pol::mma(kf[ks], shi, ak);
+        aq = Pol::mma(qf[ks], shi, aq);
+        if constexpr (NSP == 2) {
+          const Frag slo = Pol::ld(sS_lo + off);
+          ak = Pol::mma(kf[ks], slo, ak);
+          aq = Pol::mma(qf[ks], slo, aq);
         }
       }
-      const float* tb = ws.tb + unit * (C * C);
-      const float* pp = ws.p + unit * (C * C);
-      for (int e = tid * 4; e < C * C; e += 256 * 4) {
-        const int i = e / C, jj = e % C;
-        const float4 a = *reinterpret_cast<const float4*>(tb + e);
-        const float4 bq = *reinterpret_cast<const float4*>(pp + e);
-        const float av[4] = {a.x, a.y, a.z, a.w}, pv[4] = {bq.x, bq.y, bq.z, bq.w};
-        Pol::put4(sTb[0], sTb[Pol::NSPLIT - 1], i * LDT + jj, av);
-        Pol::put4(sP[0], sP[Pol::NSPLIT - 1], i * LDT + jj, pv);
-      }
-      const float* sc = ws.sc + unit * (4 * C);
-      if (tid < C) {
-        s_c1[tid] = sc[tid];
-        s_c2[tid] = sc[C + tid];
-        s_c3[tid] = sc[2 * C + tid];
-      }
-      if (tid == 0) s_bc = sc[3 * C];
-    }
-    __syncthreads();
-
-    // ---- K S^T and Q S^T for token tile `wave`; X = V - diag(b rk) K S^T ----
-    floatx4 Oacc = {0.f, 0.f, 0.f, 0.f};
-    if (wave < NMT) {
-      floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-      Pol::template mma<false, true>(ak, sK + 16 * wave * LDK, nullptr, LDK, sS[0], sS[Pol::NSPLIT - 1], LDK, D / Pol::KSTEP);
-      Pol::template mma<false, true>(aq, sQ + 16 * wave * LDK, nullptr, LDK, sS[0], sS[Pol::NSPLIT - 1], LDK, D / Pol::KSTEP);
+      const float c1[4] = {c1v.x, c1v.y, c1v.z, c1v.w}, c2[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
       float xv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * g4 + i;
-        const float vv = row < len ? In::load(v, (t0 + row) * v_stride + (int64_t)h * D + dv0 + r16) : 0.f;
-        xv[i] = vv - s_c1[row] * ak[i];
-        Oacc[i] = s_c2[row] * aq[i];
+        const float vv = (orow0 + i < vlen) ? from_u32<In>(vraw[i]) : 0.f;
+        xv[i] = vv - c1[i] * ak[i];
+        Oacc[i] = c2[i] * aq[i];
       }
-      Pol::put4(sX[0], sX[Pol::NSPLIT - 1], r16 * LDT + 16 * wave + 4 * g4, xv);
+      Pol::put4(sX, sX_lo, r16 * LDT + orow0, xv);
     }
+    GDN_LOAD_KQ(jn);   // K, Q, V and the scalars of this step are consumed
     __syncthreads();
 
-    // ---- U = Tb X (lower triangular: k up to the tile's last row) ----
-    const int nks_w = (16 * wave + 16 + Pol::KSTEP - 1) / Pol::KSTEP;
-    if (wave < NMT) {
+    // ---- B: U = Tb X (lower triangular: k up to the tile's last row) ----
+    if (tok_wave) {
       floatx4 au = {0.f, 0.f, 0.f, 0.f};
-      Pol::template mma<true, true>(au, sTb[0] + 16 * wave * LDT, sTb[Pol::NSPLIT - 1] + 16 * wave * LDT, LDT,
-                                    sX[0], sX[Pol::NSPLIT - 1], LDT, nks_w);
+#pragma unroll
+      for (int ks = 0; ks < NKS_C; ++ks) {
+        if (ks < nks_w) {
+          const int off = r16 * LDT + ks * KS + g4 * FE;
+          const Frag xh = Pol::ld(sX + off);
+          au = Pol::mma(tbh[ks], xh, au);
+          if constexpr (NSP == 2) {
+            const Frag xl = Pol::ld(sX_lo + off);
+            au = Pol::mma(tbh[ks], xl, au);
+            au = Pol::mma(tbl[ks], xh, au);
+          }
+        }
+      }
+      const float c3a[4] = {c3.x, c3.y, c3.z, c3.w};
       float u2[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u2[i] = s_c3[16 * wave + 4 * g4 + i] * au[i];
+      for (int i = 0; i < 4; ++i) u2[i] = c3a[i] * au[i];
       const float uv[4] = {au[0], au[1], au[2], au[3]};
-      Pol::put4(sU[0], sU[Pol::NSPLIT - 1], r16 * LDT + 16 * wave + 4 * g4, uv);
-      Pol::put4(sU2[0], sU2[Pol::NSPLIT - 1], r16 * LDT + 16 * wave + 4 * g4, u2);
+      Pol::put4(sU, sU_lo, r16 * LDT + orow0, uv);
+      Pol::put4(sU2, sU2_lo, r16 * LDT + orow0, u2);
     }
+    GDN_LOAD_TB(jn);
     __syncthreads();
 
-    // ---- O += P U; store rows of the chunk ----
-    if (wave < NMT) {
-      Pol::template mma<true, true>(Oacc, sP[0] + 16 * wave * LDT, sP[Pol::NSPLIT - 1] + 16 * wave * LDT, LDT,
-                                    sU[0], sU[Pol::NSPLIT - 1], LDT, nks_w);
+    // ---- C: O += P U, store rows; S^T <- b_C S^T + K^T U2 ----
+    if (tok_wave) {
+#pragma unroll
+      for (int ks = 0; ks < NKS_C; ++ks) {
+        if (ks < nks_w) {
+          const int off = r16 * LDT + ks * KS + g4 * FE;
+          const Frag uh = Pol::ld(sU + off);
+          Oacc = Pol::mma(ph[ks], uh, Oacc);
+          if constexpr (NSP == 2) {
+            const Frag ul = Pol::ld(sU_lo + off);
+            Oacc = Pol::mma(ph[ks], ul, Oacc);
+            Oacc = Pol::mma(pl[ks], uh, Oacc);
+          }
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * g4 + i;
+        const int row = orow0 + i;
         if (row < len) EO::store(o, (t0 + row) * ((int64_t)h_v * D) + (int64_t)h * D + dv0 + r16, Oacc[i]);
       }
     }
-    // ---- S^T <- b_C S^T + K^T U2 ----
-    const float bc = s_bc;
 #pragma unroll
     for (int jj = 0; jj < SPW; ++jj) {
       const int mt = wave + 4 * jj;
-      if (mt < NST) {
+      if (kAllTiles || mt < NST) {
         floatx4 acc = Sacc[jj] * bc;
-        Pol::template mma<false, true>(acc, sKt + 16 * mt * LDT, nullptr, LDT, sU2[0], sU2[Pol::NSPLIT - 1], LDT,
-                                       C / Pol::KSTEP);
+#pragma unroll
+        for (int ks = 0; ks < NKS_C; ++ks) {
+          const int off = r16 * LDT + ks * KS + g4 * FE;
+          acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2 + off), acc);
+          if constexpr (NSP == 2) acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2_lo + off), acc);
+        }
         Sacc[jj] = acc;
         const float tmp[4] = {acc[0], acc[1], acc[2], acc[3]};
-        Pol::put4(sS[0], sS[Pol::NSPLIT - 1], r16 * LDK + 16 * mt + 4 * g4, tmp);
+        Pol::put4(sS, sS_lo, r16 * LDK + 16 * mt + 4 * g4, tmp);
       }
     }
+    GDN_LOAD_PKT(jn);
     __syncthreads();
   }
+#undef GDN_LOAD_KQ
+#undef GDN_LOAD_TB
+#undef GDN_LOAD_PKT
 
   if (fin) {
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int mt = wave + 4 * j;
-      if (mt < NST)
+      if (kAllTiles || mt < NST)
         *reinterpret_cast<float4*>(fin + srow * D + 16 * mt + 4 * g4) =
             make_float4(Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
     }
@@ -499,40 +711,37 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-size_t chunk_ws_bytes(int h_v, int d, int chunk, int n_seq, int64_t t_total, int with_norm) {
-  const int64_t slots = block_slots(t_total, n_seq, chunk);
-  auto al = [](size_t b) { return (b + 255) & ~size_t(255); };
-  size_t bytes = 0;
-  bytes += al(sizeof(float) * slots * h_v * chunk * chunk);   // tb
-  bytes += al(sizeof(float) * slots * h_v * chunk * chunk);   // p
-  bytes += al(sizeof(float) * slots * h_v * 4 * chunk);       // scalars
-  if (with_norm) bytes += al(sizeof(float) * t_total * h_v * d);
-  return bytes;
+template <class Pol, int D, int C>
+static size_t ws_bytes_for(int h_qk, int h_v, int n_seq, int64_t t_total, int with_norm) {
+  const int64_t slots = block_slots(t_total, n_seq, C);
+  size_t b = WsLayout<Pol, D, C>::bytes(slots, h_qk, h_v);
+  if (with_norm) b += WsLayout<Pol, D, C>::al(sizeof(float) * t_total * h_v * D);
+  return b;
+}
+
+size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_seq, int64_t t_total,
+                      int with_norm) {
+  if (dt == GDN_BF16) return ws_bytes_for<PolBF16, 128, 64>(h_qk, h_v, n_seq, t_total, with_norm);
+  if (d == 128) return ws_bytes_for<PolF32, 128, 64>(h_qk, h_v, n_seq, t_total, with_norm);
+  return ws_bytes_for<PolF32, 16, 16>(h_qk, h_v, n_seq, t_total, with_norm);
 }
 
 template <class Pol, int D, int C>
 static hipError_t run_chunk(const ChunkArgs& a) {
   using T = typename Pol::In::T;
   const int64_t slots = block_slots(a.t_total, a.n_seq, C);
-  auto al = [](size_t b) { return (b + 255) & ~size_t(255); };
-  char* base = static_cast<char*>(a.workspace);
-  ChunkWs ws;
-  ws.tb = reinterpret_cast<float*>(base);
-  base += al(sizeof(float) * slots * a.h_v * C * C);
-  ws.p = reinterpret_cast<float*>(base);
-  base += al(sizeof(float) * slots * a.h_v * C * C);
-  ws.sc = reinterpret_cast<float*>(base);
-  base += al(sizeof(float) * slots * a.h_v * 4 * C);
-  float* o_pre = reinterpret_cast<float*>(base);   // pre-norm outputs when z is given
+  ChunkWs ws = WsLayout<Pol, D, C>::carve(a.workspace, slots, a.h_qk, a.h_v);
+  float* o_pre = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                          WsLayout<Pol, D, C>::bytes(slots, a.h_qk, a.h_v));
 
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   if (slots > 0) {
-    dim3 grid(static_cast<unsigned>(slots), a.h_qk);
-    hipLaunchKernelGGL((k_chunk_prep<Pol, D, C>), grid, dim3(256), 0, st, q, k, a.q_stride, a.k_stride,
-                       a.g, a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total, ws);
+    dim3 grid(static_cast<unsigned>(slots), a.h_v);
+    hipLaunchKernelGGL((k_chunk_prep<Pol, D, C>), grid, dim3(256), 0, st, q, k, a.q_stride, a.k_stride, a.g,
+                       a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

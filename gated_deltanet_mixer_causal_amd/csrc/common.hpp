@@ -39,6 +39,7 @@ struct BF16 {
   using T = uint16_t;
   static constexpr int kBytes = 2;
   __device__ __forceinline__ static float load(const T* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+  __device__ __forceinline__ static float cvt(T raw) { return bf16_bits_to_f32(raw); }
   __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
   // 8 consecutive elements (16 bytes) -> float[8]
   __device__ __forceinline__ static void load8(const T* p, float* out) {
@@ -64,6 +65,7 @@ struct F32 {
   using T = float;
   static constexpr int kBytes = 4;
   __device__ __forceinline__ static float load(const T* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static float cvt(T raw) { return raw; }
   __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = v; }
   __device__ __forceinline__ static void load8(const T* p, float* out) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];

@@ -21,6 +21,7 @@
 namespace gdn {
 
 constexpr int kConvBT = 32;            // tokens per prefill block (>= 3)
+constexpr int kConvGroup = 8;          // token loads issued together
 constexpr int kConvThreads = 256;
 constexpr int kConvCh = kConvThreads * 8;
 
@@ -79,13 +80,26 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
 #pragma unroll
   for (int c = 0; c < 8; ++c) { old0[c] = h0[c]; old1[c] = h1[c]; old2[c] = h2[c]; }
 
-  for (int t = 0; t < len; ++t) {
-    float cur[8], out[8];
-    E::load8(x + (t0 + t) * ld + c0, cur);
-    conv_out(wt, h0, h1, h2, cur, out);
-    E::store8(y + (t0 + t) * ld + c0, out);
+  // Tokens in groups of kConvGroup: every load of a group is issued before
+  // the first output of the group is computed (rows past the block's end
+  // re-read its last row and are not used).
+  for (int t = 0; t < len; t += kConvGroup) {
+    float cur[kConvGroup][8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) { h0[c] = h1[c]; h1[c] = h2[c]; h2[c] = cur[c]; }
+    for (int u = 0; u < kConvGroup; ++u) {
+      const int tt = t + u < len ? t + u : len - 1;
+      E::load8(x + (t0 + tt) * ld + c0, cur[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kConvGroup; ++u) {
+      if (t + u < len) {
+        float out[8];
+        conv_out(wt, h0, h1, h2, cur[u], out);
+        E::store8(y + (t0 + t + u) * ld + c0, out);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { h0[c] = h1[c]; h1[c] = h2[c]; h2[c] = cur[u][c]; }
+      }
+    }
   }
 
   if (p0 == 0) {

@@ -52,7 +52,8 @@ struct StepArgs {
   void* stream;
 };
 
-size_t chunk_ws_bytes(int h_v, int d, int chunk, int n_seq, int64_t t_total, int with_norm);
+size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_seq, int64_t t_total,
+                      int with_norm);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 hipError_t launch_recurrent_step(const StepArgs& a);
 hipError_t launch_conv1d(const void* x, gdn_dtype dt, const void* w, int channels, const int32_t* cu,

@@ -55,15 +55,20 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
   const int tid = threadIdx.x, l = tid % TPR, rg = tid / TPR;
   const int ca = 4 * l, cb = D / 2 + 4 * l;
 
+  constexpr bool FULL = RPP * PASSES == D;   // every pass row is a state row
   float* S = state + (static_cast<int64_t>(slot) * h_v + h) * D * D;
+  // Issue every load of the step before any use: the state rows of this
+  // thread, its q/k columns and the v entries of its rows.  Rows beyond D
+  // (small heads) read row 0 and are discarded.
   float4 sa[PASSES], sb[PASSES];
+  typename E::T vraw[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = rg + p * RPP;
-    if (row < D) {
-      sa[p] = *reinterpret_cast<const float4*>(S + row * D + ca);
-      sb[p] = *reinterpret_cast<const float4*>(S + row * D + cb);
-    }
+    const int rr = (FULL || row < D) ? row : 0;
+    sa[p] = *reinterpret_cast<const float4*>(S + rr * D + ca);
+    sb[p] = *reinterpret_cast<const float4*>(S + rr * D + cb);
+    vraw[p] = v[r * v_stride + h * D + rr];
   }
 
   float kk[8], qq[8];
@@ -71,6 +76,12 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
   load4<E>(k + r * k_stride + hq * D + cb, kk + 4);
   load4<E>(q + r * q_stride + hq * D + ca, qq);
   load4<E>(q + r * q_stride + hq * D + cb, qq + 4);
+  const float gv = g[static_cast<int64_t>(r) * h_v + h];
+  const float bt = beta[static_cast<int64_t>(r) * h_v + h];
+  const int64_t obase = (static_cast<int64_t>(r) * h_v + h) * D;
+  // gate of the fused norm, loaded with everything else (thread tid owns row tid)
+  typename E::T zraw = 0;
+  if (z) zraw = z[obase + (tid < D ? tid : 0)];
   float sk = 0.f, sq = 0.f, kq = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
@@ -82,8 +93,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
 #pragma unroll
   for (int i = 0; i < 8; ++i) { kk[i] *= rk; qq[i] *= rq; }
   kq *= rk * rq;
-  const float alpha = __expf(g[static_cast<int64_t>(r) * h_v + h]);
-  const float bt = beta[static_cast<int64_t>(r) * h_v + h];
+  const float alpha = __expf(gv);
 
   float orow[PASSES];
 #pragma unroll
@@ -95,11 +105,10 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
                sb[p].x * qq[4] + sb[p].y * qq[5] + sb[p].z * qq[6] + sb[p].w * qq[7];
     dk = group_sum<TPR>(dk);
     dq = group_sum<TPR>(dq);
-    if (row < D) {
-      const float vi = E::load(v, r * v_stride + h * D + row);
-      const float e = vi - alpha * dk;
-      const float be = bt * e;
-      orow[p] = scale * (alpha * dq + be * kq);
+    const float e = E::cvt(vraw[p]) - alpha * dk;
+    const float be = bt * e;
+    orow[p] = scale * (alpha * dq + be * kq);
+    if (FULL || row < D) {
       float4 na, nb;
       na.x = alpha * sa[p].x + be * kk[0]; na.y = alpha * sa[p].y + be * kk[1];
       na.z = alpha * sa[p].z + be * kk[2]; na.w = alpha * sa[p].w + be * kk[3];
@@ -110,13 +119,12 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
     }
   }
 
-  const int64_t obase = (static_cast<int64_t>(r) * h_v + h) * D;
   if (!z) {
     if (l == 0) {
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         const int row = rg + p * RPP;
-        if (row < D) EO::store(o, obase + row, orow[p]);
+        if (FULL || row < D) EO::store(o, obase + row, orow[p]);
       }
     }
     return;
@@ -128,7 +136,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = rg + p * RPP;
-      if (row < D) so[row] = orow[p];
+      if (FULL || row < D) so[row] = orow[p];
     }
   }
   __syncthreads();
@@ -141,8 +149,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
   for (int w = 0; w < NT / 64; ++w) tot += sred[w];
   if (tid < D) {
     const float rr = 1.0f / sqrtf(tot * (1.0f / D) + norm_eps);
-    const float zv = E::load(z, obase + tid);
-    EO::store(o, obase + tid, ov * rr * norm_w[tid] * silu(zv));
+    EO::store(o, obase + tid, ov * rr * norm_w[tid] * silu(E::cvt(zraw)));
   }
 }
 
