@@ -74,14 +74,18 @@ struct PolBF16 {
   __device__ __forceinline__ static Frag ld(const Elem* p) { return *reinterpret_cast<const Frag*>(p); }
   __device__ __forceinline__ static Frag ld_in(const uint16_t* p) { return *reinterpret_cast<const Frag*>(p); }
 
-  // acc += A B over nks k-steps, both operands in LDS (raw, no lo parts)
-  __device__ __forceinline__ static void mma_lds(floatx4& acc, const Elem* a, int lda, const Elem* b, int ldb,
-                                                 int nks) {
+  // acc += A B over NKS k-steps, both operands in LDS (raw, no lo parts)
+  template <int NKS>
+  __device__ __forceinline__ static void mma_lds(floatx4& acc, const Elem* a, int lda, const Elem* b, int ldb) {
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    for (int ks = 0; ks < nks; ++ks) {
-      const int off = ks * KSTEP + g * FE;
-      acc = mma(ld(a + r * lda + off), ld(b + r * ldb + off), acc);
+    Frag fa[NKS], fb[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      fa[ks] = ld(a + r * lda + ks * KSTEP + g * FE);
+      fb[ks] = ld(b + r * ldb + ks * KSTEP + g * FE);
     }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mma(fa[ks], fb[ks], acc);
   }
   // Split store of 4 consecutive values into LDS hi and lo arrays.
   __device__ __forceinline__ static void put4(Elem* hi, Elem* lo, int idx, const float* v) {
@@ -116,9 +120,16 @@ struct PolBF16 {
     for (int i = 0; i < FE; ++i) h[i] = src[i * stride];
     *reinterpret_cast<Frag*>(dst) = h;
   }
-  // 8 consecutive raw input elements: copy bits to LDS, return values.
-  __device__ __forceinline__ static void stage8(Elem* dst, const uint16_t* src, bool valid, float* f) {
-    uint4 r = *reinterpret_cast<const uint4*>(src);   // src is always a readable row
+  // 8 consecutive raw input elements: load (Raw8), then copy the bits to LDS
+  // and return the values (commit8), zeroed when the row is not valid.
+  struct Raw8 {
+    uint4 a;
+  };
+  __device__ __forceinline__ static Raw8 load8(const uint16_t* src) {
+    return Raw8{*reinterpret_cast<const uint4*>(src)};
+  }
+  __device__ __forceinline__ static void commit8(Elem* dst, Raw8 raw, bool valid, float* f) {
+    uint4 r = raw.a;
     if (!valid) r = make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(dst) = r;
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -142,22 +153,25 @@ struct PolF32 {
   __device__ __forceinline__ static floatx4 mma(Frag a, Frag b, floatx4 c) { return mfma_f32(a, b, c); }
   __device__ __forceinline__ static Frag ld(const Elem* p) { return *p; }
   __device__ __forceinline__ static Frag ld_in(const float* p) { return *p; }
-  __device__ __forceinline__ static void mma_lds(floatx4& acc, const Elem* a, int lda, const Elem* b, int ldb,
-                                                 int nks) {
+  template <int NKS>
+  __device__ __forceinline__ static void mma_lds(floatx4& acc, const Elem* a, int lda, const Elem* b, int ldb) {
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-    for (int ks = 0; ks < nks; ++ks) {
-      const int off = ks * KSTEP + g;
-      acc = mma(a[r * lda + off], b[r * ldb + off], acc);
-    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mma(a[r * lda + ks * KSTEP + g], b[r * ldb + ks * KSTEP + g], acc);
   }
   __device__ __forceinline__ static void put4(Elem* hi, Elem*, int idx, const float* v) {
     *reinterpret_cast<float4*>(hi + idx) = make_float4(v[0], v[1], v[2], v[3]);
   }
   __device__ __forceinline__ static void store_split(Elem* hi, Elem*, const float* v) { *hi = v[0]; }
   __device__ __forceinline__ static void gather(Elem* dst, const Elem* src, int) { *dst = *src; }
-  __device__ __forceinline__ static void stage8(Elem* dst, const float* src, bool valid, float* f) {
-    float4 a = reinterpret_cast<const float4*>(src)[0];   // src is always a readable row
-    float4 b = reinterpret_cast<const float4*>(src)[1];
+  struct Raw8 {
+    float4 a, b;
+  };
+  __device__ __forceinline__ static Raw8 load8(const float* src) {
+    return Raw8{reinterpret_cast<const float4*>(src)[0], reinterpret_cast<const float4*>(src)[1]};
+  }
+  __device__ __forceinline__ static void commit8(Elem* dst, Raw8 raw, bool valid, float* f) {
+    float4 a = raw.a, b = raw.b;
     if (!valid) {
       a = make_float4(0, 0, 0, 0);
       b = make_float4(0, 0, 0, 0);
@@ -263,17 +277,37 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
 
-  // 1. raw K, Q rows of the chunk into LDS (zero beyond len) and their L2 scales
+  // g and beta of this v-head over the chunk, one token per lane of wave 0,
+  // loaded before anything else (rows past the end re-read a valid row)
+  float gv = 0.f, bv = 0.f;
+  if (wave == 0) {
+    const int64_t tg = (t0 + (lane < len ? lane : len - 1)) * h_v + h;
+    gv = g[tg];
+    bv = beta[tg];
+    if (lane >= len) gv = bv = 0.f;
+  }
+
+  // 1. raw K, Q rows of the chunk into LDS (zero beyond len) and their L2
+  //    scales; every load is issued before the first one is used
   {
-    constexpr int TPR = D / 8, RPP = 256 / TPR;
-    for (int r0 = 0; r0 < C; r0 += RPP) {
-      const int row = r0 + tid / TPR, c8 = (tid % TPR) * 8;
+    constexpr int TPR = D / 8, RPP = 256 / TPR, NR = (C + RPP - 1) / RPP;
+    typename Pol::Raw8 kr[NR], qr[NR];
+#pragma unroll
+    for (int it = 0; it < NR; ++it) {
+      const int row = it * RPP + tid / TPR, c8 = (tid % TPR) * 8;
+      if (RPP <= C || row < C) {
+        const int64_t tok = t0 + (row < len ? row : 0);
+        kr[it] = Pol::load8(k + tok * k_stride + (int64_t)hq * D + c8);
+        qr[it] = Pol::load8(q + tok * q_stride + (int64_t)hq * D + c8);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NR; ++it) {
+      const int row = it * RPP + tid / TPR, c8 = (tid % TPR) * 8;
       float kv[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (RPP <= C || row < C) {
-        const bool valid = row < len;
-        const int64_t tok = t0 + (valid ? row : 0);
-        Pol::stage8(sK + row * LDK + c8, k + tok * k_stride + (int64_t)hq * D + c8, valid, kv);
-        Pol::stage8(sQ + row * LDK + c8, q + tok * q_stride + (int64_t)hq * D + c8, valid, qv);
+        Pol::commit8(sK + row * LDK + c8, kr[it], row < len, kv);
+        Pol::commit8(sQ + row * LDK + c8, qr[it], row < len, qv);
       }
       float sk = 0.f, sq = 0.f;
 #pragma unroll
@@ -289,20 +323,26 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   }
   __syncthreads();
 
-  // 2. lower-triangular tiles of K K^T and Q K^T (raw operands, exact products)
+  // 2. lower-triangular tiles of K K^T and Q K^T (raw operands, exact
+  //    products), tasks spread statically over the 4 waves
   {
-    constexpr int NLT = NT * (NT + 1) / 2;
-    for (int task = wave; task < 2 * NLT; task += 4) {
-      const bool isq = task >= NLT;
-      const int idx = isq ? task - NLT : task;
-      int ti = 0;
-      while ((ti + 1) * (ti + 2) / 2 <= idx) ++ti;
-      const int tj = idx - ti * (ti + 1) / 2;
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      Pol::mma_lds(acc, (isq ? sQ : sK) + ti * 16 * LDK, LDK, sK + tj * 16 * LDK, LDK, D / Pol::KSTEP);
-      float* dst = isq ? sGQ : sGK;
+    constexpr int NLT = NT * (NT + 1) / 2, NTASK = 2 * NLT, TPW = (NTASK + 3) / 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dst[(16 * ti + 4 * g4 + i) * LDC + 16 * tj + r16] = acc[i];
+    for (int it = 0; it < TPW; ++it) {
+      const int task = wave + 4 * it;
+      if (task < NTASK) {
+        const bool isq = task >= NLT;
+        const int idx = isq ? task - NLT : task;
+        int ti = 0;
+#pragma unroll
+        for (int r = 1; r < NT; ++r) ti += (r * (r + 1) / 2 <= idx) ? 1 : 0;
+        const int tj = idx - ti * (ti + 1) / 2;
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        Pol::template mma_lds<D / Pol::KSTEP>(acc, (isq ? sQ : sK) + ti * 16 * LDK, LDK, sK + tj * 16 * LDK, LDK);
+        float* dst = isq ? sGQ : sGK;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * ti + 4 * g4 + i) * LDC + 16 * tj + r16] = acc[i];
+      }
     }
   }
   // 3. the first v-head of a q/k head writes K^T of the chunk as fragments:
@@ -320,11 +360,6 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 
   // 4. decay: inclusive prefix sum of g over the chunk (padded tokens add 0)
   if (wave == 0) {
-    float gv = 0.f, bv = 0.f;
-    if (lane < len) {
-      gv = g[(t0 + lane) * h_v + h];
-      bv = beta[(t0 + lane) * h_v + h];
-    }
     float gam = gv;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -345,27 +380,33 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   }
   __syncthreads();   // K/Q no longer read: L and T may overlay them
 
-  // 5. L (strictly lower) into LDS; P (lower incl. diagonal) to the workspace
-  //    as split fragments.  The decay is only formed for j <= i (masked
-  //    before the exponential).
-  for (int e = tid; e < C * C; e += 256) {
-    const int i = e / C, j = e % C;
-    float lv = 0.f;
-    if (j < i) lv = s_beta[i] * __expf(s_gam[i] - s_gam[j]) * s_rk[i] * s_rk[j] * sGK[i * LDC + j];
-    sL[i * LDC + j] = lv;
-  }
+  // 5. One pass over the lower triangle in fragment order: each decay factor
+  //    exp(gamma_i - gamma_j) (formed only for j <= i, masked before the
+  //    exponential) serves both L (strictly lower, into LDS) and P (lower
+  //    incl. diagonal, split fragments to the workspace).
   {
     Elem* pb = static_cast<Elem*>(ws.p) + unit * W::op_elems;
     for (int f = tid; f < NT * NKS_C * 64; f += 256) {
       const int l = f & 63, blk = f >> 6;
       const int mt = blk / NKS_C, ks = blk % NKS_C;
       const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
-      float pv[FE];
+      float pv[FE], lv[FE];
+      if (j0 <= i) {
+        const float gi = s_gam[i], rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
 #pragma unroll
-      for (int e = 0; e < FE; ++e) {
-        const int j = j0 + e;
-        pv[e] = (j <= i) ? scale * __expf(s_gam[i] - s_gam[j]) * s_rq[i] * s_rk[j] * sGQ[i * LDC + j] : 0.f;
+        for (int e = 0; e < FE; ++e) {
+          const int j = j0 + e;
+          const float dec = (j <= i) ? __expf(gi - s_gam[j]) : 0.f;
+          const float rkj = s_rk[j];
+          pv[e] = scale * dec * rqi * rkj * sGQ[i * LDC + j];
+          lv[e] = (j < i) ? bi * dec * rki * rkj * sGK[i * LDC + j] : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < FE; ++e) pv[e] = lv[e] = 0.f;
       }
+#pragma unroll
+      for (int e = 0; e < FE; ++e) sL[i * LDC + j0 + e] = lv[e];
       Pol::store_split(pb + W::op_block(mt, ks, 0) + l * FE, pb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
                        pv);
     }
