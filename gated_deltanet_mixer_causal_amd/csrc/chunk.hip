@@ -24,7 +24,7 @@
 //                 (16x16 diagonal blocks by forward substitution in registers,
 //                 off-diagonal blocks by fp32 MFMA).  It writes Tb, P (split
 //                 into bf16 hi/lo) and K^T in matrix-core fragment order.
-//   k_chunk_scan  one workgroup per (sequence, v-head, 16-wide d_v tile),
+//   k_chunk_scan  one workgroup per (sequence, v-head, 16-wide d_v slice),
 //                 walking the sequence's chunks in order with its slice of the
 //                 state in fp32 registers; every contraction with the state or
 //                 a derived operand runs on the matrix cores.
@@ -472,9 +472,9 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 }
 
 // ---------------------------------------------------------------------------
-// k_chunk_scan: one workgroup per (sequence, v-head, 16-wide d_v tile)
+// k_chunk_scan: one workgroup per (sequence, v-head, d_v slice of 16*NV)
 // ---------------------------------------------------------------------------
-template <class Pol, class EO, int D, int C>
+template <class Pol, class EO, int D, int C, int NV>
 __global__ __launch_bounds__(256) void k_chunk_scan(
     const typename Pol::In::T* __restrict__ q, const typename Pol::In::T* __restrict__ k,
     const typename Pol::In::T* __restrict__ v, int64_t q_stride, int64_t k_stride, int64_t v_stride,
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   using In = typename Pol::In;
   using Frag = typename Pol::Frag;
   using W = WsLayout<Pol, D, C>;
-  constexpr int BV = 16;
+  constexpr int BV = 16 * NV;           // d_v columns of this workgroup (NV matrix-core N tiles)
   constexpr int NTILE = D / BV;
   constexpr int LDK = D + Pol::PAD;    // LDS rows of d_k elements
   constexpr int LDT = C + Pol::PAD;    // LDS rows of C token elements
@@ -528,21 +528,24 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   const int r16 = lane & 15, g4 = lane >> 4;
   const bool tok_wave = kAllWaves || wave < NMT;
 
-  // fp32 master state: tiles mt = wave + 4 j of S^T (rows d_k, columns d_v):
-  // lane holds S[dv0 + r16][16 mt + 4 g4 + i].
-  floatx4 Sacc[SPW];
-  const int64_t srow = ((int64_t)s * h_v + h) * D + dv0 + r16;   // state row of this lane
+  // fp32 master state: tiles (mt = wave + 4 j, nt) of S^T (rows d_k, columns
+  // d_v): lane holds S[dv0 + 16 nt + r16][16 mt + 4 g4 + i].
+  floatx4 Sacc[SPW][NV];
+  const int64_t srow = ((int64_t)s * h_v + h) * D + dv0 + r16;   // state row of this lane (nt = 0)
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int mt = wave + 4 * j;
-    Sacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (kAllTiles || mt < NST) {
-      if (init) {
-        const float4 v4 = *reinterpret_cast<const float4*>(init + srow * D + 16 * mt + 4 * g4);
-        Sacc[j] = floatx4{v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+    for (int nt = 0; nt < NV; ++nt) {
+      Sacc[j][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (kAllTiles || mt < NST) {
+        if (init) {
+          const float4 v4 = *reinterpret_cast<const float4*>(init + (srow + 16 * nt) * D + 16 * mt + 4 * g4);
+          Sacc[j][nt] = floatx4{v4.x, v4.y, v4.z, v4.w};
+        }
+        const float tmp[4] = {Sacc[j][nt][0], Sacc[j][nt][1], Sacc[j][nt][2], Sacc[j][nt][3]};
+        Pol::put4(sS, sS_lo, (16 * nt + r16) * LDK + 16 * mt + 4 * g4, tmp);
       }
-      const float tmp[4] = {Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]};
-      Pol::put4(sS, sS_lo, r16 * LDK + 16 * mt + 4 * g4, tmp);
     }
   }
 
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   Frag ktf[SPW][NKS_C];                  // K^T rows of the state tiles
   float4 c1v = {0.f, 0.f, 0.f, 0.f}, c2v = c1v, c3v = c1v;   // b rk, scale b rq, exp(.) rk of 4 output rows
   float bcv = 0.f;                       // b_C
-  uint32_t vraw[4] = {0u, 0u, 0u, 0u};   // raw V of the 4 output rows
+  uint32_t vraw[NV][4] = {};             // raw V of the 4 output rows, per N tile
   int vlen = 0;
   const int nks_w = (16 * wave + 16 + KS - 1) / KS;   // k-steps reaching this tile's last row
 
@@ -584,7 +587,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
       c3v = *reinterpret_cast<const float4*>(sc_ + 2 * C + orow0);                                     \
       _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                               \
         const int r_ = orow0 + i_;                                                                     \
-        vraw[i_] = to_u32(v[(t0_ + (r_ < len_ ? r_ : len_ - 1)) * v_stride + (int64_t)h * D + dv0 + r16]); \
+        const typename In::T* vp_ = v + (t0_ + (r_ < len_ ? r_ : len_ - 1)) * v_stride + (int64_t)h * D + dv0 + r16; \
+        _Pragma("unroll") for (int nt_ = 0; nt_ < NV; ++nt_) vraw[nt_][i_] = to_u32(vp_[16 * nt_]);  \
       }                                                                                                \
       vlen = len_;                                                                                     \
     }                                                                                                  \
@@ -637,59 +641,75 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     const int64_t jn = j + 1 < nchunks ? j + 1 : j;
 
     // ---- A: K S^T and Q S^T for token tile `wave`; X = V - diag(b rk) K S^T ----
-    floatx4 Oacc = {0.f, 0.f, 0.f, 0.f};
+    floatx4 Oacc[NV];
     const float4 c3 = c3v;
     const float bc = bcv;
     if (tok_wave) {
-      floatx4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+      floatx4 ak[NV], aq[NV];
+#pragma unroll
+      for (int nt = 0; nt < NV; ++nt) ak[nt] = aq[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS_D; ++ks) {
-        const int off = r16 * LDK + ks * KS + g4 * FE;
-        const Frag shi = Pol::ld(sS + off);
-        ak = Pol::mma(kf[ks], shi, ak);
-        aq = Pol::mma(qf[ks], shi, aq);
-        if constexpr (NSP == 2) {
-          const Frag slo = Pol::ld(sS_lo + off);
-          ak = Pol::mma(kf[ks], slo, ak);
-          aq = Pol::mma(qf[ks], slo, aq);
+#pragma unroll
+        for (int nt = 0; nt < NV; ++nt) {
+          const int off = (16 * nt + r16) * LDK + ks * KS + g4 * FE;
+          const Frag shi = Pol::ld(sS + off);
+          ak[nt] = Pol::mma(kf[ks], shi, ak[nt]);
+          aq[nt] = Pol::mma(qf[ks], shi, aq[nt]);
+          if constexpr (NSP == 2) {
+            const Frag slo = Pol::ld(sS_lo + off);
+            ak[nt] = Pol::mma(kf[ks], slo, ak[nt]);
+            aq[nt] = Pol::mma(qf[ks], slo, aq[nt]);
+          }
         }
       }
       const float c1[4] = {c1v.x, c1v.y, c1v.z, c1v.w}, c2[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
-      float xv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float vv = (orow0 + i < vlen) ? from_u32<In>(vraw[i]) : 0.f;
-        xv[i] = vv - c1[i] * ak[i];
-        Oacc[i] = c2[i] * aq[i];
+      for (int nt = 0; nt < NV; ++nt) {
+        float xv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float vv = (orow0 + i < vlen) ? from_u32<In>(vraw[nt][i]) : 0.f;
+          xv[i] = vv - c1[i] * ak[nt][i];
+          Oacc[nt][i] = c2[i] * aq[nt][i];
+        }
+        Pol::put4(sX, sX_lo, (16 * nt + r16) * LDT + orow0, xv);
       }
-      Pol::put4(sX, sX_lo, r16 * LDT + orow0, xv);
     }
     GDN_LOAD_KQ(jn);   // K, Q, V and the scalars of this step are consumed
     __syncthreads();
 
     // ---- B: U = Tb X (lower triangular: k up to the tile's last row) ----
     if (tok_wave) {
-      floatx4 au = {0.f, 0.f, 0.f, 0.f};
+      floatx4 au[NV];
+#pragma unroll
+      for (int nt = 0; nt < NV; ++nt) au[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS_C; ++ks) {
         if (ks < nks_w) {
-          const int off = r16 * LDT + ks * KS + g4 * FE;
-          const Frag xh = Pol::ld(sX + off);
-          au = Pol::mma(tbh[ks], xh, au);
-          if constexpr (NSP == 2) {
-            const Frag xl = Pol::ld(sX_lo + off);
-            au = Pol::mma(tbh[ks], xl, au);
-            au = Pol::mma(tbl[ks], xh, au);
+#pragma unroll
+          for (int nt = 0; nt < NV; ++nt) {
+            const int off = (16 * nt + r16) * LDT + ks * KS + g4 * FE;
+            const Frag xh = Pol::ld(sX + off);
+            au[nt] = Pol::mma(tbh[ks], xh, au[nt]);
+            if constexpr (NSP == 2) {
+              const Frag xl = Pol::ld(sX_lo + off);
+              au[nt] = Pol::mma(tbh[ks], xl, au[nt]);
+              au[nt] = Pol::mma(tbl[ks], xh, au[nt]);
+            }
           }
         }
       }
       const float c3a[4] = {c3.x, c3.y, c3.z, c3.w};
-      float u2[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u2[i] = c3a[i] * au[i];
-      const float uv[4] = {au[0], au[1], au[2], au[3]};
-      Pol::put4(sU, sU_lo, r16 * LDT + orow0, uv);
-      Pol::put4(sU2, sU2_lo, r16 * LDT + orow0, u2);
+      for (int nt = 0; nt < NV; ++nt) {
+        float u2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u2[i] = c3a[i] * au[nt][i];
+        const float uv[4] = {au[nt][0], au[nt][1], au[nt][2], au[nt][3]};
+        Pol::put4(sU, sU_lo, (16 * nt + r16) * LDT + orow0, uv);
+        Pol::put4(sU2, sU2_lo, (16 * nt + r16) * LDT + orow0, u2);
+      }
     }
     GDN_LOAD_TB(jn);
     __syncthreads();
@@ -699,36 +719,46 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
 #pragma unroll
       for (int ks = 0; ks < NKS_C; ++ks) {
         if (ks < nks_w) {
-          const int off = r16 * LDT + ks * KS + g4 * FE;
-          const Frag uh = Pol::ld(sU + off);
-          Oacc = Pol::mma(ph[ks], uh, Oacc);
-          if constexpr (NSP == 2) {
-            const Frag ul = Pol::ld(sU_lo + off);
-            Oacc = Pol::mma(ph[ks], ul, Oacc);
-            Oacc = Pol::mma(pl[ks], uh, Oacc);
+#pragma unroll
+          for (int nt = 0; nt < NV; ++nt) {
+            const int off = (16 * nt + r16) * LDT + ks * KS + g4 * FE;
+            const Frag uh = Pol::ld(sU + off);
+            Oacc[nt] = Pol::mma(ph[ks], uh, Oacc[nt]);
+            if constexpr (NSP == 2) {
+              const Frag ul = Pol::ld(sU_lo + off);
+              Oacc[nt] = Pol::mma(ph[ks], ul, Oacc[nt]);
+              Oacc[nt] = Pol::mma(pl[ks], uh, Oacc[nt]);
+            }
           }
         }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = orow0 + i;
-        if (row < len) EO::store(o, (t0 + row) * ((int64_t)h_v * D) + (int64_t)h * D + dv0 + r16, Oacc[i]);
+        if (row < len) {
+          const int64_t ob = (t0 + row) * ((int64_t)h_v * D) + (int64_t)h * D + dv0 + r16;
+#pragma unroll
+          for (int nt = 0; nt < NV; ++nt) EO::store(o, ob + 16 * nt, Oacc[nt][i]);
+        }
       }
     }
 #pragma unroll
     for (int jj = 0; jj < SPW; ++jj) {
       const int mt = wave + 4 * jj;
       if (kAllTiles || mt < NST) {
-        floatx4 acc = Sacc[jj] * bc;
 #pragma unroll
-        for (int ks = 0; ks < NKS_C; ++ks) {
-          const int off = r16 * LDT + ks * KS + g4 * FE;
-          acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2 + off), acc);
-          if constexpr (NSP == 2) acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2_lo + off), acc);
+        for (int nt = 0; nt < NV; ++nt) {
+          floatx4 acc = Sacc[jj][nt] * bc;
+#pragma unroll
+          for (int ks = 0; ks < NKS_C; ++ks) {
+            const int off = (16 * nt + r16) * LDT + ks * KS + g4 * FE;
+            acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2 + off), acc);
+            if constexpr (NSP == 2) acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2_lo + off), acc);
+          }
+          Sacc[jj][nt] = acc;
+          const float tmp[4] = {acc[0], acc[1], acc[2], acc[3]};
+          Pol::put4(sS, sS_lo, (16 * nt + r16) * LDK + 16 * mt + 4 * g4, tmp);
         }
-        Sacc[jj] = acc;
-        const float tmp[4] = {acc[0], acc[1], acc[2], acc[3]};
-        Pol::put4(sS, sS_lo, r16 * LDK + 16 * mt + 4 * g4, tmp);
       }
     }
     GDN_LOAD_PKT(jn);
@@ -742,9 +772,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
       const int mt = wave + 4 * j;
-      if (kAllTiles || mt < NST)
-        *reinterpret_cast<float4*>(fin + srow * D + 16 * mt + 4 * g4) =
-            make_float4(Sacc[j][0], Sacc[j][1], Sacc[j][2], Sacc[j][3]);
+      if (kAllTiles || mt < NST) {
+#pragma unroll
+        for (int nt = 0; nt < NV; ++nt)
+          *reinterpret_cast<float4*>(fin + (srow + 16 * nt) * D + 16 * mt + 4 * g4) =
+              make_float4(Sacc[j][nt][0], Sacc[j][nt][1], Sacc[j][nt][2], Sacc[j][nt][3]);
+      }
     }
   }
 }
@@ -786,9 +819,14 @@ static hipError_t run_chunk(const ChunkArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t nblk = (int64_t)a.n_seq * a.h_v * (D / 16);
+  // One 16-wide d_v tile per workgroup: a single long sequence has only
+  // heads x d_v/16 independent recurrences, and the chunk loop's latency, not
+  // the matrix cores, sets its pace, so the widest grid wins (two tiles per
+  // workgroup measured 1.6x slower on one 4096-token sequence).
+  constexpr int NV = 1;
+  const int64_t nblk = (int64_t)a.n_seq * a.h_v * (D / (16 * NV));
   if (a.z) {
-    hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
                        a.init, a.fin, o_pre, ws, nblk);
     hipError_t e = hipGetLastError();
@@ -799,11 +837,11 @@ static hipError_t run_chunk(const ChunkArgs& a) {
     return hipSuccess;
   }
   if (a.o_dt == GDN_BF16)
-    hipLaunchKernelGGL((k_chunk_scan<Pol, BF16, D, C>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_chunk_scan<Pol, BF16, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
                        a.init, a.fin, static_cast<uint16_t*>(a.o), ws, nblk);
   else
-    hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
                        a.init, a.fin, static_cast<float*>(a.o), ws, nblk);
   return hipGetLastError();
