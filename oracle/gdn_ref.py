@@ -14,16 +14,16 @@ What it computes (sources):
   * The conv runs over the raw projected q|k|v channels with dilation 1,
     SiLU, and an explicit history of raw inputs; the history of a sequence
     is its last three inputs (Flare core-design, short-convolution paragraph
-    and the prepared-interface list under it; "three-token GDN windows" in
-    the speculative snapshot paragraph).
+    and the prepared-interface list under it; the speculative snapshot
+    paragraph, which keeps a three-token conv window per position).
   * The gated delta rule: S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T
     and o_t = S_t q_t, with a_t = exp(g_t), applied token by token with an
     fp32 recurrent state on the device (Flare core-design, Qwen defaults
-    table "Main KV / GDN recurrence BF16 / FP32"; the GDN chunking paragraph
-    on BF16 intermediates and FP32 state).
+    table, the row giving bf16 main KV and fp32 GDN recurrence; the GDN
+    chunking paragraph on bf16 intermediates and an fp32 state).
   * A prefill call ends with the state after exactly the consumed tokens
-    (Flare core-design, exact consumed endpoints: "Endpoints are not rounded
-    to token groups").
+    (Flare core-design, the paragraph on exact consumed endpoints, which are
+    never rounded up to a token group).
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes of the repository):
