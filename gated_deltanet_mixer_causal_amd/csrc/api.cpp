@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <initializer_list>
 
 #include "../../include/gdn.h"
@@ -75,6 +76,23 @@ gdn_status check_qkv(const void* q, const void* k, const void* v, int64_t& q_str
 }
 
 }  // namespace
+
+namespace gdn {
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace gdn
 
 extern "C" {
 

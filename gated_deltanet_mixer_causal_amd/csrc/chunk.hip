@@ -18,12 +18,15 @@
 // U solves u_i = beta_i (v_i - a_i S_{i-1} k^_i) for every token of the chunk.
 //
 // Two kernels:
-//   k_chunk_prep  one workgroup per (chunk, v-head): the Gram matrices K K^T
-//                 and Q K^T on the matrix cores (raw operands, exact products),
-//                 the decay scalars, L, P and the unit-lower-triangular solve
-//                 (16x16 diagonal blocks by forward substitution in registers,
-//                 off-diagonal blocks by fp32 MFMA).  It writes Tb, P (split
-//                 into bf16 hi/lo) and K^T in matrix-core fragment order.
+//   k_chunk_prep  persistent workgroups over (chunk, q/k head) units: the
+//                 Gram matrices K K^T and Q K^T on the matrix cores (raw
+//                 operands, exact products) once per unit, then for each v-head
+//                 reading that q/k head the decay scalars, L, P and the
+//                 unit-lower-triangular solve (16x16 diagonal blocks by forward
+//                 substitution in registers, off-diagonal blocks by fp32 MFMA).
+//                 It writes Tb, P (split into bf16 hi/lo) and K^T in
+//                 matrix-core fragment order, and loads the next unit's K, Q
+//                 while it computes.
 //   k_chunk_scan  one workgroup per (sequence, v-head, 16-wide d_v slice),
 //                 walking the sequence's chunks in order with its slice of the
 //                 state in fp32 registers; every contraction with the state or
@@ -239,14 +242,14 @@ struct WsLayout {
 };
 
 // ---------------------------------------------------------------------------
-// k_chunk_prep: one workgroup per (chunk slot, v-head)
+// k_chunk_prep: persistent workgroups over (chunk slot, q/k head) units
 // ---------------------------------------------------------------------------
 template <class Pol, int D, int C>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const typename Pol::In::T* __restrict__ q, const typename Pol::In::T* __restrict__ k,
     int64_t q_stride, int64_t k_stride, const float* __restrict__ g, const float* __restrict__ beta,
     float scale, int use_l2, float l2_eps, int h_qk, int h_v,
-    const int32_t* __restrict__ cu, int n_seq, int64_t t_total, ChunkWs ws) {
+    const int32_t* __restrict__ cu, int n_seq, int64_t t_total, ChunkWs ws, int64_t n_slots) {
   using Elem = typename Pol::Elem;
   using W = WsLayout<Pol, D, C>;
   constexpr int LDK = D + Pol::PAD;
@@ -268,207 +271,244 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   float* sL = reinterpret_cast<float*>(smem);
   float* sT = sL + C * LDC;
 
-  int seq, len;
-  int64_t t0;
-  if (!locate_block(cu, n_seq, t_total, C, blockIdx.x, seq, t0, len)) return;
-  const int h = blockIdx.y;
-  const int grp = h_v / h_qk;
-  const int hq = h / grp;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int grp = h_v / h_qk;
+  constexpr int TPR = D / 8, RPP = 256 / TPR, NR = (C + RPP - 1) / RPP;
 
-  // g and beta of this v-head over the chunk, one token per lane of wave 0,
-  // loaded before anything else (rows past the end re-read a valid row)
-  float gv = 0.f, bv = 0.f;
-  if (wave == 0) {
-    const int64_t tg = (t0 + (lane < len ? lane : len - 1)) * h_v + h;
-    gv = g[tg];
-    bv = beta[tg];
-    if (lane >= len) gv = bv = 0.f;
-  }
-
-  // 1. raw K, Q rows of the chunk into LDS (zero beyond len) and their L2
-  //    scales; every load is issued before the first one is used
-  {
-    constexpr int TPR = D / 8, RPP = 256 / TPR, NR = (C + RPP - 1) / RPP;
-    typename Pol::Raw8 kr[NR], qr[NR];
+  // Persistent loop over units u = (chunk slot u / h_qk, q/k head u % h_qk),
+  // slot-major so that slots left empty by the slot numbering come last.  A
+  // unit loads K and Q and forms their Gram matrices once, then runs the
+  // decay, the solve and the outputs for each v-head that reads this q/k head.
+  // The raw K, Q rows and the g, beta values of the next unit are loaded
+  // while the current one is computed.
+  const int64_t n_units = n_slots * h_qk;
+  const int64_t stride = gridDim.x;
+  typename Pol::Raw8 kr[NR], qr[NR];   // raw rows of the unit to be committed next
+  float gn = 0.f, bn = 0.f;            // g, beta of its first v-head (wave 0, one token per lane)
+  int n_seq_i = 0, n_len = 0;
+  int64_t n_t0 = 0;
+  bool n_ok = false;
+  int64_t u = blockIdx.x;
+#define GDN_PREP_FETCH(uu)                                                                              \
+  do {                                                                                                 \
+    n_ok = (uu) < n_units && locate_block(cu, n_seq, t_total, C, (uu) / h_qk, n_seq_i, n_t0, n_len);     \
+    if (n_ok) {                                                                                        \
+      const int fq_ = static_cast<int>((uu) % h_qk);                                                   \
+      _Pragma("unroll") for (int it = 0; it < NR; ++it) {                                              \
+        const int row = it * RPP + tid / TPR, c8 = (tid % TPR) * 8;                                    \
+        if (RPP <= C || row < C) {                                                                     \
+          const int64_t tok = n_t0 + (row < n_len ? row : 0);                                          \
+          kr[it] = Pol::load8(k + tok * k_stride + (int64_t)fq_ * D + c8);                             \
+          qr[it] = Pol::load8(q + tok * q_stride + (int64_t)fq_ * D + c8);                             \
+        }                                                                                              \
+      }                                                                                                \
+      if (wave == 0) {                                                                                 \
+        const int64_t tg = (n_t0 + (lane < n_len ? lane : n_len - 1)) * h_v + (int64_t)fq_ * grp;      \
+        gn = g[tg];                                                                                    \
+        bn = beta[tg];                                                                                 \
+      }                                                                                                \
+    }                                                                                                  \
+  } while (0)
+  GDN_PREP_FETCH(u);
+  for (; u < n_units; u += stride) {
+    const bool ok = n_ok;
+    const int len = n_len;
+    const int64_t t0 = n_t0;
+    float gv = gn, bv = bn;
+    const int64_t cslot = u / h_qk;
+    const int hq = static_cast<int>(u % h_qk);
+    if (ok) {
+      // 1. commit the raw K, Q rows to LDS (zero beyond len) and form their
+      //    L2 scales
 #pragma unroll
-    for (int it = 0; it < NR; ++it) {
-      const int row = it * RPP + tid / TPR, c8 = (tid % TPR) * 8;
-      if (RPP <= C || row < C) {
-        const int64_t tok = t0 + (row < len ? row : 0);
-        kr[it] = Pol::load8(k + tok * k_stride + (int64_t)hq * D + c8);
-        qr[it] = Pol::load8(q + tok * q_stride + (int64_t)hq * D + c8);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < NR; ++it) {
-      const int row = it * RPP + tid / TPR, c8 = (tid % TPR) * 8;
-      float kv[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (RPP <= C || row < C) {
-        Pol::commit8(sK + row * LDK + c8, kr[it], row < len, kv);
-        Pol::commit8(sQ + row * LDK + c8, qr[it], row < len, qv);
-      }
-      float sk = 0.f, sq = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { sk += kv[i] * kv[i]; sq += qv[i] * qv[i]; }
-      sk = group_sum<TPR>(sk);
-      sq = group_sum<TPR>(sq);
-      if ((RPP <= C || row < C) && tid % TPR == 0) {
-        const bool valid = row < len;
-        s_rk[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f);
-        s_rq[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f);
-      }
-    }
-  }
-  __syncthreads();
-
-  // 2. lower-triangular tiles of K K^T and Q K^T (raw operands, exact
-  //    products), tasks spread statically over the 4 waves
-  {
-    constexpr int NLT = NT * (NT + 1) / 2, NTASK = 2 * NLT, TPW = (NTASK + 3) / 4;
-#pragma unroll
-    for (int it = 0; it < TPW; ++it) {
-      const int task = wave + 4 * it;
-      if (task < NTASK) {
-        const bool isq = task >= NLT;
-        const int idx = isq ? task - NLT : task;
-        int ti = 0;
-#pragma unroll
-        for (int r = 1; r < NT; ++r) ti += (r * (r + 1) / 2 <= idx) ? 1 : 0;
-        const int tj = idx - ti * (ti + 1) / 2;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        Pol::template mma_lds<D / Pol::KSTEP>(acc, (isq ? sQ : sK) + ti * 16 * LDK, LDK, sK + tj * 16 * LDK, LDK);
-        float* dst = isq ? sGQ : sGK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * ti + 4 * g4 + i) * LDC + 16 * tj + r16] = acc[i];
-      }
-    }
-  }
-  // 3. the first v-head of a q/k head writes K^T of the chunk as fragments:
-  //    block (mt, ks), lane l: K[token ks*KSTEP + (l/16)*FE + e][dk 16 mt + l%16]
-  if (h % grp == 0) {
-    Elem* kt = static_cast<Elem*>(ws.kt) + ((int64_t)blockIdx.x * h_qk + hq) * W::kt_elems;
-    for (int f = tid; f < (D / 16) * NKS_C * 64; f += 256) {
-      const int l = f & 63, blk = f >> 6;
-      const int mt = blk / NKS_C, ks = blk % NKS_C;
-      const int dk = 16 * mt + (l & 15), tok0 = ks * Pol::KSTEP + (l >> 4) * FE;
-      Pol::gather(kt + W::kt_block(mt, ks) + l * FE, sK + tok0 * LDK + dk, LDK);
-    }
-  }
-  const int64_t unit = (int64_t)blockIdx.x * h_v + h;
-
-  // 4. decay: inclusive prefix sum of g over the chunk (padded tokens add 0)
-  if (wave == 0) {
-    float gam = gv;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(gam, off, 64);
-      if (lane >= off) gam += o;
-    }
-    const float glast = __shfl(gam, C - 1, 64);
-    if (lane < C) {
-      float* sc_out = ws.sc + unit * (4 * C);
-      s_gam[lane] = gam;
-      s_beta[lane] = bv;
-      const float b = __expf(gam);
-      sc_out[lane] = b * s_rk[lane];
-      sc_out[C + lane] = scale * b * s_rq[lane];
-      sc_out[2 * C + lane] = __expf(glast - gam) * s_rk[lane];
-      sc_out[3 * C + lane] = __expf(glast);
-    }
-  }
-  __syncthreads();   // K/Q no longer read: L and T may overlay them
-
-  // 5. One pass over the lower triangle in fragment order: each decay factor
-  //    exp(gamma_i - gamma_j) (formed only for j <= i, masked before the
-  //    exponential) serves both L (strictly lower, into LDS) and P (lower
-  //    incl. diagonal, split fragments to the workspace).
-  {
-    Elem* pb = static_cast<Elem*>(ws.p) + unit * W::op_elems;
-    for (int f = tid; f < NT * NKS_C * 64; f += 256) {
-      const int l = f & 63, blk = f >> 6;
-      const int mt = blk / NKS_C, ks = blk % NKS_C;
-      const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
-      float pv[FE], lv[FE];
-      if (j0 <= i) {
-        const float gi = s_gam[i], rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
-#pragma unroll
-        for (int e = 0; e < FE; ++e) {
-          const int j = j0 + e;
-          const float dec = (j <= i) ? __expf(gi - s_gam[j]) : 0.f;
-          const float rkj = s_rk[j];
-          pv[e] = scale * dec * rqi * rkj * sGQ[i * LDC + j];
-          lv[e] = (j < i) ? bi * dec * rki * rkj * sGK[i * LDC + j] : 0.f;
+      for (int it = 0; it < NR; ++it) {
+        const int row = it * RPP + tid / TPR, c8 = (tid % TPR) * 8;
+        float kv[8] = {0, 0, 0, 0, 0, 0, 0, 0}, qv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (RPP <= C || row < C) {
+          Pol::commit8(sK + row * LDK + c8, kr[it], row < len, kv);
+          Pol::commit8(sQ + row * LDK + c8, qr[it], row < len, qv);
         }
-      } else {
+        float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int e = 0; e < FE; ++e) pv[e] = lv[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < FE; ++e) sL[i * LDC + j0 + e] = lv[e];
-      Pol::store_split(pb + W::op_block(mt, ks, 0) + l * FE, pb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
-                       pv);
-    }
-  }
-  __syncthreads();
-
-  // 6. T = (I + L)^-1.  Diagonal 16x16 blocks: lane 16b + c owns column c of
-  //    block b and runs forward substitution T_i = e_i - sum_{j<i} L_ij T_j.
-  if (wave == 0 && lane < 16 * NT) {
-    const int b = lane >> 4, c = lane & 15, base = 16 * b;
-    float tcol[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < i; ++j) acc -= sL[(base + i) * LDC + base + j] * tcol[j];
-      tcol[i] = acc;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + c] = tcol[i];
-  }
-  __syncthreads();
-  //    Off-diagonal blocks by block diagonals d = bi - bj:
-  //    T_{bi,bj} = -T_{bi,bi} * sum_{kb=bj}^{bi-1} L_{bi,kb} T_{kb,bj}   (fp32 MFMA)
-  for (int d = 1; d < NT; ++d) {
-    for (int bi = d + wave; bi < NT; bi += 4) {
-      const int bj = bi - d;
-      floatx4 w = {0.f, 0.f, 0.f, 0.f};
-      for (int kb = bj; kb < bi; ++kb) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int kk = 4 * ks + g4;
-          w = mfma_f32(sL[(16 * bi + r16) * LDC + 16 * kb + kk], sT[(16 * kb + kk) * LDC + 16 * bj + r16], w);
+        for (int i = 0; i < 8; ++i) { sk += kv[i] * kv[i]; sq += qv[i] * qv[i]; }
+        sk = group_sum<TPR>(sk);
+        sq = group_sum<TPR>(sq);
+        if ((RPP <= C || row < C) && tid % TPR == 0) {
+          const bool valid = row < len;
+          s_rk[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f);
+          s_rq[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f);
         }
       }
-      // w holds W[4g+i][r16]; use it as the B operand with k = 4g + step
-      floatx4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) t = mfma_f32(sT[(16 * bi + r16) * LDC + 16 * bi + 4 * g4 + s], w[s], t);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * g4 + i) * LDC + 16 * bj + r16] = -t[i];
     }
+    // the next unit's loads go out now and land during this unit's work
+    GDN_PREP_FETCH(u + stride);
+    if (!ok) continue;
     __syncthreads();
-  }
 
-  // 7. Tb = T diag(beta) (zero above the diagonal) as split fragments
-  {
-    Elem* tb = static_cast<Elem*>(ws.tb) + unit * W::op_elems;
-    for (int f = tid; f < NT * NKS_C * 64; f += 256) {
-      const int l = f & 63, blk = f >> 6;
-      const int mt = blk / NKS_C, ks = blk % NKS_C;
-      const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
-      float tv[FE];
+    // 2. lower-triangular tiles of K K^T and Q K^T (raw operands, exact
+    //    products), tasks spread statically over the 4 waves
+    {
+      constexpr int NLT = NT * (NT + 1) / 2, NTASK = 2 * NLT, TPW = (NTASK + 3) / 4;
 #pragma unroll
-      for (int e = 0; e < FE; ++e) {
-        const int j = j0 + e;
-        tv[e] = (j <= i) ? sT[i * LDC + j] * s_beta[j] : 0.f;
+      for (int it = 0; it < TPW; ++it) {
+        const int task = wave + 4 * it;
+        if (task < NTASK) {
+          const bool isq = task >= NLT;
+          const int idx = isq ? task - NLT : task;
+          int ti = 0;
+#pragma unroll
+          for (int r = 1; r < NT; ++r) ti += (r * (r + 1) / 2 <= idx) ? 1 : 0;
+          const int tj = idx - ti * (ti + 1) / 2;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          Pol::template mma_lds<D / Pol::KSTEP>(acc, (isq ? sQ : sK) + ti * 16 * LDK, LDK, sK + tj * 16 * LDK, LDK);
+          float* dst = isq ? sGQ : sGK;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[(16 * ti + 4 * g4 + i) * LDC + 16 * tj + r16] = acc[i];
+        }
       }
-      Pol::store_split(tb + W::op_block(mt, ks, 0) + l * FE, tb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
-                       tv);
+    }
+    // 3. K^T of the chunk as fragments:
+    //    block (mt, ks), lane l: K[token ks*KSTEP + (l/16)*FE + e][dk 16 mt + l%16]
+    {
+      Elem* kt = static_cast<Elem*>(ws.kt) + (cslot * h_qk + hq) * W::kt_elems;
+      for (int f = tid; f < (D / 16) * NKS_C * 64; f += 256) {
+        const int l = f & 63, blk = f >> 6;
+        const int mt = blk / NKS_C, ks = blk % NKS_C;
+        const int dk = 16 * mt + (l & 15), tok0 = ks * Pol::KSTEP + (l >> 4) * FE;
+        Pol::gather(kt + W::kt_block(mt, ks) + l * FE, sK + tok0 * LDK + dk, LDK);
+      }
+    }
+
+    for (int vh = 0; vh < grp; ++vh) {
+      const int h = hq * grp + vh;
+      const int64_t unit = cslot * h_v + h;
+      // g, beta of the following v-head of the group, loaded now for later
+      float g_next = 0.f, b_next = 0.f;
+      if (wave == 0 && vh + 1 < grp) {
+        const int64_t tg = (t0 + (lane < len ? lane : len - 1)) * h_v + h + 1;
+        g_next = g[tg];
+        b_next = beta[tg];
+      }
+      if (lane >= len) gv = bv = 0.f;
+
+      // 4. decay: inclusive prefix sum of g over the chunk (padded tokens add 0)
+      if (wave == 0) {
+        float gam = gv;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const float o = __shfl_up(gam, off, 64);
+          if (lane >= off) gam += o;
+        }
+        const float glast = __shfl(gam, C - 1, 64);
+        if (lane < C) {
+          float* sc_out = ws.sc + unit * (4 * C);
+          s_gam[lane] = gam;
+          s_beta[lane] = bv;
+          const float b = __expf(gam);
+          sc_out[lane] = b * s_rk[lane];
+          sc_out[C + lane] = scale * b * s_rq[lane];
+          sc_out[2 * C + lane] = __expf(glast - gam) * s_rk[lane];
+          sc_out[3 * C + lane] = __expf(glast);
+        }
+      }
+      __syncthreads();   // K/Q no longer read: L and T may overlay them
+
+      // 5. One pass over the lower triangle in fragment order: each decay factor
+      //    exp(gamma_i - gamma_j) (formed only for j <= i, masked before the
+      //    exponential) serves both L (strictly lower, into LDS) and P (lower
+      //    incl. diagonal, split fragments to the workspace).
+      {
+        Elem* pb = static_cast<Elem*>(ws.p) + unit * W::op_elems;
+        for (int f = tid; f < NT * NKS_C * 64; f += 256) {
+          const int l = f & 63, blk = f >> 6;
+          const int mt = blk / NKS_C, ks = blk % NKS_C;
+          const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
+          float pv[FE], lv[FE];
+          if (j0 <= i) {
+            const float gi = s_gam[i], rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
+#pragma unroll
+            for (int e = 0; e < FE; ++e) {
+              const int j = j0 + e;
+              const float dec = (j <= i) ? __expf(gi - s_gam[j]) : 0.f;
+              const float rkj = s_rk[j];
+              pv[e] = scale * dec * rqi * rkj * sGQ[i * LDC + j];
+              lv[e] = (j < i) ? bi * dec * rki * rkj * sGK[i * LDC + j] : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < FE; ++e) pv[e] = lv[e] = 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < FE; ++e) sL[i * LDC + j0 + e] = lv[e];
+          Pol::store_split(pb + W::op_block(mt, ks, 0) + l * FE, pb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
+                           pv);
+        }
+      }
+      __syncthreads();
+
+      // 6. T = (I + L)^-1.  Diagonal 16x16 blocks: lane 16b + c owns column c of
+      //    block b and runs forward substitution T_i = e_i - sum_{j<i} L_ij T_j.
+      if (wave == 0 && lane < 16 * NT) {
+        const int b = lane >> 4, c = lane & 15, base = 16 * b;
+        float tcol[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float acc = (i == c) ? 1.f : 0.f;
+#pragma unroll
+          for (int j = 0; j < i; ++j) acc -= sL[(base + i) * LDC + base + j] * tcol[j];
+          tcol[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(base + i) * LDC + base + c] = tcol[i];
+      }
+      __syncthreads();
+      //    Off-diagonal blocks by block diagonals d = bi - bj:
+      //    T_{bi,bj} = -T_{bi,bi} * sum_{kb=bj}^{bi-1} L_{bi,kb} T_{kb,bj}   (fp32 MFMA)
+      for (int d = 1; d < NT; ++d) {
+        for (int bi = d + wave; bi < NT; bi += 4) {
+          const int bj = bi - d;
+          floatx4 w = {0.f, 0.f, 0.f, 0.f};
+          for (int kb = bj; kb < bi; ++kb) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+              const int kk = 4 * ks + g4;
+              w = mfma_f32(sL[(16 * bi + r16) * LDC + 16 * kb + kk], sT[(16 * kb + kk) * LDC + 16 * bj + r16], w);
+            }
+          }
+          // w holds W[4g+i][r16]; use it as the B operand with k = 4g + step
+          floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) t = mfma_f32(sT[(16 * bi + r16) * LDC + 16 * bi + 4 * g4 + s], w[s], t);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sT[(16 * bi + 4 * g4 + i) * LDC + 16 * bj + r16] = -t[i];
+        }
+        __syncthreads();
+      }
+
+      // 7. Tb = T diag(beta) (zero above the diagonal) as split fragments
+      {
+        Elem* tb = static_cast<Elem*>(ws.tb) + unit * W::op_elems;
+        for (int f = tid; f < NT * NKS_C * 64; f += 256) {
+          const int l = f & 63, blk = f >> 6;
+          const int mt = blk / NKS_C, ks = blk % NKS_C;
+          const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
+          float tv[FE];
+#pragma unroll
+          for (int e = 0; e < FE; ++e) {
+            const int j = j0 + e;
+            tv[e] = (j <= i) ? sT[i * LDC + j] * s_beta[j] : 0.f;
+          }
+          Pol::store_split(tb + W::op_block(mt, ks, 0) + l * FE, tb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
+                           tv);
+        }
+      }
+      __syncthreads();   // L, T, gamma and beta are rewritten by the next v-head or unit
+      gv = g_next;
+      bv = b_next;
     }
   }
+#undef GDN_PREP_FETCH
 }
 
 // ---------------------------------------------------------------------------
@@ -515,7 +555,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   // XCD a contiguous range of logical ids; the d_v tiles of one head then
   // share an L2 and its K/Q/Tb/P reads.
   const int64_t b = blockIdx.x;
-  const int64_t lid = (n_blocks % 8 == 0) ? (b % 8) * (n_blocks / 8) + b / 8 : b;
+  const int64_t lid = xcd_order(b, n_blocks);
   const int tile = static_cast<int>(lid % NTILE);
   const int64_t sh = lid / NTILE;
   const int h = static_cast<int>(sh % h_v);
@@ -813,9 +853,20 @@ static hipError_t run_chunk(const ChunkArgs& a) {
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   if (slots > 0) {
-    dim3 grid(static_cast<unsigned>(slots), a.h_v);
-    hipLaunchKernelGGL((k_chunk_prep<Pol, D, C>), grid, dim3(256), 0, st, q, k, a.q_stride, a.k_stride, a.g,
-                       a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total, ws);
+    // persistent grid: as many workgroups as can be resident at once, so
+    // every workgroup runs from the start and the unit loop balances
+    static const int per_cu = [] {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_chunk_prep<Pol, D, C>, 256, 0) != hipSuccess || n < 1)
+        n = 1;
+      return n;
+    }();
+    const int64_t units = slots * a.h_qk;
+    const int64_t resident = static_cast<int64_t>(per_cu) * device_cu_count();
+    const int64_t grid = units < resident ? units : resident;
+    hipLaunchKernelGGL((k_chunk_prep<Pol, D, C>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, q, k,
+                       a.q_stride, a.k_stride, a.g, a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu,
+                       a.n_seq, a.t_total, ws, slots);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -42,6 +42,18 @@ struct BF16 {
   __device__ __forceinline__ static float cvt(T raw) { return bf16_bits_to_f32(raw); }
   __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
   // 8 consecutive elements (16 bytes) -> float[8]
+  // 8 consecutive elements as raw bits (one 16-byte access)
+  using Vec = uint4;
+  __device__ __forceinline__ static Vec ld_vec(const T* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static void st_vec(T* p, Vec v) { *reinterpret_cast<uint4*>(p) = v; }
+  __device__ __forceinline__ static void unpack8(Vec r, float* out) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
   __device__ __forceinline__ static void load8(const T* p, float* out) {
     const uint4 r = *reinterpret_cast<const uint4*>(p);
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -67,6 +79,20 @@ struct F32 {
   __device__ __forceinline__ static float load(const T* p, int64_t i) { return p[i]; }
   __device__ __forceinline__ static float cvt(T raw) { return raw; }
   __device__ __forceinline__ static void store(T* p, int64_t i, float v) { p[i] = v; }
+  struct Vec {
+    float4 a, b;
+  };
+  __device__ __forceinline__ static Vec ld_vec(const T* p) {
+    return Vec{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+  }
+  __device__ __forceinline__ static void st_vec(T* p, Vec v) {
+    reinterpret_cast<float4*>(p)[0] = v.a;
+    reinterpret_cast<float4*>(p)[1] = v.b;
+  }
+  __device__ __forceinline__ static void unpack8(Vec v, float* out) {
+    out[0] = v.a.x; out[1] = v.a.y; out[2] = v.a.z; out[3] = v.a.w;
+    out[4] = v.b.x; out[5] = v.b.y; out[6] = v.b.z; out[7] = v.b.w;
+  }
   __device__ __forceinline__ static void load8(const T* p, float* out) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
     const float4 b = reinterpret_cast<const float4*>(p)[1];
@@ -121,6 +147,15 @@ __device__ __forceinline__ bool locate_block(const int32_t* cu, int n_seq, int64
 
 __host__ __device__ constexpr int64_t block_slots(int64_t t_total, int n_seq, int blk) {
   return (t_total + blk - 1) / blk + n_seq;
+}
+
+// XCD-aware order.  The dispatcher hands workgroup b of a 1-D grid to XCD
+// b % 8, and each of the 8 XCDs has its own L2.  This bijection of [0, n)
+// gives XCD x the contiguous logical range [start(x), start(x) + count(x)),
+// so logical neighbours (which share operands) run under one L2.
+__device__ __forceinline__ int64_t xcd_order(int64_t b, int64_t n) {
+  const int64_t x = b % 8, r = b / 8, q = n / 8, m = n % 8;
+  return x * q + (x < m ? x : m) + r;
 }
 
 }  // namespace gdn

@@ -52,6 +52,9 @@ struct StepArgs {
   void* stream;
 };
 
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_seq, int64_t t_total,
                       int with_norm);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
