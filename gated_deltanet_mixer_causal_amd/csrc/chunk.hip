@@ -196,6 +196,7 @@ template <>
 __device__ __forceinline__ float from_u32<F32>(uint32_t x) { return __uint_as_float(x); }
 
 // Workspace, all indexed by chunk slot (see locate_block):
+//   kq [slots][h_qk][2][C*D]       K, Q fragments (raw): blocks (token tile mt, d_k k-step ks)
 //   kt [slots][h_qk][D*C]          K^T fragments: blocks (dk tile mt, k-step ks)
 //   tb [slots][h_v][NSPLIT*C*C]    Tb fragments:  blocks (token tile mt, k-step ks, hi|lo)
 //   p  [slots][h_v][NSPLIT*C*C]    P fragments:   same order
@@ -204,6 +205,7 @@ __device__ __forceinline__ float from_u32<F32>(uint32_t x) { return __uint_as_fl
 // k elements (l / 16) * FE .. + FE - 1 of its k-step, so one wave reads a
 // block with one contiguous 16-byte load per lane (bf16).
 struct ChunkWs {
+  void* kq;
   void* kt;
   void* tb;
   void* p;
@@ -215,21 +217,29 @@ struct WsLayout {
   using Elem = typename Pol::Elem;
   static constexpr int NKS_C = C / Pol::KSTEP;
   static constexpr int BLK = 64 * Pol::FE;                            // elements per fragment block
+  static constexpr int NKS_D = D / Pol::KSTEP;
   static constexpr int64_t kt_elems = (int64_t)D * C;                 // per (slot, qk head)
+  static constexpr int64_t kq_elems = 2 * (int64_t)C * D;             // per (slot, qk head): K then Q
   static constexpr int64_t op_elems = (int64_t)Pol::NSPLIT * C * C;   // per (slot, v head)
   // offset of block (mt, ks, split) of a Tb/P region, and of block (mt, ks) of a K^T region
   __host__ __device__ static constexpr int op_block(int mt, int ks, int split) {
     return ((mt * NKS_C + ks) * Pol::NSPLIT + split) * BLK;
   }
   __host__ __device__ static constexpr int kt_block(int mt, int ks) { return (mt * NKS_C + ks) * BLK; }
+  // block (token tile mt, d_k k-step ks) of the K (which 0) or Q (which 1) half of a kq region
+  __host__ __device__ static constexpr int kq_block(int which, int mt, int ks) {
+    return which * C * D + (mt * NKS_D + ks) * BLK;
+  }
   static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
   static size_t bytes(int64_t slots, int h_qk, int h_v) {
-    return al(sizeof(Elem) * slots * h_qk * kt_elems) + 2 * al(sizeof(Elem) * slots * h_v * op_elems) +
-           al(sizeof(float) * slots * h_v * 4 * C);
+    return al(sizeof(Elem) * slots * h_qk * kq_elems) + al(sizeof(Elem) * slots * h_qk * kt_elems) +
+           2 * al(sizeof(Elem) * slots * h_v * op_elems) + al(sizeof(float) * slots * h_v * 4 * C);
   }
   static ChunkWs carve(void* base, int64_t slots, int h_qk, int h_v) {
     char* b = static_cast<char*>(base);
     ChunkWs w;
+    w.kq = b;
+    b += al(sizeof(Elem) * slots * h_qk * kq_elems);
     w.kt = b;
     b += al(sizeof(Elem) * slots * h_qk * kt_elems);
     w.tb = b;
@@ -257,6 +267,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   constexpr int NT = C / 16;
   constexpr int FE = Pol::FE;
   constexpr int NKS_C = C / Pol::KSTEP;
+  using Frag = typename Pol::Frag;
   constexpr int KQ_BYTES = 2 * C * LDK * (int)sizeof(Elem);
   constexpr int LT_BYTES = 2 * C * LDC * 4;
   static_assert(C % 16 == 0 && D % 16 == 0 && C <= 64, "tile shape");
@@ -368,8 +379,21 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         }
       }
     }
-    // 3. K^T of the chunk as fragments:
+    // 3. K and Q of the chunk as the scan's A fragments (block (token tile mt,
+    //    d_k k-step ks), lane l: row 16 mt + l%16, d_k ks*KSTEP + (l/16)*FE + e;
+    //    rows past the chunk's end are zero), so the scan reads contiguous
+    //    blocks instead of rows spread over the input, and K^T as fragments:
     //    block (mt, ks), lane l: K[token ks*KSTEP + (l/16)*FE + e][dk 16 mt + l%16]
+    {
+      Elem* kqb = static_cast<Elem*>(ws.kq) + (cslot * h_qk + hq) * W::kq_elems;
+      constexpr int NKS_D = D / Pol::KSTEP;
+      for (int f = tid; f < 2 * NT * NKS_D * 64; f += 256) {
+        const int l = f & 63, blk = f >> 6;
+        const int which = blk / (NT * NKS_D), mt = (blk / NKS_D) % NT, ks = blk % NKS_D;
+        const Elem* src = (which ? sQ : sK) + (16 * mt + (l & 15)) * LDK + ks * Pol::KSTEP + (l >> 4) * FE;
+        *reinterpret_cast<Frag*>(kqb + W::kq_block(which, mt, ks) + l * FE) = Pol::ld(src);
+      }
+    }
     {
       Elem* kt = static_cast<Elem*>(ws.kt) + (cslot * h_qk + hq) * W::kt_elems;
       for (int f = tid; f < (D / 16) * NKS_C * 64; f += 256) {
@@ -592,7 +616,6 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   const int64_t start = seq_start(cu, s, t_total), end = seq_start(cu, s + 1, t_total);
   const int64_t nchunks = (end - start + C - 1) / C;
   const int64_t slot0 = start / C + s;
-  const int mrow = 16 * wave + r16;               // this lane's A-fragment row
   const int orow0 = 16 * wave + 4 * g4;           // this lane's first output row
 
   // This wave's operand fragments for one chunk (registers).  Rows of K, Q
@@ -614,12 +637,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     const int64_t t0_ = start + (jj) * C;                                                              \
     const int len_ = static_cast<int>(end - t0_ < C ? end - t0_ : C);                                  \
     if (tok_wave) {                                                                                    \
-      const int64_t row_ = t0_ + (mrow < len_ ? mrow : len_ - 1);                                      \
-      const typename In::T* kp_ = k + row_ * k_stride + (int64_t)hq * D + g4 * FE;                    \
-      const typename In::T* qp_ = q + row_ * q_stride + (int64_t)hq * D + g4 * FE;                    \
+      const Elem* kq_ = static_cast<const Elem*>(ws.kq) + ((slot0 + (jj)) * h_qk + hq) * W::kq_elems + lane * FE; \
       _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_D; ++ks_) {                                        \
-        kf[ks_] = Pol::ld_in(kp_ + ks_ * KS);                                                          \
-        qf[ks_] = Pol::ld_in(qp_ + ks_ * KS);                                                          \
+        kf[ks_] = Pol::ld(kq_ + W::kq_block(0, wave, ks_));                                            \
+        qf[ks_] = Pol::ld(kq_ + W::kq_block(1, wave, ks_));                                            \
       }                                                                                                \
       const float* sc_ = ws.sc + ((slot0 + (jj)) * h_v + h) * (4 * C);                                \
       c1v = *reinterpret_cast<const float4*>(sc_ + orow0);                                             \

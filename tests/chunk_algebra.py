@@ -17,6 +17,12 @@ gamma = inclusive cumsum of g over the chunk and b = exp(gamma):
     S_C   = b_C S0 + U^T diag(exp(gamma_C - gamma) rk) K
 U solves u_i = beta_i (v_i - a_i S_{i-1} k^_i) token by token, which is the
 delta rule written with the decayed entering state.
+
+Form "gr" folds Tb into the two products that read U, so a chunk needs X only:
+    R     = P Tb                                (C x C, lower triangular)
+    G     = K^T diag(exp(gamma_C - gamma) rk) Tb   (dk x C)
+    O     = scale diag(b rq) Q S0^T + R X
+    S_C^T = b_C S0^T + G X
 """
 from __future__ import annotations
 
@@ -80,9 +86,11 @@ class Plan:
 
 def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_state=None,
                              cu_seqlens=None, use_qk_l2norm=True, l2_eps=1e-6,
-                             plan: str = "exact"):
+                             plan: str = "exact", form: str = "tx"):
     """Same contract as the oracle's gated_delta_rule, evaluated chunk by chunk.
-    Chunks restart at every sequence start; the last chunk may be partial."""
+    Chunks restart at every sequence start; the last chunk may be partial.
+    form "tx" forms U = Tb X; form "gr" uses R = P Tb and G = K^T diag(.) Tb."""
+    assert form in ("tx", "gr")
     P = Plan(plan)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -133,11 +141,17 @@ def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_stat
             KS = P.mm(K, S, False, True, "hcd,hvd->hcv")        # K S^T  [Hv, C, dv]
             QS = P.mm(Q, S, False, True, "hcd,hvd->hcv")
             X = P.store(V - (b * rk)[:, :, None] * KS)
-            U = P.mm(Tb, X, True, True, "hij,hjv->hiv")
-            O = scale * (b * rq)[:, :, None] * QS + P.mm(Pm, U, True, True, "hij,hjv->hiv")
-            o[c0:c1] = O.transpose(1, 0, 2)
             dec = np.exp(gam[:, -1:] - gam) * rk                # [Hv, C]
-            Ud = P.store(U * dec[:, :, None])
-            S = P.store(b[:, -1][:, None, None] * S + P.mm(Ud, K, True, False, "hcv,hcd->hvd"))
+            if form == "tx":
+                U = P.mm(Tb, X, True, True, "hij,hjv->hiv")
+                O = scale * (b * rq)[:, :, None] * QS + P.mm(Pm, U, True, True, "hij,hjv->hiv")
+                Ud = P.store(U * dec[:, :, None])
+                S = P.store(b[:, -1][:, None, None] * S + P.mm(Ud, K, True, False, "hcv,hcd->hvd"))
+            else:
+                Rm = P.mm(Pm, Tb, True, True, "hik,hkj->hij")
+                G = P.mm(K, P.store(dec[:, :, None] * Tb), False, True, "hcd,hcj->hdj")
+                O = scale * (b * rq)[:, :, None] * QS + P.mm(Rm, X, True, True, "hij,hjv->hiv")
+                S = P.store(b[:, -1][:, None, None] * S + P.mm(X, G, True, True, "hjv,hdj->hvd"))
+            o[c0:c1] = O.transpose(1, 0, 2)
         final[s] = S
     return o, final

@@ -108,8 +108,10 @@ def test_chunk_workspace_size(lib):
     out = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0
     slots = 4096 // 64 + 1
-    # transposed K (bf16) per q/k head, Tb and P as bf16 hi+lo per v-head, fp32 scalars
-    expect = slots * 16 * 128 * 64 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2 + slots * 32 * 4 * 64 * 4
+    # per q/k head: K and Q fragments, transposed K (bf16); per v-head: Tb and P as
+    # bf16 hi+lo, fp32 scalars
+    expect = (slots * 16 * 2 * 64 * 128 * 2 + slots * 16 * 128 * 64 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2
+              + slots * 32 * 4 * 64 * 4)
     assert out.value == expect
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 1, ctypes.byref(out)) == 0
     assert out.value == expect + 4096 * 32 * 128 * 4

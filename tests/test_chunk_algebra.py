@@ -25,13 +25,14 @@ def _case(rng, lengths, hqk=2, hv=4, dk=8, dv=6, strong_decay=True):
 
 @pytest.mark.parametrize("chunk", [1, 4, 16, 64, 200])
 @pytest.mark.parametrize("strong", [True, False])
-def test_chunked_equals_sequential(chunk, strong):
+@pytest.mark.parametrize("form", ["tx", "gr"])
+def test_chunked_equals_sequential(chunk, strong, form):
     rng = np.random.default_rng(100 + chunk)
     lengths = [37, 0, 130, 1, 64]
     q, k, v, g, beta, S0, cu = _case(rng, lengths, strong_decay=strong)
     o_ref, f_ref = R.gated_delta_rule(q, k, v, g, beta, scale=0.8, initial_state=S0, cu_seqlens=cu)
     o, f = chunked_gated_delta_rule(q, k, v, g, beta, chunk=chunk, scale=0.8, initial_state=S0,
-                                    cu_seqlens=cu)
+                                    cu_seqlens=cu, form=form)
     scale_o = np.sqrt(np.mean(o_ref ** 2))
     assert np.max(np.abs(o - o_ref)) <= 1e-12 * max(1.0, scale_o)
     assert np.max(np.abs(f - f_ref)) <= 1e-12
@@ -46,3 +47,25 @@ def test_chunked_without_l2norm():
     o_ref, f_ref = R.gated_delta_rule(q, k, v, g, beta, initial_state=S0, use_qk_l2norm=False)
     o, f = chunked_gated_delta_rule(q, k, v, g, beta, chunk=16, initial_state=S0, use_qk_l2norm=False)
     assert np.max(np.abs(o - o_ref)) < 1e-12 and np.max(np.abs(f - f_ref)) < 1e-12
+
+
+@pytest.mark.parametrize("form", ["tx", "gr"])
+def test_split_bf16_plan_precision(form):
+    """Derived operands as bf16 hi+lo pairs (raw bf16 q/k/v single) stay well
+    inside the 2e-3 bound of max|err|/RMS at the model's decay statistics."""
+    rng = np.random.default_rng(9)
+    T, hqk, hv, d = 256, 1, 2, 128
+    bf = lambda a: np.asarray(a, np.float32).astype(np.float64)
+    from chunk_algebra import _bf16
+    q = _bf16(np.logaddexp(0, rng.standard_normal((T, hqk, d))) * rng.standard_normal((T, hqk, d)))
+    k = _bf16(np.logaddexp(0, rng.standard_normal((T, hqk, d))) * rng.standard_normal((T, hqk, d)))
+    v = _bf16(rng.standard_normal((T, hv, d)))
+    a = rng.uniform(0, np.log(16), hv)
+    g = bf(-np.exp(a)[None] * np.logaddexp(0, rng.standard_normal((T, hv))))
+    beta = bf(1 / (1 + np.exp(-rng.standard_normal((T, hv)))))
+    S0 = bf(rng.standard_normal((1, hv, d, d)) * 0.02)
+    o_ref, f_ref = R.gated_delta_rule(q, k, v, g, beta, initial_state=S0)
+    o, f = chunked_gated_delta_rule(q, k, v, g, beta, chunk=64, initial_state=S0, plan="bf16x3", form=form)
+    err_o = np.max(np.abs(o - o_ref)) / np.sqrt(np.mean(o_ref ** 2))
+    err_f = np.max(np.abs(f - f_ref)) / np.sqrt(np.mean(f_ref ** 2))
+    assert err_o < 5e-4 and err_f < 5e-4, (err_o, err_f)
