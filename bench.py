@@ -39,6 +39,29 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorithmic)
 
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# on this workload (FETCH scaled by 2.0 and WRITE by 1.0, the readings of a
+# 256 MiB device-to-device copy; see profiles/), valid for the kernel sources
+# with these hashes (sha256, first 16 hex digits).  A kernel changed since the
+# counters were taken reports null.
+CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
+MEASURED_TRAFFIC = {
+    "gdn_chunk_fwd": (340_172_185, {"chunk.hip": "58f0767fbe36b200", "common.hpp": "9789884ded6edf16",
+                                    "launch.hpp": "87391e0d859dd5e0"}),
+    "gdn_recurrent_step": (271_174_451, {"recurrent.hip": "c228b4968470e50e", "common.hpp": "9789884ded6edf16",
+                                         "launch.hpp": "87391e0d859dd5e0"}),
+}
+
+
+def measured_traffic(entry):
+    import hashlib
+    nbytes, sources = MEASURED_TRAFFIC[entry]
+    for name, digest in sources.items():
+        with open(os.path.join(CSRC, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
+                return None
+    return nbytes
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -51,8 +74,6 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="before the timed legs, copy 256 MiB device-to-device once (a plain copy of known "
                          "size that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per gdn_chunk_fwd call {'fetch': B, 'write': B}")
     return ap.parse_args()
 
 
@@ -207,10 +228,7 @@ def main():
     tok_s = T / (pf["ms"] * 1e-3)
     flop = FLOP_PER_TOKEN_HEAD * lay.h_v * T
     chunk_tflops = flop / (pf["ms_chunk"] * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        tr = json.load(open(args.traffic))
-        traffic = tr.get("fetch", 0) + tr.get("write", 0)
+    traffic = measured_traffic("gdn_chunk_fwd")
     out = {
         "metric": "GDN prefill tokens/s (% MFMA peak) + decode state GB/s (% HBM peak)",
         "value": round(tok_s, 1),
@@ -247,7 +265,7 @@ def main():
             "roofline": {"kernel": "gdn_recurrent_step", "bound": "hbm",
                          "achieved": round(alg / (dc["ms_rec"] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(alg / (dc["ms_rec"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                         "traffic": None, "avg_launch_ms": round(dc["ms_rec"], 4),
+                         "traffic": measured_traffic("gdn_recurrent_step"), "avg_launch_ms": round(dc["ms_rec"], 4),
                          "algorithmic_bytes_per_launch": alg},
         }
     if not args.no_cpu_baseline:
