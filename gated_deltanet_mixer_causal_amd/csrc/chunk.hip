@@ -251,6 +251,24 @@ struct WsLayout {
   }
 };
 
+// N consecutive floats from LDS, as 16-byte reads when N is a multiple of 4
+template <int N>
+__device__ __forceinline__ void lds_row(const float* p, float* out) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const float4 v = reinterpret_cast<const float4*>(p)[k];
+      out[4 * k] = v.x;
+      out[4 * k + 1] = v.y;
+      out[4 * k + 2] = v.z;
+      out[4 * k + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) out[k] = p[k];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_chunk_prep: persistent workgroups over (chunk slot, q/k head) units
 // ---------------------------------------------------------------------------
@@ -275,8 +293,12 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 
   // K/Q rows during the Gram phase, then L and T (overlaid).
   __shared__ __attribute__((aligned(16))) char smem[KQ_BYTES > LT_BYTES ? KQ_BYTES : LT_BYTES];
-  __shared__ float sGK[C * LDC], sGQ[C * LDC];
-  __shared__ float s_rk[C], s_rq[C], s_gam[C], s_beta[C];
+  __shared__ __attribute__((aligned(16))) float sGK[C * LDC];
+  __shared__ __attribute__((aligned(16))) float sGQ[C * LDC];
+  __shared__ __attribute__((aligned(16))) float s_rk[C];
+  __shared__ __attribute__((aligned(16))) float s_rq[C];
+  __shared__ __attribute__((aligned(16))) float s_gam[C];
+  __shared__ __attribute__((aligned(16))) float s_beta[C];
   Elem* sK = reinterpret_cast<Elem*>(smem);
   Elem* sQ = sK + C * LDK;
   float* sL = reinterpret_cast<float*>(smem);
@@ -439,29 +461,29 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
       __syncthreads();   // K/Q no longer read: L and T may overlay them
 
       // 5. One pass over the lower triangle in fragment order: each decay factor
-      //    exp(gamma_i - gamma_j) (formed only for j <= i, masked before the
-      //    exponential) serves both L (strictly lower, into LDS) and P (lower
-      //    incl. diagonal, split fragments to the workspace).
+      //    exp(gamma_i - gamma_j) serves both L (strictly lower, into LDS) and P
+      //    (lower incl. diagonal, split fragments to the workspace).  No
+      //    branches: the exponent is masked to -inf above the diagonal and the
+      //    masks are selects (the Gram tiles above the diagonal are never
+      //    written, so their contents must not reach a product).
       {
         Elem* pb = static_cast<Elem*>(ws.p) + unit * W::op_elems;
         for (int f = tid; f < NT * NKS_C * 64; f += 256) {
           const int l = f & 63, blk = f >> 6;
           const int mt = blk / NKS_C, ks = blk % NKS_C;
           const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
-          float pv[FE], lv[FE];
-          if (j0 <= i) {
-            const float gi = s_gam[i], rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
+          const float gi = s_gam[i], rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
+          float gj[FE], rkj[FE], gq[FE], gk[FE], pv[FE], lv[FE];
+          lds_row<FE>(s_gam + j0, gj);
+          lds_row<FE>(s_rk + j0, rkj);
+          lds_row<FE>(sGQ + i * LDC + j0, gq);
+          lds_row<FE>(sGK + i * LDC + j0, gk);
 #pragma unroll
-            for (int e = 0; e < FE; ++e) {
-              const int j = j0 + e;
-              const float dec = (j <= i) ? __expf(gi - s_gam[j]) : 0.f;
-              const float rkj = s_rk[j];
-              pv[e] = scale * dec * rqi * rkj * sGQ[i * LDC + j];
-              lv[e] = (j < i) ? bi * dec * rki * rkj * sGK[i * LDC + j] : 0.f;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < FE; ++e) pv[e] = lv[e] = 0.f;
+          for (int e = 0; e < FE; ++e) {
+            const int j = j0 + e;
+            const float dec = __expf(j <= i ? gi - gj[e] : -INFINITY);
+            pv[e] = j <= i ? scale * dec * rqi * rkj[e] * gq[e] : 0.f;
+            lv[e] = j < i ? bi * dec * rki * rkj[e] * gk[e] : 0.f;
           }
 #pragma unroll
           for (int e = 0; e < FE; ++e) sL[i * LDC + j0 + e] = lv[e];
@@ -517,12 +539,11 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
           const int l = f & 63, blk = f >> 6;
           const int mt = blk / NKS_C, ks = blk % NKS_C;
           const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
-          float tv[FE];
+          float tr[FE], bj[FE], tv[FE];
+          lds_row<FE>(sT + i * LDC + j0, tr);
+          lds_row<FE>(s_beta + j0, bj);
 #pragma unroll
-          for (int e = 0; e < FE; ++e) {
-            const int j = j0 + e;
-            tv[e] = (j <= i) ? sT[i * LDC + j] * s_beta[j] : 0.f;
-          }
+          for (int e = 0; e < FE; ++e) tv[e] = j0 + e <= i ? tr[e] * bj[e] : 0.f;   // T above the diagonal is not written
           Pol::store_split(tb + W::op_block(mt, ks, 0) + l * FE, tb + W::op_block(mt, ks, Pol::NSPLIT - 1) + l * FE,
                            tv);
         }
