@@ -60,8 +60,8 @@ gdn_status finish(hipError_t e) {
 // Shared checks of the q/k/v/g/beta arguments of the recurrence entry points.
 gdn_status check_qkv(const void* q, const void* k, const void* v, int64_t& q_stride, int64_t& k_stride,
                      int64_t& v_stride, gdn_dtype dt, const float* g, const float* beta, int32_t h_qk,
-                     int32_t h_v, int32_t d_k, int32_t d_v) {
-  if (!q || !k || !v || !g || !beta) return GDN_ERR_NULL;
+                     int32_t h_v, int32_t d_k, int32_t d_v, bool has_rows = true) {
+  if (has_rows && (!q || !k || !v || !g || !beta)) return GDN_ERR_NULL;
   if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0 || h_v % h_qk != 0) return GDN_ERR_INVALID;
   if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
   if (q_stride == 0) q_stride = static_cast<int64_t>(h_qk) * d_k;
@@ -159,9 +159,10 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_
                          const float* norm_w, float norm_eps, void* workspace, size_t ws_bytes, void* stream) {
   if (n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
   if (n_seq == 0) return GDN_OK;
-  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, g, beta, h_qk, h_v, d_k, d_v);
+  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, g, beta, h_qk, h_v, d_k, d_v, t_total > 0);
   if (st != GDN_OK) return st;
-  if (!o || !workspace) return !o ? GDN_ERR_NULL : GDN_ERR_WORKSPACE;
+  if (!o && t_total > 0) return GDN_ERR_NULL;
+  if (!workspace) return GDN_ERR_WORKSPACE;
   if (z && !norm_w) return GDN_ERR_NULL;
   if (!cu_seqlens && n_seq != 1) return GDN_ERR_NULL;
   if (!dt_valid(o_dt)) return GDN_ERR_UNSUPPORTED;

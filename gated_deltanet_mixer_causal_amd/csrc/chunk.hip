@@ -251,17 +251,17 @@ struct WsLayout {
   }
 };
 
-// N consecutive floats from LDS, as 16-byte reads when N is a multiple of 4
-template <int N>
-__device__ __forceinline__ void lds_row(const float* p, float* out) {
-  if constexpr (N % 4 == 0) {
+// N consecutive values from LDS, as 16-byte reads when they fill them
+template <int N, class T>
+__device__ __forceinline__ void lds_row(const T* p, T* out) {
+  constexpr int V = 16 / (int)sizeof(T);
+  if constexpr (N % V == 0) {
+    typedef T vec __attribute__((ext_vector_type(V)));
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) {
-      const float4 v = reinterpret_cast<const float4*>(p)[k];
-      out[4 * k] = v.x;
-      out[4 * k + 1] = v.y;
-      out[4 * k + 2] = v.z;
-      out[4 * k + 3] = v.w;
+    for (int k = 0; k < N / V; ++k) {
+      const vec v = reinterpret_cast<const vec*>(p)[k];
+#pragma unroll
+      for (int e = 0; e < V; ++e) out[V * k + e] = v[e];
     }
   } else {
 #pragma unroll
@@ -297,7 +297,9 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   __shared__ __attribute__((aligned(16))) float sGQ[C * LDC];
   __shared__ __attribute__((aligned(16))) float s_rk[C];
   __shared__ __attribute__((aligned(16))) float s_rq[C];
-  __shared__ __attribute__((aligned(16))) float s_gam[C];
+  // the chunk's running sum of g, kept in fp64: with strong decays it reaches
+  // hundreds, and the decay between two tokens is a difference of two sums
+  __shared__ __attribute__((aligned(16))) double s_gam[C];
   __shared__ __attribute__((aligned(16))) float s_beta[C];
   Elem* sK = reinterpret_cast<Elem*>(smem);
   Elem* sQ = sK + C * LDK;
@@ -440,22 +442,22 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 
       // 4. decay: inclusive prefix sum of g over the chunk (padded tokens add 0)
       if (wave == 0) {
-        float gam = gv;
+        double gam = gv;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-          const float o = __shfl_up(gam, off, 64);
+          const double o = __shfl_up(gam, off, 64);
           if (lane >= off) gam += o;
         }
-        const float glast = __shfl(gam, C - 1, 64);
+        const double glast = __shfl(gam, C - 1, 64);
         if (lane < C) {
           float* sc_out = ws.sc + unit * (4 * C);
           s_gam[lane] = gam;
           s_beta[lane] = bv;
-          const float b = __expf(gam);
+          const float b = __expf(static_cast<float>(gam));
           sc_out[lane] = b * s_rk[lane];
           sc_out[C + lane] = scale * b * s_rq[lane];
-          sc_out[2 * C + lane] = __expf(glast - gam) * s_rk[lane];
-          sc_out[3 * C + lane] = __expf(glast);
+          sc_out[2 * C + lane] = __expf(static_cast<float>(glast - gam)) * s_rk[lane];
+          sc_out[3 * C + lane] = __expf(static_cast<float>(glast));
         }
       }
       __syncthreads();   // K/Q no longer read: L and T may overlay them
@@ -472,8 +474,10 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
           const int l = f & 63, blk = f >> 6;
           const int mt = blk / NKS_C, ks = blk % NKS_C;
           const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
-          const float gi = s_gam[i], rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
-          float gj[FE], rkj[FE], gq[FE], gk[FE], pv[FE], lv[FE];
+          const double gi = s_gam[i];
+          const float rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
+          double gj[FE];
+          float rkj[FE], gq[FE], gk[FE], pv[FE], lv[FE];
           lds_row<FE>(s_gam + j0, gj);
           lds_row<FE>(s_rk + j0, rkj);
           lds_row<FE>(sGQ + i * LDC + j0, gq);
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 #pragma unroll
           for (int e = 0; e < FE; ++e) {
             const int j = j0 + e;
-            const float dec = __expf(j <= i ? gi - gj[e] : -INFINITY);
+            const float dec = __expf(j <= i ? static_cast<float>(gi - gj[e]) : -INFINITY);
             pv[e] = j <= i ? scale * dec * rqi * rkj[e] * gq[e] : 0.f;
             lv[e] = j < i ? bi * dec * rki * rkj[e] * gk[e] : 0.f;
           }

@@ -108,8 +108,8 @@ gdn_status gdn_conv1d_fwd(const void* x, gdn_dtype dt, const void* w, int32_t ch
  *  recurrent decode as in haskell-infer-demo README, "Architecture", fla_gdn.cu.
  *  FP32 recurrent state and BF16 intermediates, chunks relative to each call:
  *  Flare core-design, GDN numerics paragraph and Qwen defaults table.  Final
- *  state at the exact consumed length: Flare core-design, checkpoint endpoints
- *  "not rounded to token groups".)
+ *  state at the exact consumed length: Flare core-design, the paragraph on
+ *  checkpoint endpoints, which are never rounded up to a token group.)
  *
  * Chunks of `chunk` tokens restart at every sequence start.  Within a chunk the
  * kernels use the UT/WY form (intra-chunk triangular solve, then contractions
@@ -141,7 +141,9 @@ gdn_status gdn_conv1d_fwd(const void* x, gdn_dtype dt, const void* w, int32_t ch
  *   workspace   device scratch of ws_bytes >= gdn_chunk_fwd_workspace_size(...);
  *               its contents need no initialisation and are not preserved
  * n_seq == 0 is a no-op.  Zero-length sequences are legal: their final state
- * equals their initial state (or zeros).
+ * equals their initial state (or zeros).  With t_total == 0 the per-token
+ * buffers (q, k, v, g, beta, o, z) may be NULL; the final states are still
+ * written.
  */
 gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
