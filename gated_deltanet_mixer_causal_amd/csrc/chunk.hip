@@ -473,6 +473,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         for (int f = tid; f < NT * NKS_C * 64; f += 256) {
           const int l = f & 63, blk = f >> 6;
           const int mt = blk / NKS_C, ks = blk % NKS_C;
+          if (ks * Pol::KSTEP > 16 * mt + 15) continue;   // wholly above the diagonal: never read
           const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
           const double gi = s_gam[i];
           const float rki = s_rk[i], rqi = s_rq[i], bi = s_beta[i];
@@ -542,6 +543,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         for (int f = tid; f < NT * NKS_C * 64; f += 256) {
           const int l = f & 63, blk = f >> 6;
           const int mt = blk / NKS_C, ks = blk % NKS_C;
+          if (ks * Pol::KSTEP > 16 * mt + 15) continue;   // wholly above the diagonal: never read
           const int i = 16 * mt + (l & 15), j0 = ks * Pol::KSTEP + (l >> 4) * FE;
           float tr[FE], bj[FE], tv[FE];
           lds_row<FE>(sT + i * LDC + j0, tr);
