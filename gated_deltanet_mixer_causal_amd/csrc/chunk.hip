@@ -201,6 +201,7 @@ __device__ __forceinline__ float from_u32<F32>(uint32_t x) { return __uint_as_fl
 //   tb [slots][h_v][NSPLIT*C*C]    Tb fragments:  blocks (token tile mt, k-step ks, hi|lo)
 //   p  [slots][h_v][NSPLIT*C*C]    P fragments:   same order
 //   sc [slots][h_v][4][C] fp32     b rk | scale b rq | exp(gamma_C - gamma) rk | b_C
+//   order [n_seq] int32            sequences, most chunks first (only when n_seq > 1)
 // A fragment block is 64 lanes x FE elements, lane l holding row l % 16 and
 // k elements (l / 16) * FE .. + FE - 1 of its k-step, so one wave reads a
 // block with one contiguous 16-byte load per lane (bf16).
@@ -210,6 +211,7 @@ struct ChunkWs {
   void* tb;
   void* p;
   float* sc;
+  int32_t* order;   // NULL for a single sequence
 };
 
 template <class Pol, int D, int C>
@@ -231,11 +233,13 @@ struct WsLayout {
     return which * C * D + (mt * NKS_D + ks) * BLK;
   }
   static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
-  static size_t bytes(int64_t slots, int h_qk, int h_v) {
+  static size_t order_bytes(int n_seq) { return n_seq > 1 ? al(sizeof(int32_t) * n_seq) : 0; }
+  static size_t bytes(int64_t slots, int h_qk, int h_v, int n_seq) {
     return al(sizeof(Elem) * slots * h_qk * kq_elems) + al(sizeof(Elem) * slots * h_qk * kt_elems) +
-           2 * al(sizeof(Elem) * slots * h_v * op_elems) + al(sizeof(float) * slots * h_v * 4 * C);
+           2 * al(sizeof(Elem) * slots * h_v * op_elems) + al(sizeof(float) * slots * h_v * 4 * C) +
+           order_bytes(n_seq);
   }
-  static ChunkWs carve(void* base, int64_t slots, int h_qk, int h_v) {
+  static ChunkWs carve(void* base, int64_t slots, int h_qk, int h_v, int n_seq) {
     char* b = static_cast<char*>(base);
     ChunkWs w;
     w.kq = b;
@@ -247,6 +251,8 @@ struct WsLayout {
     w.p = b;
     b += al(sizeof(Elem) * slots * h_v * op_elems);
     w.sc = reinterpret_cast<float*>(b);
+    b += al(sizeof(float) * slots * h_v * 4 * C);
+    w.order = n_seq > 1 ? reinterpret_cast<int32_t*>(b) : nullptr;
     return w;
   }
 };
@@ -563,6 +569,50 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 }
 
 // ---------------------------------------------------------------------------
+// k_seq_order: the sequences, most chunks first, for the scan's block order.
+// The scan's workgroups start in index order and each runs one sequence's
+// chunks back to back, so the longest sequence bounds the call: listing it
+// first starts it at once, spread over every XCD, and the shorter ones fill
+// the compute units behind it (longest-first list scheduling).  A counting
+// sort on a key that is exact below 32 chunks and has eight steps per octave
+// above; equal keys may come out in any order, which changes no result.
+// ---------------------------------------------------------------------------
+constexpr int kOrderBins = 256;
+
+__device__ __forceinline__ int order_key(int64_t nch) {
+  if (nch < 32) return nch > 0 ? static_cast<int>(nch) : 0;
+  const int e = 63 - __builtin_clzll(static_cast<unsigned long long>(nch));   // >= 5
+  const int key = 32 + 8 * (e - 5) + static_cast<int>((nch >> (e - 3)) & 7);
+  return key < kOrderBins ? key : kOrderBins - 1;
+}
+
+__global__ __launch_bounds__(kOrderBins) void k_seq_order(const int32_t* __restrict__ cu, int n_seq, int C,
+                                                          int32_t* __restrict__ order) {
+  __shared__ int cnt[kOrderBins];
+  __shared__ int scan[2][kOrderBins];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  for (int s = tid; s < n_seq; s += kOrderBins) atomicAdd(&cnt[order_key((cu[s + 1] - cu[s] + C - 1) / C)], 1);
+  __syncthreads();
+  // inclusive scan of the counts in descending key order: x_t = cnt[last - t]
+  const int x = cnt[kOrderBins - 1 - tid];
+  int cur = 0;
+  scan[0][tid] = x;
+  __syncthreads();
+  for (int off = 1; off < kOrderBins; off <<= 1) {
+    const int y = scan[cur][tid] + (tid >= off ? scan[cur][tid - off] : 0);
+    scan[cur ^ 1][tid] = y;
+    cur ^= 1;
+    __syncthreads();
+  }
+  cnt[kOrderBins - 1 - tid] = scan[cur][tid] - x;   // first position of the key
+  __syncthreads();
+  for (int s = tid; s < n_seq; s += kOrderBins)
+    order[atomicAdd(&cnt[order_key((cu[s + 1] - cu[s] + C - 1) / C)], 1)] = s;
+}
+
+// ---------------------------------------------------------------------------
 // k_chunk_scan: one workgroup per (sequence, v-head, d_v slice of 16*NV)
 // ---------------------------------------------------------------------------
 template <class Pol, class EO, int D, int C, int NV>
@@ -571,7 +621,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     const typename Pol::In::T* __restrict__ v, int64_t q_stride, int64_t k_stride, int64_t v_stride,
     int h_qk, int h_v, const int32_t* __restrict__ cu, int n_seq, int64_t t_total,
     const float* __restrict__ init, float* __restrict__ fin,
-    typename EO::T* __restrict__ o, ChunkWs ws, int64_t n_blocks) {
+    typename EO::T* __restrict__ o, ChunkWs ws) {
   using Elem = typename Pol::Elem;
   using In = typename Pol::In;
   using Frag = typename Pol::Frag;
@@ -602,16 +652,19 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   Elem* const sU2_lo = sU2 + (NSP - 1) * BV * LDT;
   Elem* const sS_lo = sS + (NSP - 1) * BV * LDK;
 
-  // XCD-aware order: the dispatcher places block b on XCD b % 8, so give each
-  // XCD a contiguous range of logical ids; the d_v tiles of one head then
-  // share an L2 and its K/Q/Tb/P reads.
+  // Block order: sequences in ws.order (longest first), each a run of
+  // h_v * NTILE consecutive blocks.  Inside a run the XCD-aware bijection
+  // gives each XCD (the dispatcher places block b on XCD b % 8) a contiguous
+  // range of heads, so the d_v tiles of one head share an L2 and its
+  // K/Q/Tb/P reads, and every sequence is spread over all XCDs.
+  const int64_t per_seq = static_cast<int64_t>(h_v) * NTILE;
   const int64_t b = blockIdx.x;
-  const int64_t lid = xcd_order(b, n_blocks);
+  const int64_t rank = b / per_seq;
+  if (rank >= n_seq) return;
+  const int s = ws.order ? ws.order[rank] : static_cast<int>(rank);
+  const int64_t lid = xcd_order(b % per_seq, per_seq);
   const int tile = static_cast<int>(lid % NTILE);
-  const int64_t sh = lid / NTILE;
-  const int h = static_cast<int>(sh % h_v);
-  const int s = static_cast<int>(sh / h_v);
-  if (s >= n_seq) return;
+  const int h = static_cast<int>(lid / NTILE);
   const int hq = h / (h_v / h_qk);
   const int dv0 = tile * BV;
 
@@ -876,7 +929,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
 template <class Pol, int D, int C>
 static size_t ws_bytes_for(int h_qk, int h_v, int n_seq, int64_t t_total, int with_norm) {
   const int64_t slots = block_slots(t_total, n_seq, C);
-  size_t b = WsLayout<Pol, D, C>::bytes(slots, h_qk, h_v);
+  size_t b = WsLayout<Pol, D, C>::bytes(slots, h_qk, h_v, n_seq);
   if (with_norm) b += WsLayout<Pol, D, C>::al(sizeof(float) * t_total * h_v * D);
   return b;
 }
@@ -892,9 +945,9 @@ template <class Pol, int D, int C>
 static hipError_t run_chunk(const ChunkArgs& a) {
   using T = typename Pol::In::T;
   const int64_t slots = block_slots(a.t_total, a.n_seq, C);
-  ChunkWs ws = WsLayout<Pol, D, C>::carve(a.workspace, slots, a.h_qk, a.h_v);
+  ChunkWs ws = WsLayout<Pol, D, C>::carve(a.workspace, slots, a.h_qk, a.h_v, a.n_seq);
   float* o_pre = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
-                                          WsLayout<Pol, D, C>::bytes(slots, a.h_qk, a.h_v));
+                                          WsLayout<Pol, D, C>::bytes(slots, a.h_qk, a.h_v, a.n_seq));
 
   hipStream_t st = static_cast<hipStream_t>(a.stream);
   const T* q = static_cast<const T*>(a.q);
@@ -918,6 +971,11 @@ static hipError_t run_chunk(const ChunkArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (ws.order) {
+    hipLaunchKernelGGL(k_seq_order, dim3(1), dim3(kOrderBins), 0, st, a.cu, a.n_seq, C, ws.order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   // One 16-wide d_v tile per workgroup: a single long sequence has only
   // heads x d_v/16 independent recurrences, and the chunk loop's latency, not
   // the matrix cores, sets its pace, so the widest grid wins (two tiles per
@@ -927,7 +985,7 @@ static hipError_t run_chunk(const ChunkArgs& a) {
   if (a.z) {
     hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
-                       a.init, a.fin, o_pre, ws, nblk);
+                       a.init, a.fin, o_pre, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.t_total > 0)
@@ -938,11 +996,11 @@ static hipError_t run_chunk(const ChunkArgs& a) {
   if (a.o_dt == GDN_BF16)
     hipLaunchKernelGGL((k_chunk_scan<Pol, BF16, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
-                       a.init, a.fin, static_cast<uint16_t*>(a.o), ws, nblk);
+                       a.init, a.fin, static_cast<uint16_t*>(a.o), ws);
   else
     hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
-                       a.init, a.fin, static_cast<float*>(a.o), ws, nblk);
+                       a.init, a.fin, static_cast<float*>(a.o), ws);
   return hipGetLastError();
 }
 

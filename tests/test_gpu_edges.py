@@ -1,6 +1,6 @@
 """GPU edge cases of the chunk and decode entry points against the oracle:
-fp32 inputs at d=128, a non-unit scale with permuted sequences, calls whose
-sequences are all empty, a poisoned workspace, and a hard reset (g = -inf)
+fp32 inputs at d=128, a non-unit scale with permuted sequences, 300 packed
+sequences, calls whose sequences are all empty, a poisoned workspace, and a hard reset (g = -inf)
 in the decode step.
 """
 import numpy as np
@@ -81,6 +81,26 @@ def test_chunk_scale_and_sequence_permutation(ops):
                       d["state"][perm], scale=scale)
     assert torch.equal(o_p, o[torch.from_numpy(rows).to(DEV)])
     assert torch.equal(fin_p, fin[torch.tensor(perm, device=DEV)])
+
+
+def test_chunk_many_sequences(ops):
+    """300 packed sequences (more than one pass of the longest-first ordering
+    loop), many of equal length, some empty, lengths around chunk edges."""
+    note("chunk 300 sequences")
+    lay = I.Layout(h_qk=1, h_v=2, d_k=128, d_v=128, chunk=64, dtype="bf16")
+    rng = np.random.default_rng(36)
+    lengths = [int(v) for v in rng.choice([0, 1, 5, 63, 64, 65, 130, 200], 300)]
+    lengths[17] = 700   # one long sequence in the middle of the list
+    d = I.prefill_inputs(36, lay, lengths, state_std=0.02)
+    q, k, v = I.split_qkv(d["x"], lay)
+    o, fin = _run(ops, lay, q, k, v, d["g"], d["beta"], d["cu_seqlens"], d["state"])
+    o_ref, f_ref = R.gated_delta_rule(q, k, v, d["g"], d["beta"], initial_state=d["state"],
+                                      cu_seqlens=d["cu_seqlens"])
+    eo, ef = rel_max(host(o), o_ref), rel_max(host(fin), f_ref)
+    note(f"  o {eo:.2e} state {ef:.2e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
+    empty = [i for i, n in enumerate(lengths) if n == 0]
+    assert torch.equal(fin[empty], dev(d["state"][empty]))
 
 
 def test_chunk_all_sequences_empty(ops):
