@@ -46,7 +46,7 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (323_389_645, {"chunk.hip": "5d0cb9e1e611c99b", "common.hpp": "9789884ded6edf16",
+    "gdn_chunk_fwd": (323_372_851, {"chunk.hip": "f8673bd616eb5c6e", "common.hpp": "9789884ded6edf16",
                                     "launch.hpp": "87391e0d859dd5e0"}),
     "gdn_recurrent_step": (271_171_379, {"recurrent.hip": "c228b4968470e50e", "common.hpp": "9789884ded6edf16",
                                          "launch.hpp": "87391e0d859dd5e0"}),

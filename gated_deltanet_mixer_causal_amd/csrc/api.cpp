@@ -70,6 +70,9 @@ gdn_status check_qkv(const void* q, const void* k, const void* v, int64_t& q_str
   if (q_stride < static_cast<int64_t>(h_qk) * d_k || k_stride < static_cast<int64_t>(h_qk) * d_k ||
       v_stride < static_cast<int64_t>(h_v) * d_v)
     return GDN_ERR_INVALID;
+  // row offsets inside a chunk or a decode batch row are formed in 32 bits
+  constexpr int64_t kMaxStride = int64_t(1) << 24;
+  if (q_stride > kMaxStride || k_stride > kMaxStride || v_stride > kMaxStride) return GDN_ERR_INVALID;
   if (q_stride % 8 || k_stride % 8 || v_stride % 8) return GDN_ERR_ALIGN;
   if (!all_aligned({q, k, v, g, beta})) return GDN_ERR_ALIGN;
   return GDN_OK;

@@ -568,6 +568,20 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 #undef GDN_PREP_FETCH
 }
 
+// Four consecutive output values of one row (one 16- or 8-byte store).
+template <class EO>
+__device__ __forceinline__ void store_row4(typename EO::T* p, floatx4 v);
+template <>
+__device__ __forceinline__ void store_row4<F32>(float* p, floatx4 v) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ void store_row4<BF16>(uint16_t* p, floatx4 v) {
+  const uint32_t a = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+  const uint32_t b = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
+}
+
 // ---------------------------------------------------------------------------
 // k_seq_order: the sequences, most chunks first, for the scan's block order.
 // The scan's workgroups start in index order and each runs one sequence's
@@ -706,11 +720,15 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   Frag tbh[NKS_C], tbl[NKS_C];           // Tb rows (hi, lo)
   Frag ph[NKS_C], pl[NKS_C];             // P rows (hi, lo)
   Frag ktf[SPW][NKS_C];                  // K^T rows of the state tiles
-  float4 c1v = {0.f, 0.f, 0.f, 0.f}, c2v = c1v, c3v = c1v;   // b rk, scale b rq, exp(.) rk of 4 output rows
+  float4 c1v = {0.f, 0.f, 0.f, 0.f}, c3v = c1v;   // b rk, exp(.) rk of rows orow0 .. orow0 + 3
+  float c2s = 0.f;                       // scale b rq of row 16 wave + r16 (outputs are built transposed)
   float bcv = 0.f;                       // b_C
-  uint32_t vraw[NV][4] = {};             // raw V of the 4 output rows, per N tile
+  uint32_t vraw[NV][4] = {};             // raw V of rows orow0 .. orow0 + 3, per N tile
   int vlen = 0;
   const int nks_w = (16 * wave + 16 + KS - 1) / KS;   // k-steps reaching this tile's last row
+  const uint32_t vs32 = static_cast<uint32_t>(v_stride);   // at most 2^24
+  // V element (row orow0 + i, column dv0 + 16 nt + r16) of a chunk: the chunk's
+  // uniform base plus a 32-bit lane offset (strides are at most 2^24)
 
 #define GDN_LOAD_KQ(jj)                                                                                 \
   do {                                                                                                 \
@@ -724,12 +742,13 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
       }                                                                                                \
       const float* sc_ = ws.sc + ((slot0 + (jj)) * h_v + h) * (4 * C);                                \
       c1v = *reinterpret_cast<const float4*>(sc_ + orow0);                                             \
-      c2v = *reinterpret_cast<const float4*>(sc_ + C + orow0);                                         \
+      c2s = sc_[C + 16 * wave + r16];                                                                  \
       c3v = *reinterpret_cast<const float4*>(sc_ + 2 * C + orow0);                                     \
+      const typename In::T* vc_ = v + t0_ * v_stride + (int64_t)h * D + dv0 + r16;                     \
       _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                               \
-        const int r_ = orow0 + i_;                                                                     \
-        const typename In::T* vp_ = v + (t0_ + (r_ < len_ ? r_ : len_ - 1)) * v_stride + (int64_t)h * D + dv0 + r16; \
-        _Pragma("unroll") for (int nt_ = 0; nt_ < NV; ++nt_) vraw[nt_][i_] = to_u32(vp_[16 * nt_]);  \
+        const int r_ = orow0 + i_ < len_ ? orow0 + i_ : len_ - 1;                                      \
+        const uint32_t o_ = __umul24(static_cast<uint32_t>(r_), vs32);                                 \
+        _Pragma("unroll") for (int nt_ = 0; nt_ < NV; ++nt_) vraw[nt_][i_] = to_u32(vc_[o_ + 16 * nt_]); \
       }                                                                                                \
       vlen = len_;                                                                                     \
     }                                                                                                  \
@@ -796,15 +815,15 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
           const int off = (16 * nt + r16) * LDK + ks * KS + g4 * FE;
           const Frag shi = Pol::ld(sS + off);
           ak[nt] = Pol::mma(kf[ks], shi, ak[nt]);
-          aq[nt] = Pol::mma(qf[ks], shi, aq[nt]);
+          aq[nt] = Pol::mma(shi, qf[ks], aq[nt]);   // transposed: lane holds O[16 wave + r16][dv 4 g4 + i]
           if constexpr (NSP == 2) {
             const Frag slo = Pol::ld(sS_lo + off);
             ak[nt] = Pol::mma(kf[ks], slo, ak[nt]);
-            aq[nt] = Pol::mma(qf[ks], slo, aq[nt]);
+            aq[nt] = Pol::mma(slo, qf[ks], aq[nt]);
           }
         }
       }
-      const float c1[4] = {c1v.x, c1v.y, c1v.z, c1v.w}, c2[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
+      const float c1[4] = {c1v.x, c1v.y, c1v.z, c1v.w};
 #pragma unroll
       for (int nt = 0; nt < NV; ++nt) {
         float xv[4];
@@ -812,7 +831,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
         for (int i = 0; i < 4; ++i) {
           const float vv = (orow0 + i < vlen) ? from_u32<In>(vraw[nt][i]) : 0.f;
           xv[i] = vv - c1[i] * ak[nt][i];
-          Oacc[nt][i] = c2[i] * aq[nt][i];
+          Oacc[nt][i] = c2s * aq[nt][i];
         }
         Pol::put4(sX, sX_lo, (16 * nt + r16) * LDT + orow0, xv);
       }
@@ -864,23 +883,20 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
           for (int nt = 0; nt < NV; ++nt) {
             const int off = (16 * nt + r16) * LDT + ks * KS + g4 * FE;
             const Frag uh = Pol::ld(sU + off);
-            Oacc[nt] = Pol::mma(ph[ks], uh, Oacc[nt]);
+            Oacc[nt] = Pol::mma(uh, ph[ks], Oacc[nt]);
             if constexpr (NSP == 2) {
               const Frag ul = Pol::ld(sU_lo + off);
-              Oacc[nt] = Pol::mma(ph[ks], ul, Oacc[nt]);
-              Oacc[nt] = Pol::mma(pl[ks], uh, Oacc[nt]);
+              Oacc[nt] = Pol::mma(ul, ph[ks], Oacc[nt]);
+              Oacc[nt] = Pol::mma(uh, pl[ks], Oacc[nt]);
             }
           }
         }
       }
+      const int row = 16 * wave + r16;
+      if (row < len) {
+        typename EO::T* ob = o + (t0 + row) * ((int64_t)h_v * D) + (int64_t)h * D + dv0 + 4 * g4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = orow0 + i;
-        if (row < len) {
-          const int64_t ob = (t0 + row) * ((int64_t)h_v * D) + (int64_t)h * D + dv0 + r16;
-#pragma unroll
-          for (int nt = 0; nt < NV; ++nt) EO::store(o, ob + 16 * nt, Oacc[nt][i]);
-        }
+        for (int nt = 0; nt < NV; ++nt) store_row4<EO>(ob + 16 * nt, Oacc[nt]);
       }
     }
 #pragma unroll

@@ -118,7 +118,7 @@ gdn_status gdn_conv1d_fwd(const void* x, gdn_dtype dt, const void* w, int32_t ch
  *
  *   q, k        [t_total, h_qk, d_k] of dt, token stride q_stride / k_stride
  *   v           [t_total, h_v, d_v] of dt, token stride v_stride
- *               (strides in elements; 0 = dense; multiples of 8)
+ *               (strides in elements; 0 = dense; multiples of 8; at most 2^24)
  *   dt          GDN_BF16 (bf16 operands on the matrix cores, derived operands as
  *               bf16 hi+lo pairs, fp32 accumulation) or GDN_F32 (fp32 matrix cores)
  *   g, beta     [t_total, h_v] fp32: a_t = exp(g_t), write strength beta_t

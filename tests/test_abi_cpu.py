@@ -96,6 +96,7 @@ def test_chunk_validation(lib):
     assert chunk(lib, odt=9) == L.GDN_ERR_UNSUPPORTED
     assert chunk(lib, qs=100) == L.GDN_ERR_INVALID           # stride below a row
     assert chunk(lib, qs=260) == L.GDN_ERR_ALIGN             # stride not a multiple of 8
+    assert chunk(lib, vs=(1 << 24) + 8) == L.GDN_ERR_INVALID  # stride above 2^24 elements
     assert chunk(lib, g=_addr(3) + 8) == L.GDN_ERR_ALIGN
     assert chunk(lib, z=_addr(9)) == L.GDN_ERR_NULL          # z without norm weight
     assert chunk(lib, cu=None, n=2) == L.GDN_ERR_NULL        # NULL cu_seqlens only for one sequence
