@@ -63,6 +63,99 @@ def measured_traffic(entry):
     return nbytes
 
 
+# Executed matrix-core work per gdn_chunk_fwd launch on the same workload, from
+# rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_INSTS_VALU_MFMA_MOPS_F32
+# (512 FLOP per op) summed over the prep and scan kernels; hash-gated like the
+# traffic above.
+MEASURED_MFMA = {
+    "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
+                      {"chunk.hip": "f8673bd616eb5c6e", "common.hpp": "9789884ded6edf16",
+                       "launch.hpp": "87391e0d859dd5e0"}),
+}
+
+
+def measured_mfma(entry):
+    bf16, f32, sources = MEASURED_MFMA[entry]
+    if bf16 is None:
+        return None
+    import hashlib
+    for name, digest in sources.items():
+        with open(os.path.join(CSRC, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] != digest:
+                return None
+    return bf16, f32
+
+
+def call_stats(fn, n, start, torch):
+    """Per-call durations (ms) of n calls fn(start + i), each between its own events."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(start + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    import statistics
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"n": n, "median_ms": round(statistics.median(t), 4), "min_ms": round(t[0], 4),
+            "max_ms": round(t[-1], 4), "std_ms": round(statistics.pstdev(t), 4)}
+
+
+class ClockSampler:
+    """Samples the shader clock from sysfs (the level marked '*' in pp_dpm_sclk)
+    on a background thread while the timed calls run; file reads only."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for p in self.paths:
+            try:
+                with open(p) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            return int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def median(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return v[len(v) // 2]
+
+
+def environment(torch, sclk=None):
+    props = torch.cuda.get_device_properties(0)
+    return {"rocm_hip": torch.version.hip, "arch": getattr(props, "gcnArchName", None),
+            "sclk_mhz_median_during_calls": sclk}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +228,9 @@ def prefill_leg(args, torch, np, ops, I):
 
     ms, wall = timed(step, args.steps, args.warmup, torch)
     ms_chunk, _ = timed(chunk_only, args.steps, args.warmup, torch)
-    return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, layout=lay)
+    with ClockSampler() as clk:
+        stats = call_stats(chunk_only, max(args.steps, 50), args.warmup + args.steps, torch)
+    return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, chunk_stats=stats, sclk=clk.median(), layout=lay)
 
 
 def decode_leg(args, torch, np, ops, I):
@@ -173,10 +268,12 @@ def decode_leg(args, torch, np, ops, I):
 
     ms, wall = timed(step, args.steps, args.warmup, torch)
     ms_rec, _ = timed(rec_only, args.steps, args.warmup, torch)
+    rec_stats = call_stats(rec_only, max(args.steps, 50), args.warmup + args.steps, torch)
     state_bytes = n_req * lay.h_v * lay.d_v * lay.d_k * 4
     # per request: q, k, v, z (bf16), g, beta (fp32), o (bf16)
     small = n_req * (2 * lay.h_qk * lay.d_k * 2 + lay.h_v * lay.d_v * 2 + 2 * lay.h_v * 4 + lay.h_v * lay.d_v * 2)
-    return dict(ms=ms, wall=wall, ms_rec=ms_rec, n_req=n_req, state_bytes=state_bytes, small=small)
+    return dict(ms=ms, wall=wall, ms_rec=ms_rec, rec_stats=rec_stats, n_req=n_req, state_bytes=state_bytes,
+                small=small)
 
 
 def cpu_baseline(np, I, R):
@@ -250,8 +347,16 @@ def main():
                      "achieved": round(chunk_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(chunk_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "avg_launch_ms": round(pf["ms_chunk"], 4),
-                     "algorithmic_flop_per_launch": flop},
+                     "algorithmic_flop_per_launch": flop,
+                     "per_call": pf["chunk_stats"]},
+        "env": environment(torch, pf["sclk"]),
     }
+    mf = measured_mfma("gdn_chunk_fwd")
+    if mf is not None:
+        out["roofline"]["mfma_executed"] = {
+            "bf16_flop_per_launch": mf[0], "f32_flop_per_launch": mf[1],
+            "bf16_frac_of_peak": round(mf[0] / (pf["ms_chunk"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "source": "rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F32 x 512 FLOP (profiles/)"}
     if not args.no_decode:
         dc = decode_leg(args, torch, np, ops, I)
         gbs = 2 * dc["state_bytes"] / (dc["ms_rec"] * 1e-3) / 1e9
@@ -266,7 +371,7 @@ def main():
                          "achieved": round(alg / (dc["ms_rec"] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(alg / (dc["ms_rec"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                          "traffic": measured_traffic("gdn_recurrent_step"), "avg_launch_ms": round(dc["ms_rec"], 4),
-                         "algorithmic_bytes_per_launch": alg},
+                         "algorithmic_bytes_per_launch": alg, "per_call": dc["rec_stats"]},
         }
     if not args.no_cpu_baseline:
         from oracle import gdn_ref as R
