@@ -17,7 +17,7 @@
 //     S_C  = b_C S0 + U^T diag(exp(gamma_C - gamma) rk) K
 // U solves u_i = beta_i (v_i - a_i S_{i-1} k^_i) for every token of the chunk.
 //
-// Two kernels:
+// Kernels:
 //   k_chunk_prep  persistent workgroups over (chunk, q/k head) units: the
 //                 Gram matrices K K^T and Q K^T on the matrix cores (raw
 //                 operands, exact products) once per unit, then for each v-head
@@ -31,6 +31,8 @@
 //                 walking the sequence's chunks in order with its slice of the
 //                 state in fp32 registers; every contraction with the state or
 //                 a derived operand runs on the matrix cores.
+//   k_seq_order   (calls with several sequences) the sequences longest first,
+//                 the order in which the scan starts them.
 //
 // Data movement of the scan.  Every chunk operand the scan reads (K, Q, Tb,
 // P, K^T) is a matrix-core A operand that exactly one wave uses: wave w owns
@@ -39,8 +41,10 @@
 // registers the MFMAs read -- nothing is staged through LDS -- and issues the
 // next chunk's loads for a register set as soon as the current chunk's MFMAs
 // have consumed it, giving every load a full chunk step of latency.  Only the
-// B operands every wave needs (the state S, X, U and the decayed U) pass
-// through LDS, three barriers per chunk.
+// operands every wave needs (the state S, X, U and the decayed U) pass
+// through LDS, three barriers per chunk.  The outputs are built transposed,
+// O^T = S Q^T and U^T P^T (S and U as A operands, Q and P as B operands), so
+// a lane ends with four consecutive d_v values of one token: one vector store.
 //
 // Operand precision (policy PolBF16): raw bf16 q/k/v are exact single bf16
 // operands; derived operands (S, X, U, Tb, P) are bf16 hi+lo pairs and a

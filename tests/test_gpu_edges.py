@@ -1,6 +1,6 @@
 """GPU edge cases of the chunk and decode entry points against the oracle:
-fp32 inputs at d=128, a non-unit scale with permuted sequences, 300 packed
-sequences, calls whose sequences are all empty, a poisoned workspace, and a hard reset (g = -inf)
+fp32 inputs at d=128, a non-unit scale with permuted sequences, head
+groupings of 1 and 4 v-heads per q/k head, 300 packed sequences, calls whose sequences are all empty, a poisoned workspace, and a hard reset (g = -inf)
 in the decode step.
 """
 import numpy as np
@@ -81,6 +81,22 @@ def test_chunk_scale_and_sequence_permutation(ops):
                       d["state"][perm], scale=scale)
     assert torch.equal(o_p, o[torch.from_numpy(rows).to(DEV)])
     assert torch.equal(fin_p, fin[torch.tensor(perm, device=DEV)])
+
+
+@pytest.mark.parametrize("h_qk,h_v", [(4, 4), (1, 4), (2, 8)])
+def test_chunk_head_grouping(ops, h_qk, h_v):
+    """v-heads per q/k head of 1 and 4 (the model layout has 2), with a
+    scale, ragged sequences and nonzero states, against the oracle."""
+    lay = I.Layout(h_qk=h_qk, h_v=h_v, d_k=128, d_v=128, chunk=64, dtype="bf16")
+    note(f"chunk head grouping {h_qk} q/k heads, {h_v} v-heads")
+    d = I.prefill_inputs(37, lay, [100, 64, 3], state_std=0.02)
+    q, k, v = I.split_qkv(d["x"], lay)
+    o, fin = _run(ops, lay, q, k, v, d["g"], d["beta"], d["cu_seqlens"], d["state"], scale=0.25)
+    o_ref, f_ref = R.gated_delta_rule(q, k, v, d["g"], d["beta"], scale=0.25, initial_state=d["state"],
+                                      cu_seqlens=d["cu_seqlens"])
+    eo, ef = rel_max(host(o), o_ref), rel_max(host(fin), f_ref)
+    note(f"  o {eo:.2e} state {ef:.2e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
 
 
 def test_chunk_many_sequences(ops):
