@@ -46,7 +46,7 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (323_372_851, {"chunk.hip": "8f13dd30ff6815df", "common.hpp": "9789884ded6edf16",
+    "gdn_chunk_fwd": (323_342_746, {"chunk.hip": "b76e7fa050369c00", "common.hpp": "9789884ded6edf16",
                                     "launch.hpp": "87391e0d859dd5e0"}),
     "gdn_recurrent_step": (271_171_379, {"recurrent.hip": "c228b4968470e50e", "common.hpp": "9789884ded6edf16",
                                          "launch.hpp": "87391e0d859dd5e0"}),
@@ -69,7 +69,7 @@ def measured_traffic(entry):
 # traffic above.
 MEASURED_MFMA = {
     "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
-                      {"chunk.hip": "8f13dd30ff6815df", "common.hpp": "9789884ded6edf16",
+                      {"chunk.hip": "b76e7fa050369c00", "common.hpp": "9789884ded6edf16",
                        "launch.hpp": "87391e0d859dd5e0"}),
 }
 
@@ -102,67 +102,9 @@ def call_stats(fn, n, start, torch):
             "max_ms": round(t[-1], 4), "std_ms": round(statistics.pstdev(t), 4)}
 
 
-class ClockSampler:
-    """Samples the shader clock from the device's sysfs node (the level marked
-    '*' in pp_dpm_sclk) on a background thread while the timed calls run; file
-    reads only.  None when the node cannot be matched to the device."""
-
-    def __init__(self, torch, period_s=0.002):
-        import threading
-        self.paths = []
-        props = torch.cuda.get_device_properties(0)
-        bus = getattr(props, "pci_bus_id", None)
-        dev = getattr(props, "pci_device_id", None)
-        dom = getattr(props, "pci_domain_id", 0) or 0
-        if bus is not None and dev is not None:
-            # the sysfs node of this device (a host can list several GPUs)
-            p = f"/sys/bus/pci/devices/{dom:04x}:{bus:02x}:{dev:02x}.0/pp_dpm_sclk"
-            if os.path.exists(p):
-                self.paths = [p]
-        self.period = period_s
-        self.samples = []
-        self._stop = threading.Event()
-        self._thread = threading.Thread(target=self._run, daemon=True)
-
-    def _read(self):
-        for p in self.paths:
-            try:
-                with open(p) as f:
-                    for line in f:
-                        if line.rstrip().endswith("*"):
-                            return int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
-            except (OSError, ValueError, IndexError):
-                continue
-        return None
-
-    def _run(self):
-        while not self._stop.is_set():
-            v = self._read()
-            if v is not None:
-                self.samples.append(v)
-            self._stop.wait(self.period)
-
-    def __enter__(self):
-        if self.paths:
-            self._thread.start()
-        return self
-
-    def __exit__(self, *exc):
-        self._stop.set()
-        if self._thread.is_alive():
-            self._thread.join()
-
-    def median(self):
-        if not self.samples:
-            return None
-        v = sorted(self.samples)
-        return v[len(v) // 2]
-
-
-def environment(torch, sclk=None):
+def environment(torch):
     props = torch.cuda.get_device_properties(0)
-    return {"rocm_hip": torch.version.hip, "arch": getattr(props, "gcnArchName", None),
-            "sclk_mhz_median_during_calls": sclk}
+    return {"rocm_hip": torch.version.hip, "arch": getattr(props, "gcnArchName", None)}
 
 
 def parse():
@@ -237,9 +179,8 @@ def prefill_leg(args, torch, np, ops, I):
 
     ms, wall = timed(step, args.steps, args.warmup, torch)
     ms_chunk, _ = timed(chunk_only, args.steps, args.warmup, torch)
-    with ClockSampler(torch) as clk:
-        stats = call_stats(chunk_only, max(args.steps, 50), args.warmup + args.steps, torch)
-    return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, chunk_stats=stats, sclk=clk.median(), layout=lay)
+    stats = call_stats(chunk_only, max(args.steps, 50), args.warmup + args.steps, torch)
+    return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, chunk_stats=stats, layout=lay)
 
 
 def decode_leg(args, torch, np, ops, I):
@@ -358,7 +299,7 @@ def main():
                      "avg_launch_ms": round(pf["ms_chunk"], 4),
                      "algorithmic_flop_per_launch": flop,
                      "per_call": pf["chunk_stats"]},
-        "env": environment(torch, pf["sclk"]),
+        "env": environment(torch),
     }
     mf = measured_mfma("gdn_chunk_fwd")
     if mf is not None:

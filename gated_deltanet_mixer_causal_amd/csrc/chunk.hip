@@ -742,11 +742,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
       const Elem* kq_ = static_cast<const Elem*>(ws.kq) + ((slot0 + (jj)) * h_qk + hq) * W::kq_elems + lane * FE; \
       _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_D; ++ks_) {                                        \
         kf[ks_] = Pol::ld(kq_ + W::kq_block(0, wave, ks_));                                            \
-        qf[ks_] = Pol::ld(kq_ + W::kq_block(1, wave, ks_));                                            \
       }                                                                                                \
       const float* sc_ = ws.sc + ((slot0 + (jj)) * h_v + h) * (4 * C);                                \
       c1v = *reinterpret_cast<const float4*>(sc_ + orow0);                                             \
-      c2s = sc_[C + 16 * wave + r16];                                                                  \
       c3v = *reinterpret_cast<const float4*>(sc_ + 2 * C + orow0);                                     \
       const typename In::T* vc_ = v + t0_ * v_stride + (int64_t)h * D + dv0 + r16;                     \
       _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                               \
@@ -757,6 +755,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
       vlen = len_;                                                                                     \
     }                                                                                                  \
     bcv = ws.sc[((slot0 + (jj)) * h_v + h) * (4 * C) + 3 * C];                                         \
+  } while (0)
+#define GDN_LOAD_Q(jj)                                                                                 \
+  do {                                                                                                 \
+    if (tok_wave) {                                                                                    \
+      const Elem* kq_ = static_cast<const Elem*>(ws.kq) + ((slot0 + (jj)) * h_qk + hq) * W::kq_elems + lane * FE; \
+      _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_D; ++ks_) qf[ks_] = Pol::ld(kq_ + W::kq_block(1, wave, ks_)); \
+      c2s = ws.sc[((slot0 + (jj)) * h_v + h) * (4 * C) + C + 16 * wave + r16];                         \
+    }                                                                                                  \
   } while (0)
 #define GDN_LOAD_TB(jj)                                                                                \
   do {                                                                                                 \
@@ -792,6 +798,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
 
   if (nchunks > 0) {
     GDN_LOAD_KQ(0);
+    GDN_LOAD_Q(0);
     GDN_LOAD_TB(0);
     GDN_LOAD_PKT(0);
   }
@@ -804,26 +811,25 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     // re-reads its own chunk, so every load is unconditional)
     const int64_t jn = j + 1 < nchunks ? j + 1 : j;
 
-    // ---- A: K S^T and Q S^T for token tile `wave`; X = V - diag(b rk) K S^T ----
+    // ---- A: K S^T for token tile `wave`; X = V - diag(b rk) K S^T ----
     floatx4 Oacc[NV];
+    Frag sfh[NV][NKS_D], sfl[NV][NKS_D];   // S fragments, reused for S Q^T in phase B
     const float4 c3 = c3v;
     const float bc = bcv;
     if (tok_wave) {
-      floatx4 ak[NV], aq[NV];
+      floatx4 ak[NV];
 #pragma unroll
-      for (int nt = 0; nt < NV; ++nt) ak[nt] = aq[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NV; ++nt) ak[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS_D; ++ks) {
 #pragma unroll
         for (int nt = 0; nt < NV; ++nt) {
           const int off = (16 * nt + r16) * LDK + ks * KS + g4 * FE;
-          const Frag shi = Pol::ld(sS + off);
-          ak[nt] = Pol::mma(kf[ks], shi, ak[nt]);
-          aq[nt] = Pol::mma(shi, qf[ks], aq[nt]);   // transposed: lane holds O[16 wave + r16][dv 4 g4 + i]
+          sfh[nt][ks] = Pol::ld(sS + off);
+          ak[nt] = Pol::mma(kf[ks], sfh[nt][ks], ak[nt]);
           if constexpr (NSP == 2) {
-            const Frag slo = Pol::ld(sS_lo + off);
-            ak[nt] = Pol::mma(kf[ks], slo, ak[nt]);
-            aq[nt] = Pol::mma(slo, qf[ks], aq[nt]);
+            sfl[nt][ks] = Pol::ld(sS_lo + off);
+            ak[nt] = Pol::mma(kf[ks], sfl[nt][ks], ak[nt]);
           }
         }
       }
@@ -835,7 +841,6 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
         for (int i = 0; i < 4; ++i) {
           const float vv = (orow0 + i < vlen) ? from_u32<In>(vraw[nt][i]) : 0.f;
           xv[i] = vv - c1[i] * ak[nt][i];
-          Oacc[nt][i] = c2s * aq[nt][i];
         }
         Pol::put4(sX, sX_lo, (16 * nt + r16) * LDT + orow0, xv);
       }
@@ -879,6 +884,21 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     __syncthreads();
 
     // ---- C: O += P U, store rows; S^T <- b_C S^T + K^T U2 ----
+    if (tok_wave) {
+      floatx4 aq[NV];
+#pragma unroll
+      for (int nt = 0; nt < NV; ++nt) {
+        aq[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS_D; ++ks) {
+          aq[nt] = Pol::mma(sfh[nt][ks], qf[ks], aq[nt]);   // transposed: O[16 wave + r16][dv 4 g4 + i]
+          if constexpr (NSP == 2) aq[nt] = Pol::mma(sfl[nt][ks], qf[ks], aq[nt]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Oacc[nt][i] = c2s * aq[nt][i];
+      }
+    }
+    GDN_LOAD_Q(jn);
     if (tok_wave) {
 #pragma unroll
       for (int ks = 0; ks < NKS_C; ++ks) {
@@ -927,6 +947,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   }
 #undef GDN_LOAD_KQ
 #undef GDN_LOAD_TB
+#undef GDN_LOAD_Q
 #undef GDN_LOAD_PKT
 
   if (fin) {
