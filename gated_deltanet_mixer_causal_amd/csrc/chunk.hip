@@ -734,7 +734,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   // V element (row orow0 + i, column dv0 + 16 nt + r16) of a chunk: the chunk's
   // uniform base plus a 32-bit lane offset (strides are at most 2^24)
 
-#define GDN_LOAD_KQ(jj)                                                                                 \
+#define GDN_LOAD_KV(jj)                                                                                 \
   do {                                                                                                 \
     const int64_t t0_ = start + (jj) * C;                                                              \
     const int len_ = static_cast<int>(end - t0_ < C ? end - t0_ : C);                                  \
@@ -797,7 +797,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   } while (0)
 
   if (nchunks > 0) {
-    GDN_LOAD_KQ(0);
+    GDN_LOAD_KV(0);
     GDN_LOAD_Q(0);
     GDN_LOAD_TB(0);
     GDN_LOAD_PKT(0);
@@ -845,8 +845,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
         Pol::put4(sX, sX_lo, (16 * nt + r16) * LDT + orow0, xv);
       }
     }
-    GDN_LOAD_KQ(jn);   // K, Q, V and the scalars of this step are consumed
     __syncthreads();
+    GDN_LOAD_KV(jn);   // K, V and the scalars of this step are consumed
 
     // ---- B: U = Tb X (lower triangular: k up to the tile's last row) ----
     if (tok_wave) {
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     GDN_LOAD_PKT(jn);
     __syncthreads();
   }
-#undef GDN_LOAD_KQ
+#undef GDN_LOAD_KV
 #undef GDN_LOAD_TB
 #undef GDN_LOAD_Q
 #undef GDN_LOAD_PKT
