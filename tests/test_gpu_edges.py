@@ -1,6 +1,7 @@
 """GPU edge cases of the chunk and decode entry points against the oracle:
 fp32 inputs at d=128, a non-unit scale with permuted sequences, head
-groupings of 1 and 4 v-heads per q/k head, 300 packed sequences, calls whose sequences are all empty, a poisoned workspace, and a hard reset (g = -inf)
+groupings of 1 and 4 v-heads per q/k head, an optional final state, 300
+packed sequences, calls whose sequences are all empty, a poisoned workspace, and a hard reset (g = -inf)
 in the decode step.
 """
 import numpy as np
@@ -97,6 +98,45 @@ def test_chunk_head_grouping(ops, h_qk, h_v):
     eo, ef = rel_max(host(o), o_ref), rel_max(host(fin), f_ref)
     note(f"  o {eo:.2e} state {ef:.2e}")
     assert eo <= TOL_BF16 and ef <= TOL_BF16
+
+
+def test_chunk_final_state_optional(ops):
+    """Three sequences, 9,000 tokens, 4 q/k and 8 v-heads: the outputs do not
+    depend on whether a final state is asked for or updated in place (bit for
+    bit), they match the oracle, and a NULL initial state equals zeros."""
+    lay = I.Layout(h_qk=4, h_v=8, d_k=128, d_v=128, chunk=64, dtype="bf16")
+    note("chunk 3 sequences, 9,000 tokens, optional final state")
+    lengths = [5000, 3000, 1000]
+    d = I.prefill_inputs(38, lay, lengths, state_std=0.02)
+    q, k, v = I.split_qkv(d["x"], lay)
+    cu = d["cu_seqlens"]
+    tdt = torch.bfloat16
+    T = q.shape[0]
+    args = (dev(q, tdt), dev(k, tdt), dev(v, tdt), dev(d["g"]), dev(d["beta"]))
+    o_split = torch.full((T, lay.h_v, lay.d_v), float("nan"), device=DEV)
+    fin = torch.full(d["state"].shape, float("nan"), device=DEV)
+    ops.gdn_chunk_fwd(*args, o_split, chunk=64, cu_seqlens=dev_i32(cu), initial_state=dev(d["state"]),
+                      final_state=fin)
+    o_one = torch.full_like(o_split, float("nan"))
+    ops.gdn_chunk_fwd(*args, o_one, chunk=64, cu_seqlens=dev_i32(cu), initial_state=dev(d["state"]))
+    st_inplace = dev(d["state"])
+    o_inplace = torch.full_like(o_split, float("nan"))
+    ops.gdn_chunk_fwd(*args, o_inplace, chunk=64, cu_seqlens=dev_i32(cu), initial_state=st_inplace,
+                      final_state=st_inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(o_split, o_one) and torch.equal(o_split, o_inplace) and torch.equal(fin, st_inplace)
+    o_ref, f_ref = R.gated_delta_rule(q, k, v, d["g"], d["beta"], initial_state=d["state"], cu_seqlens=cu)
+    eo, ef = rel_max(host(o_split), o_ref), rel_max(host(fin), f_ref)
+    note(f"  o {eo:.2e} state {ef:.2e}")
+    assert eo <= TOL_BF16 and ef <= TOL_BF16
+    # NULL initial state
+    o0 = torch.empty_like(o_split)
+    f0 = torch.empty_like(fin)
+    ops.gdn_chunk_fwd(*args, o0, chunk=64, cu_seqlens=dev_i32(cu), final_state=f0)
+    o0_one = torch.empty_like(o_split)
+    ops.gdn_chunk_fwd(*args, o0_one, chunk=64, cu_seqlens=dev_i32(cu))
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o0_one)
 
 
 def test_chunk_many_sequences(ops):
