@@ -24,9 +24,9 @@
 //                 reading that q/k head the decay scalars, L, P and the
 //                 unit-lower-triangular solve (16x16 diagonal blocks by forward
 //                 substitution in registers, off-diagonal blocks by fp32 MFMA).
-//                 It writes Tb, P (split into bf16 hi/lo) and K^T in
-//                 matrix-core fragment order, and loads the next unit's K, Q
-//                 while it computes.
+//                 It writes K, Q, Tb and P (Tb, P split into bf16 hi/lo; for
+//                 fp32 inputs also K^T) in matrix-core fragment order, and
+//                 loads the next unit's K, Q while it computes.
 //   k_chunk_scan  one workgroup per (sequence, v-head, 16-wide d_v slice),
 //                 walking the sequence's chunks in order with its slice of the
 //                 state in fp32 registers; every contraction with the state or
@@ -35,9 +35,11 @@
 //                 the order in which the scan starts them.
 //
 // Data movement of the scan.  Every chunk operand the scan reads (K, Q, Tb,
-// P, K^T) is a matrix-core A operand that exactly one wave uses: wave w owns
-// token rows 16w..16w+15 of K, Q, Tb and P and the d_k rows 16(w + 4j) of
-// K^T.  So each wave loads its fragments straight from memory into the
+// P) is a matrix-core operand that exactly one wave uses: wave w owns token
+// rows 16w..16w+15 of K, Q, Tb and P.  The K^T operands of the state update
+// (d_k rows 16(w + 4j)) come from the chunk's K rows, which the waves leave in
+// LDS, through transposing LDS reads (bf16); for fp32 inputs from a K^T copy
+// in the workspace.  So each wave loads its fragments straight from memory into the
 // registers the MFMAs read -- nothing is staged through LDS -- and issues the
 // next chunk's loads for a register set as soon as the current chunk's MFMAs
 // have consumed it, giving every load a full chunk step of latency.  Only the
@@ -76,6 +78,10 @@ struct PolBF16 {
   static constexpr int FE = 8;        // elements per lane per fragment
   static constexpr int PAD = 8;
   static constexpr int NSPLIT = 2;    // hi and lo arrays
+  // The scan keeps the chunk's K in LDS and builds the K^T operands of the
+  // state update with transposing LDS reads (16-bit elements), so the
+  // workspace holds no K^T copy.
+  static constexpr bool kKtInLds = true;
 
   __device__ __forceinline__ static floatx4 mma(Frag a, Frag b, floatx4 c) { return mfma_bf16(a, b, c); }
   __device__ __forceinline__ static Frag ld(const Elem* p) { return *reinterpret_cast<const Frag*>(p); }
@@ -156,6 +162,7 @@ struct PolF32 {
   static constexpr int FE = 1;
   static constexpr int PAD = 4;
   static constexpr int NSPLIT = 1;    // fp32 operands need no lo part
+  static constexpr bool kKtInLds = false;   // K^T fragments come from the workspace
 
   __device__ __forceinline__ static floatx4 mma(Frag a, Frag b, floatx4 c) { return mfma_f32(a, b, c); }
   __device__ __forceinline__ static Frag ld(const Elem* p) { return *p; }
@@ -201,7 +208,7 @@ __device__ __forceinline__ float from_u32<F32>(uint32_t x) { return __uint_as_fl
 
 // Workspace, all indexed by chunk slot (see locate_block):
 //   kq [slots][h_qk][2][C*D]       K, Q fragments (raw): blocks (token tile mt, d_k k-step ks)
-//   kt [slots][h_qk][D*C]          K^T fragments: blocks (dk tile mt, k-step ks)
+//   kt [slots][h_qk][D*C]          K^T fragments: blocks (dk tile mt, k-step ks); fp32 only
 //   tb [slots][h_v][NSPLIT*C*C]    Tb fragments:  blocks (token tile mt, k-step ks, hi|lo)
 //   p  [slots][h_v][NSPLIT*C*C]    P fragments:   same order
 //   sc [slots][h_v][4][C] fp32     b rk | scale b rq | exp(gamma_C - gamma) rk | b_C
@@ -238,8 +245,11 @@ struct WsLayout {
   }
   static size_t al(size_t x) { return (x + 255) & ~size_t(255); }
   static size_t order_bytes(int n_seq) { return n_seq > 1 ? al(sizeof(int32_t) * n_seq) : 0; }
+  static size_t kt_bytes(int64_t slots, int h_qk) {
+    return Pol::kKtInLds ? 0 : al(sizeof(Elem) * slots * h_qk * kt_elems);
+  }
   static size_t bytes(int64_t slots, int h_qk, int h_v, int n_seq) {
-    return al(sizeof(Elem) * slots * h_qk * kq_elems) + al(sizeof(Elem) * slots * h_qk * kt_elems) +
+    return al(sizeof(Elem) * slots * h_qk * kq_elems) + kt_bytes(slots, h_qk) +
            2 * al(sizeof(Elem) * slots * h_v * op_elems) + al(sizeof(float) * slots * h_v * 4 * C) +
            order_bytes(n_seq);
   }
@@ -249,7 +259,7 @@ struct WsLayout {
     w.kq = b;
     b += al(sizeof(Elem) * slots * h_qk * kq_elems);
     w.kt = b;
-    b += al(sizeof(Elem) * slots * h_qk * kt_elems);
+    b += kt_bytes(slots, h_qk);
     w.tb = b;
     b += al(sizeof(Elem) * slots * h_v * op_elems);
     w.p = b;
@@ -428,7 +438,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
         *reinterpret_cast<Frag*>(kqb + W::kq_block(which, mt, ks) + l * FE) = Pol::ld(src);
       }
     }
-    {
+    if constexpr (!Pol::kKtInLds) {
       Elem* kt = static_cast<Elem*>(ws.kt) + (cslot * h_qk + hq) * W::kt_elems;
       for (int f = tid; f < (D / 16) * NKS_C * 64; f += 256) {
         const int l = f & 63, blk = f >> 6;
@@ -572,6 +582,17 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 #undef GDN_PREP_FETCH
 }
 
+// Transposing LDS read of 16-bit elements (gfx950 ds_read_b64_tr_b16): in each
+// group of 16 lanes, lane i receives element i % 4 of the 8-byte rows that the
+// lanes (i / 4) + 4 j address, j = 0..3 (checked on the device with a probe of
+// distinct values).  Returned as the raw 64 bits (four bf16, element 0 low).
+__device__ __forceinline__ uint2 lds_read_tr16(const __bf16* p) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf16_t;
+  auto q = reinterpret_cast<__attribute__((address_space(3))) v4bf16_t*>(
+      (__attribute__((address_space(3))) __bf16*)(const_cast<__bf16*>(p)));
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(q));
+}
+
 // Four consecutive output values of one row (one 16- or 8-byte store).
 template <class EO>
 __device__ __forceinline__ void store_row4(typename EO::T* p, floatx4 v);
@@ -665,6 +686,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   __shared__ __attribute__((aligned(16))) Elem sU[NSP * BV * LDT];
   __shared__ __attribute__((aligned(16))) Elem sU2[NSP * BV * LDT];
   __shared__ __attribute__((aligned(16))) Elem sS[NSP * BV * LDK];
+  // the chunk's K rows (bf16 policy): rows of LDKT elements, a stride of 8
+  // banks, so the four rows a transposing read touches use distinct banks
+  constexpr int LDKT = D + 16;
+  __shared__ __attribute__((aligned(16))) Elem sKt[Pol::kKtInLds ? C * LDKT : 1];
   Elem* const sX_lo = sX + (NSP - 1) * BV * LDT;
   Elem* const sU_lo = sU + (NSP - 1) * BV * LDT;
   Elem* const sU2_lo = sU2 + (NSP - 1) * BV * LDT;
@@ -787,11 +812,13 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
         }                                                                                              \
       }                                                                                                \
     }                                                                                                  \
-    const Elem* kt_ = static_cast<const Elem*>(ws.kt) + ((slot0 + (jj)) * h_qk + hq) * W::kt_elems + lane * FE; \
-    _Pragma("unroll") for (int j_ = 0; j_ < SPW; ++j_) {                                               \
-      if (kAllTiles || wave + 4 * j_ < NST) {                                                          \
-        _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_C; ++ks_)                                        \
-            ktf[j_][ks_] = Pol::ld(kt_ + W::kt_block(wave + 4 * j_, ks_));                             \
+    if constexpr (!Pol::kKtInLds) {                                                                    \
+      const Elem* kt_ = static_cast<const Elem*>(ws.kt) + ((slot0 + (jj)) * h_qk + hq) * W::kt_elems + lane * FE; \
+      _Pragma("unroll") for (int j_ = 0; j_ < SPW; ++j_) {                                             \
+        if (kAllTiles || wave + 4 * j_ < NST) {                                                        \
+          _Pragma("unroll") for (int ks_ = 0; ks_ < NKS_C; ++ks_)                                      \
+              ktf[j_][ks_] = Pol::ld(kt_ + W::kt_block(wave + 4 * j_, ks_));                           \
+        }                                                                                              \
       }                                                                                                \
     }                                                                                                  \
   } while (0)
@@ -832,6 +859,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
             ak[nt] = Pol::mma(kf[ks], sfl[nt][ks], ak[nt]);
           }
         }
+      }
+      if constexpr (Pol::kKtInLds) {
+        // the K rows of this token tile, for the K^T operands of the state update
+#pragma unroll
+        for (int ks = 0; ks < NKS_D; ++ks)
+          *reinterpret_cast<Frag*>(sKt + (16 * wave + r16) * LDKT + ks * KS + g4 * FE) = kf[ks];
       }
       const float c1[4] = {c1v.x, c1v.y, c1v.z, c1v.w};
 #pragma unroll
@@ -933,8 +966,20 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
 #pragma unroll
           for (int ks = 0; ks < NKS_C; ++ks) {
             const int off = (16 * nt + r16) * LDT + ks * KS + g4 * FE;
-            acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2 + off), acc);
-            if constexpr (NSP == 2) acc = Pol::mma(ktf[jj][ks], Pol::ld(sU2_lo + off), acc);
+            Frag kt;
+            if constexpr (Pol::kKtInLds) {
+              // lane (r16, g4): K[tokens ks*KS + 8 g4 + 0..7][d_k 16 mt + r16], as two
+              // transposing reads of four tokens (lane r16 addresses row r16 / 4,
+              // columns 4 (r16 % 4) .. + 3 of the 16-column block)
+              const Elem* kp = sKt + (ks * KS + 8 * g4 + (r16 >> 2)) * LDKT + 16 * mt + 4 * (r16 & 3);
+              const uint2 a = lds_read_tr16(kp);
+              const uint2 b = lds_read_tr16(kp + 4 * LDKT);
+              kt = __builtin_bit_cast(Frag, make_uint4(a.x, a.y, b.x, b.y));
+            } else {
+              kt = ktf[jj][ks];
+            }
+            acc = Pol::mma(kt, Pol::ld(sU2 + off), acc);
+            if constexpr (NSP == 2) acc = Pol::mma(kt, Pol::ld(sU2_lo + off), acc);
           }
           Sacc[jj][nt] = acc;
           const float tmp[4] = {acc[0], acc[1], acc[2], acc[3]};

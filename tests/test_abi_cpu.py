@@ -109,18 +109,16 @@ def test_chunk_workspace_size(lib):
     out = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0
     slots = 4096 // 64 + 1
-    # per q/k head: K and Q fragments, transposed K (bf16); per v-head: Tb and P as
-    # bf16 hi+lo, fp32 scalars
-    expect = (slots * 16 * 2 * 64 * 128 * 2 + slots * 16 * 128 * 64 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2
-              + slots * 32 * 4 * 64 * 4)
+    # per q/k head: K and Q fragments (bf16); per v-head: Tb and P as bf16 hi+lo,
+    # fp32 scalars (the bf16 scan builds K^T from K in LDS)
+    expect = (slots * 16 * 2 * 64 * 128 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2 + slots * 32 * 4 * 64 * 4)
     assert out.value == expect
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 1, ctypes.byref(out)) == 0
     assert out.value == expect + 4096 * 32 * 128 * 4
     # several sequences: one slot more per sequence, and the longest-first order (int32 each)
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 8, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0
     slots = 4096 // 64 + 8
-    expect = (slots * 16 * 2 * 64 * 128 * 2 + slots * 16 * 128 * 64 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2
-              + slots * 32 * 4 * 64 * 4 + 256)
+    expect = (slots * 16 * 2 * 64 * 128 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2 + slots * 32 * 4 * 64 * 4 + 256)
     assert out.value == expect
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, None) == L.GDN_ERR_NULL
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 64, 64, 64, 1, 4096, L.GDN_BF16, 0,
