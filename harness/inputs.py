@@ -146,6 +146,24 @@ def prefill_inputs(seed: int, layout: Layout, lengths, *, state_std: float | Non
                 lengths=lengths, scale=1.0, l2_eps=L2_EPS, norm_eps=NORM_EPS)
 
 
+def raw_gate_inputs(seed: int, t: int, h_v: int, *, dtype: str = "f32",
+                    a_log_range=(0.0, math.log(16.0)), bias_std: float | None = None) -> dict:
+    """Raw gate projections for the fused gate preparation.
+
+    a, b ~ N(0,1) [T, Hv] (rounded to bf16 when dtype is "bf16"); a_log ~
+    U(a_log_range) per v-head; dt_bias ~ N(0, bias_std^2) per v-head, or None.
+    With the default range and no bias, -exp(a_log) softplus(a) has the same
+    distribution as the model workload's log-decay.  Draw order: a_log, a, b,
+    dt_bias.
+    """
+    rng = np.random.default_rng(seed)
+    a_log = rng.uniform(a_log_range[0], a_log_range[1], h_v).astype(np.float32)
+    a = _cast(_normal(rng, (t, h_v)), dtype)
+    b = _cast(_normal(rng, (t, h_v)), dtype)
+    dt_bias = None if bias_std is None else _normal(rng, (h_v,), bias_std)
+    return dict(a=a, b=b, a_log=a_log, dt_bias=dt_bias)
+
+
 def split_qkv(x: np.ndarray, layout: Layout):
     """Views of the q | k | v channel blocks of a [T, Ch] array as per-head arrays."""
     t = x.shape[0]

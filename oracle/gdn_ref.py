@@ -37,6 +37,13 @@ the design notes of the repository):
   * For bf16 workloads the conv output is a bf16 tensor at the library
     boundary, so the oracle rounds SiLU(conv) to bf16 (nearest, ties to even)
     before the recurrence reads it; everything else stays float64.
+  * Gate preparation from the raw gate projections (the B/A projection pair
+    the pages give the GDN mixer: Flare core-design, the paragraph on fused
+    projection weights): g = -exp(A_log[h]) softplus(a[t,h] + dt_bias[h])
+    and beta = sigmoid(b[t,h]).  The pages print neither formula; this is the
+    plainest reading that fits the log-decay g < 0 of the rule above and a
+    write strength beta in (0, 1).  dt_bias is an optional per-head bias
+    (absent = 0).
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (closed forms, invariants, brute force, an
@@ -79,6 +86,48 @@ def l2_normalize(x, eps: float):
     """x / sqrt(sum(x^2) + eps) over the last axis."""
     x = np.asarray(x, dtype=np.float64)
     return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def softplus(x):
+    """softplus(x) = ln(1 + e^x), written as max(x, 0) + ln(1 + e^-|x|) so that
+    no exponential overflows (the two forms are equal for every real x)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x):
+    """sigmoid(x) = 1 / (1 + e^-x), evaluated through e^-|x| so that no
+    exponential overflows."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+# ---------------------------------------------------------------------------
+# Gate preparation
+# ---------------------------------------------------------------------------
+
+def gates_from_projections(a, b, a_log, dt_bias=None):
+    """Log-decay g and write strength beta from the raw gate projections.
+
+    a, b [T, Hv] are the outputs of the A and B gate projections (Flare
+    core-design, fused projection weights paragraph); a_log and dt_bias are
+    per-v-head parameters [Hv].  For every token t and v-head h:
+        g[t, h]    = -exp(a_log[h]) * softplus(a[t, h] + dt_bias[h])
+        beta[t, h] = sigmoid(b[t, h])
+    dt_bias None means a zero bias.  Returns (g, beta) as float64 [T, Hv].
+    """
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    a_log = np.asarray(a_log, np.float64)
+    t, hv = a.shape
+    g = np.empty((t, hv))
+    beta = np.empty((t, hv))
+    for h in range(hv):
+        bias = 0.0 if dt_bias is None else float(np.asarray(dt_bias, np.float64)[h])
+        g[:, h] = -math.exp(a_log[h]) * softplus(a[:, h] + bias)
+        beta[:, h] = sigmoid(b[:, h])
+    return g, beta
 
 
 # ---------------------------------------------------------------------------

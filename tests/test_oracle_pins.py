@@ -417,3 +417,80 @@ def test_decode_steps_equal_prefill_and_inactive_lanes():
     np.testing.assert_array_equal(tails[1], ref["tail"][0])
     assert np.all(tails[0] == 7.0) and np.all(tails[2] == 9.0)
     assert np.all(states[0] == 5.0) and np.all(states[2] == 6.0)
+
+
+# ---------------------------------------------------------------------------
+# Gate preparation from the raw gate projections
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("x,expect", [
+    (0.0, math.log(2.0)),               # ln(1 + 1)
+    (math.log(3.0), 2.0 * math.log(2.0)),   # ln(1 + 3) = ln 4
+    (-math.log(3.0), math.log(4.0 / 3.0)),  # ln(1 + 1/3)
+    (50.0, 50.0 + math.exp(-50.0)),      # far right: x + e^-x to first order
+    (-50.0, math.exp(-50.0)),            # far left: e^x to first order
+    (-800.0, 0.0),                       # e^-800 underflows to 0 without overflow on the way
+    (800.0, 800.0),
+])
+def test_softplus_closed_forms(x, expect):
+    assert R.softplus(np.float64(x)) == pytest.approx(expect, rel=1e-15, abs=1e-300)
+
+
+def test_softplus_odd_part_and_slope():
+    # softplus(x) - softplus(-x) = x for every x, and its slope is the sigmoid
+    x = np.linspace(-30.0, 30.0, 601)
+    np.testing.assert_allclose(R.softplus(x) - R.softplus(-x), x, rtol=0, atol=1e-13)
+    h = 1e-5
+    slope = (R.softplus(x + h) - R.softplus(x - h)) / (2 * h)
+    np.testing.assert_allclose(slope, 1.0 / (1.0 + np.exp(-x)), rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("x,expect", [
+    (0.0, 0.5), (math.log(3.0), 0.75), (-math.log(3.0), 0.25), (-800.0, 0.0), (800.0, 1.0),
+])
+def test_sigmoid_closed_forms(x, expect):
+    assert R.sigmoid(np.float64(x)) == pytest.approx(expect, rel=1e-15, abs=1e-300)
+
+
+def test_sigmoid_symmetry():
+    x = np.linspace(-40.0, 40.0, 801)
+    np.testing.assert_allclose(R.sigmoid(x) + R.sigmoid(-x), 1.0, rtol=0, atol=1e-15)
+
+
+def test_gates_closed_forms_and_head_indexing():
+    # a = ln 3 gives softplus = ln 4 exactly; a_log = ln 2 doubles it; b = ln 3 gives beta = 3/4
+    t, hv = 5, 3
+    a = np.full((t, hv), math.log(3.0))
+    b = np.full((t, hv), math.log(3.0))
+    a_log = np.array([0.0, math.log(2.0), math.log(0.5)])
+    g, beta = R.gates_from_projections(a, b, a_log)
+    for h, mult in enumerate([1.0, 2.0, 0.5]):
+        np.testing.assert_allclose(g[:, h], -mult * math.log(4.0), rtol=1e-15)
+    np.testing.assert_allclose(beta, 0.75, rtol=1e-15)
+    assert np.all(g < 0)
+
+
+def test_gates_bias_is_a_shift_of_a():
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((7, 4))
+    b = rng.standard_normal((7, 4))
+    a_log = rng.uniform(0, math.log(16.0), 4)
+    bias = rng.standard_normal(4)
+    g1, b1 = R.gates_from_projections(a, b, a_log, bias)
+    g2, b2 = R.gates_from_projections(a + bias[None, :], b, a_log)
+    np.testing.assert_allclose(g1, g2, rtol=1e-15)
+    np.testing.assert_array_equal(b1, b2)
+    # beta ignores a, a_log and the bias; g ignores b
+    g3, b3 = R.gates_from_projections(a, -b, a_log, bias)
+    np.testing.assert_array_equal(g3, g1)
+    np.testing.assert_allclose(b3, 1.0 - b1, rtol=0, atol=1e-15)
+
+
+def test_gates_match_log_decay_recipe():
+    # g = -exp(A) softplus(n): the decay becomes exp(g) = (1 + e^n)^(-exp(A)),
+    # a product form computed here without the oracle's functions
+    rng = np.random.default_rng(6)
+    n = rng.standard_normal((9, 2))
+    A = rng.uniform(0, math.log(16.0), 2)
+    g, _ = R.gates_from_projections(n, np.zeros_like(n), A)
+    np.testing.assert_allclose(np.exp(g), (1.0 + np.exp(n)) ** (-np.exp(A)[None, :]), rtol=1e-13)
