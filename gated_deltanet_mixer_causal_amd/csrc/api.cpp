@@ -57,11 +57,82 @@ gdn_status finish(hipError_t e) {
   return GDN_OK;
 }
 
-// Shared checks of the q/k/v/g/beta arguments of the recurrence entry points.
+// The gates of a recurrence call as the caller passed them: fp32 g and beta,
+// or (raw) the gate projections a, b with a_log and an optional dt_bias.
+struct GateArgs {
+  bool raw;
+  const float* g;
+  const float* beta;
+  const void* a;
+  const void* b;
+  int64_t ab_stride;
+  gdn_dtype ab_dt;
+  const float* a_log;
+  const float* dt_bias;
+
+  bool rows_missing() const { return raw ? (!a || !b) : (!g || !beta); }
+};
+
+GateArgs plain_gates(const float* g, const float* beta) {
+  return GateArgs{false, g, beta, nullptr, nullptr, 0, GDN_F32, nullptr, nullptr};
+}
+
+GateArgs raw_gates(const void* a, const void* b, int64_t ab_stride, gdn_dtype ab_dt, const float* a_log,
+                   const float* dt_bias) {
+  return GateArgs{true, nullptr, nullptr, a, b, ab_stride, ab_dt, a_log, dt_bias};
+}
+
+// Validated gates of `rows` token rows: the kernels' gate source and the byte
+// ranges the gate inputs occupy (for the overlap checks of the outputs).
+struct Gates {
+  gdn::GateSrc src{};
+  Range r[4]{};
+};
+
+gdn_status check_gates(const GateArgs& ga, int64_t rows, int32_t h_v, Gates& out) {
+  out = Gates{};
+  if (!ga.raw) {
+    if (!all_aligned({ga.g, ga.beta})) return GDN_ERR_ALIGN;
+    out.src.g = ga.g;
+    out.src.beta = ga.beta;
+    out.r[0] = Range{ga.g, static_cast<uint64_t>(rows) * h_v * 4};
+    out.r[1] = Range{ga.beta, static_cast<uint64_t>(rows) * h_v * 4};
+    return GDN_OK;
+  }
+  if (!ga.a_log) return GDN_ERR_NULL;
+  if (!dt_valid(ga.ab_dt)) return GDN_ERR_UNSUPPORTED;
+  const int64_t stride = ga.ab_stride == 0 ? h_v : ga.ab_stride;
+  if (stride < h_v) return GDN_ERR_INVALID;
+  // a and b are read one element at a time, so element alignment suffices
+  // (a packed [rows, 2 h_v] b|a tensor puts a at an offset of h_v elements)
+  const int eb = dt_bytes(ga.ab_dt);
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(ga.a), pb = reinterpret_cast<uintptr_t>(ga.b);
+  if (pa % eb || pb % eb || reinterpret_cast<uintptr_t>(ga.a_log) % 4 || reinterpret_cast<uintptr_t>(ga.dt_bias) % 4)
+    return GDN_ERR_ALIGN;
+  out.src.a = ga.a;
+  out.src.b = ga.b;
+  out.src.ab_stride = stride;
+  out.src.ab_bf16 = ga.ab_dt == GDN_BF16;
+  out.src.a_log = ga.a_log;
+  out.src.dt_bias = ga.dt_bias;
+  out.r[0] = Range{ga.a, strided_bytes(rows, stride, h_v, eb)};
+  out.r[1] = Range{ga.b, strided_bytes(rows, stride, h_v, eb)};
+  out.r[2] = Range{ga.a_log, static_cast<uint64_t>(h_v) * 4};
+  out.r[3] = Range{ga.dt_bias, ga.dt_bias ? static_cast<uint64_t>(h_v) * 4 : 0};
+  return GDN_OK;
+}
+
+bool disjoint_gates(const Range& out, const Gates& gt) {
+  for (const Range& r : gt.r)
+    if (overlap(out, r)) return false;
+  return true;
+}
+
+// Shared checks of the q/k/v arguments of the recurrence entry points.
 gdn_status check_qkv(const void* q, const void* k, const void* v, int64_t& q_stride, int64_t& k_stride,
-                     int64_t& v_stride, gdn_dtype dt, const float* g, const float* beta, int32_t h_qk,
+                     int64_t& v_stride, gdn_dtype dt, bool gate_rows_missing, int32_t h_qk,
                      int32_t h_v, int32_t d_k, int32_t d_v, bool has_rows = true) {
-  if (has_rows && (!q || !k || !v || !g || !beta)) return GDN_ERR_NULL;
+  if (has_rows && (!q || !k || !v || gate_rows_missing)) return GDN_ERR_NULL;
   if (h_qk <= 0 || h_v <= 0 || d_k <= 0 || d_v <= 0 || h_v % h_qk != 0) return GDN_ERR_INVALID;
   if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
   if (q_stride == 0) q_stride = static_cast<int64_t>(h_qk) * d_k;
@@ -74,7 +145,7 @@ gdn_status check_qkv(const void* q, const void* k, const void* v, int64_t& q_str
   constexpr int64_t kMaxStride = int64_t(1) << 24;
   if (q_stride > kMaxStride || k_stride > kMaxStride || v_stride > kMaxStride) return GDN_ERR_INVALID;
   if (q_stride % 8 || k_stride % 8 || v_stride % 8) return GDN_ERR_ALIGN;
-  if (!all_aligned({q, k, v, g, beta})) return GDN_ERR_ALIGN;
+  if (!all_aligned({q, k, v})) return GDN_ERR_ALIGN;
   return GDN_OK;
 }
 
@@ -154,15 +225,23 @@ gdn_status gdn_chunk_fwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, 
   return GDN_OK;
 }
 
-gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
-                         int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
-                         int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
-                         int32_t chunk, const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
-                         const float* initial_state, float* final_state, void* o, gdn_dtype o_dt, const void* z,
-                         const float* norm_w, float norm_eps, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                          int64_t v_stride, gdn_dtype dt, const GateArgs& ga, float scale, int32_t use_qk_l2norm,
+                          float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t chunk,
+                          const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total, const float* initial_state,
+                          float* final_state, void* o, gdn_dtype o_dt, const void* z, const float* norm_w,
+                          float norm_eps, void* workspace, size_t ws_bytes, void* stream) {
   if (n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
   if (n_seq == 0) return GDN_OK;
-  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, g, beta, h_qk, h_v, d_k, d_v, t_total > 0);
+  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, ga.rows_missing(), h_qk, h_v, d_k, d_v,
+                            t_total > 0);
+  if (st != GDN_OK) return st;
+  Gates gt;
+  st = check_gates(ga, t_total, h_v, gt);
   if (st != GDN_OK) return st;
   if (!o && t_total > 0) return GDN_ERR_NULL;
   if (!workspace) return GDN_ERR_WORKSPACE;
@@ -179,8 +258,6 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_
   const Range rq{q, strided_bytes(t_total, q_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
   const Range rk{k, strided_bytes(t_total, k_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
   const Range rv{v, strided_bytes(t_total, v_stride, static_cast<int64_t>(h_v) * d_v, eb)};
-  const Range rg{g, static_cast<uint64_t>(t_total) * h_v * 4};
-  const Range rb{beta, static_cast<uint64_t>(t_total) * h_v * 4};
   const Range ro{o, static_cast<uint64_t>(t_total) * h_v * d_v * dt_bytes(o_dt)};
   const Range rz{z, z ? static_cast<uint64_t>(t_total) * h_v * d_v * eb : 0};
   const Range rw{norm_w, z ? static_cast<uint64_t>(d_v) * 4 : 0};
@@ -188,15 +265,15 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_
   const Range rf{final_state, final_state ? state_bytes : 0};
   const Range rws{workspace, need};
   const Range rcu{cu_seqlens, cu_seqlens ? static_cast<uint64_t>(n_seq + 1) * 4 : 0};
-  if (!disjoint(ro, {rq, rk, rv, rg, rb, rz, rw, ri, rf, rws, rcu})) return GDN_ERR_ALIAS;
-  if (!disjoint(rws, {rq, rk, rv, rg, rb, rz, rw, ri, rf, rcu})) return GDN_ERR_ALIAS;
-  if (!disjoint(rf, {rq, rk, rv, rg, rb, rz, rw, rcu})) return GDN_ERR_ALIAS;
+  if (!disjoint(ro, {rq, rk, rv, rz, rw, ri, rf, rws, rcu}) || !disjoint_gates(ro, gt)) return GDN_ERR_ALIAS;
+  if (!disjoint(rws, {rq, rk, rv, rz, rw, ri, rf, rcu}) || !disjoint_gates(rws, gt)) return GDN_ERR_ALIAS;
+  if (!disjoint(rf, {rq, rk, rv, rz, rw, rcu}) || !disjoint_gates(rf, gt)) return GDN_ERR_ALIAS;
   if (initial_state && final_state && initial_state != final_state && overlap(ri, rf)) return GDN_ERR_ALIAS;
 
   gdn::ChunkArgs a;
   a.q = q; a.k = k; a.v = v;
   a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride;
-  a.dt = dt; a.g = g; a.beta = beta; a.scale = scale;
+  a.dt = dt; a.gate = gt.src; a.scale = scale;
   a.use_l2 = use_qk_l2norm != 0; a.l2_eps = l2_eps;
   a.h_qk = h_qk; a.h_v = h_v; a.d = d_k; a.chunk = chunk;
   a.cu = cu_seqlens; a.n_seq = n_seq; a.t_total = t_total;
@@ -206,15 +283,18 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_
   return finish(gdn::launch_chunk_fwd(a));
 }
 
-gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
-                              int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
-                              int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k,
-                              int32_t d_v, int32_t n_req, float* state, int32_t n_slots,
-                              const int32_t* state_slots, void* o, gdn_dtype o_dt, const void* z,
-                              const float* norm_w, float norm_eps, void* stream) {
+gdn_status recurrent_step_impl(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                               int64_t v_stride, gdn_dtype dt, const GateArgs& ga, float scale,
+                               int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k,
+                               int32_t d_v, int32_t n_req, float* state, int32_t n_slots,
+                               const int32_t* state_slots, void* o, gdn_dtype o_dt, const void* z,
+                               const float* norm_w, float norm_eps, void* stream) {
   if (n_req < 0 || n_slots < 0) return GDN_ERR_INVALID;
   if (n_req == 0) return GDN_OK;
-  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, g, beta, h_qk, h_v, d_k, d_v);
+  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, ga.rows_missing(), h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  Gates gt;
+  st = check_gates(ga, n_req, h_v, gt);
   if (st != GDN_OK) return st;
   if (!state || !o) return GDN_ERR_NULL;
   if (z && !norm_w) return GDN_ERR_NULL;
@@ -226,26 +306,75 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, int64
   const Range rq{q, strided_bytes(n_req, q_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
   const Range rk{k, strided_bytes(n_req, k_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
   const Range rv{v, strided_bytes(n_req, v_stride, static_cast<int64_t>(h_v) * d_v, eb)};
-  const Range rg{g, static_cast<uint64_t>(n_req) * h_v * 4};
-  const Range rb{beta, static_cast<uint64_t>(n_req) * h_v * 4};
   const Range rs{state, static_cast<uint64_t>(n_slots) * h_v * d_v * d_k * 4};
   const Range ro{o, static_cast<uint64_t>(n_req) * h_v * d_v * dt_bytes(o_dt)};
   const Range rz{z, z ? static_cast<uint64_t>(n_req) * h_v * d_v * eb : 0};
   const Range rw{norm_w, z ? static_cast<uint64_t>(d_v) * 4 : 0};
   const Range rsl{state_slots, state_slots ? static_cast<uint64_t>(n_req) * 4 : 0};
-  if (!disjoint(ro, {rq, rk, rv, rg, rb, rs, rz, rw, rsl})) return GDN_ERR_ALIAS;
-  if (!disjoint(rs, {rq, rk, rv, rg, rb, rz, rw, rsl})) return GDN_ERR_ALIAS;
+  if (!disjoint(ro, {rq, rk, rv, rs, rz, rw, rsl}) || !disjoint_gates(ro, gt)) return GDN_ERR_ALIAS;
+  if (!disjoint(rs, {rq, rk, rv, rz, rw, rsl}) || !disjoint_gates(rs, gt)) return GDN_ERR_ALIAS;
 
   gdn::StepArgs a;
   a.q = q; a.k = k; a.v = v;
   a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride;
-  a.dt = dt; a.g = g; a.beta = beta; a.scale = scale;
+  a.dt = dt; a.gate = gt.src; a.scale = scale;
   a.use_l2 = use_qk_l2norm != 0; a.l2_eps = l2_eps;
   a.h_qk = h_qk; a.h_v = h_v; a.d = d_k; a.n_req = n_req;
   a.state = state; a.slots = state_slots;
   a.o = o; a.o_dt = o_dt; a.z = z; a.norm_w = norm_w; a.norm_eps = norm_eps;
   a.stream = stream;
   return finish(gdn::launch_recurrent_step(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                         int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                         int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                         int32_t chunk, const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                         const float* initial_state, float* final_state, void* o, gdn_dtype o_dt, const void* z,
+                         const float* norm_w, float norm_eps, void* workspace, size_t ws_bytes, void* stream) {
+  return chunk_fwd_impl(q, k, v, q_stride, k_stride, v_stride, dt, plain_gates(g, beta), scale, use_qk_l2norm,
+                        l2_eps, h_qk, h_v, d_k, d_v, chunk, cu_seqlens, n_seq, t_total, initial_state,
+                        final_state, o, o_dt, z, norm_w, norm_eps, workspace, ws_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                               int64_t v_stride, gdn_dtype dt, const void* a, const void* b, int64_t ab_stride,
+                               gdn_dtype ab_dt, const float* a_log, const float* dt_bias, float scale,
+                               int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k,
+                               int32_t d_v, int32_t chunk, const int32_t* cu_seqlens, int32_t n_seq,
+                               int64_t t_total, const float* initial_state, float* final_state, void* o,
+                               gdn_dtype o_dt, const void* z, const float* norm_w, float norm_eps, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  return chunk_fwd_impl(q, k, v, q_stride, k_stride, v_stride, dt, raw_gates(a, b, ab_stride, ab_dt, a_log, dt_bias),
+                        scale, use_qk_l2norm, l2_eps, h_qk, h_v, d_k, d_v, chunk, cu_seqlens, n_seq, t_total,
+                        initial_state, final_state, o, o_dt, z, norm_w, norm_eps, workspace, ws_bytes, stream);
+}
+
+gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                              int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                              int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k,
+                              int32_t d_v, int32_t n_req, float* state, int32_t n_slots,
+                              const int32_t* state_slots, void* o, gdn_dtype o_dt, const void* z,
+                              const float* norm_w, float norm_eps, void* stream) {
+  return recurrent_step_impl(q, k, v, q_stride, k_stride, v_stride, dt, plain_gates(g, beta), scale, use_qk_l2norm,
+                             l2_eps, h_qk, h_v, d_k, d_v, n_req, state, n_slots, state_slots, o, o_dt, z, norm_w,
+                             norm_eps, stream);
+}
+
+gdn_status gdn_recurrent_step_gated(const void* q, const void* k, const void* v, int64_t q_stride,
+                                    int64_t k_stride, int64_t v_stride, gdn_dtype dt, const void* a, const void* b,
+                                    int64_t ab_stride, gdn_dtype ab_dt, const float* a_log, const float* dt_bias,
+                                    float scale, int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v,
+                                    int32_t d_k, int32_t d_v, int32_t n_req, float* state, int32_t n_slots,
+                                    const int32_t* state_slots, void* o, gdn_dtype o_dt, const void* z,
+                                    const float* norm_w, float norm_eps, void* stream) {
+  return recurrent_step_impl(q, k, v, q_stride, k_stride, v_stride, dt,
+                             raw_gates(a, b, ab_stride, ab_dt, a_log, dt_bias), scale, use_qk_l2norm, l2_eps, h_qk,
+                             h_v, d_k, d_v, n_req, state, n_slots, state_slots, o, o_dt, z, norm_w, norm_eps, stream);
 }
 
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w, float eps,

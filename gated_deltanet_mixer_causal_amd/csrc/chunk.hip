@@ -295,8 +295,7 @@ __device__ __forceinline__ void lds_row(const T* p, T* out) {
 template <class Pol, int D, int C>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const typename Pol::In::T* __restrict__ q, const typename Pol::In::T* __restrict__ k,
-    int64_t q_stride, int64_t k_stride, const float* __restrict__ g, const float* __restrict__ beta,
-    float scale, int use_l2, float l2_eps, int h_qk, int h_v,
+    int64_t q_stride, int64_t k_stride, GateSrc gates, float scale, int use_l2, float l2_eps, int h_qk, int h_v,
     const int32_t* __restrict__ cu, int n_seq, int64_t t_total, ChunkWs ws, int64_t n_slots) {
   using Elem = typename Pol::Elem;
   using W = WsLayout<Pol, D, C>;
@@ -358,11 +357,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
           qr[it] = Pol::load8(q + tok * q_stride + (int64_t)fq_ * D + c8);                             \
         }                                                                                              \
       }                                                                                                \
-      if (wave == 0) {                                                                                 \
-        const int64_t tg = (n_t0 + (lane < n_len ? lane : n_len - 1)) * h_v + (int64_t)fq_ * grp;      \
-        gn = g[tg];                                                                                    \
-        bn = beta[tg];                                                                                 \
-      }                                                                                                \
+      if (wave == 0)                                                                                   \
+        load_gate(gates, n_t0 + (lane < n_len ? lane : n_len - 1), fq_ * grp, h_v, gn, bn);            \
     }                                                                                                  \
   } while (0)
   GDN_PREP_FETCH(u);
@@ -453,11 +449,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
       const int64_t unit = cslot * h_v + h;
       // g, beta of the following v-head of the group, loaded now for later
       float g_next = 0.f, b_next = 0.f;
-      if (wave == 0 && vh + 1 < grp) {
-        const int64_t tg = (t0 + (lane < len ? lane : len - 1)) * h_v + h + 1;
-        g_next = g[tg];
-        b_next = beta[tg];
-      }
+      if (wave == 0 && vh + 1 < grp) load_gate(gates, t0 + (lane < len ? lane : len - 1), h + 1, h_v, g_next, b_next);
       if (lane >= len) gv = bv = 0.f;
 
       // 4. decay: inclusive prefix sum of g over the chunk (padded tokens add 0)
@@ -1052,7 +1044,7 @@ static hipError_t run_chunk(const ChunkArgs& a) {
     const int64_t resident = static_cast<int64_t>(per_cu) * device_cu_count();
     const int64_t grid = units < resident ? units : resident;
     hipLaunchKernelGGL((k_chunk_prep<Pol, D, C>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, q, k,
-                       a.q_stride, a.k_stride, a.g, a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu,
+                       a.q_stride, a.k_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu,
                        a.n_seq, a.t_total, ws, slots);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

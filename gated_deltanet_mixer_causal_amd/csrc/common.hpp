@@ -115,6 +115,52 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ---- per-(token, v-head) gates ---------------------------------------------
+
+// Where the log-decay g and the write strength beta of the gated delta rule
+// come from: fp32 tensors g, beta [rows][h_v] (a == nullptr), or the raw
+// outputs a, b of the gate projections (row stride ab_stride elements, bf16
+// or fp32) with per-v-head a_log and an optional dt_bias, from which
+//     g = -exp(a_log[h]) * softplus(a + dt_bias[h]),   beta = sigmoid(b)
+// (the B/A gate projections of the GDN mixer: Flare core-design, fused
+// projection weights paragraph).  Plain data, passed to kernels by value.
+struct GateSrc {
+  const float* g;
+  const float* beta;
+  const void* a;
+  const void* b;
+  int64_t ab_stride;
+  int ab_bf16;
+  const float* a_log;
+  const float* dt_bias;
+};
+
+// g and beta of token row t, v-head h.  softplus(x) is evaluated as
+// max(x, 0) + log1p(exp(-|x|)) and sigmoid(x) through exp(-|x|), so no
+// exponential overflows for any finite input.
+__device__ __forceinline__ void load_gate(const GateSrc& s, int64_t t, int h, int h_v, float& g, float& beta) {
+  if (s.a == nullptr) {
+    const int64_t i = t * h_v + h;
+    g = s.g[i];
+    beta = s.beta[i];
+    return;
+  }
+  const int64_t i = t * s.ab_stride + h;
+  float av, bv;
+  if (s.ab_bf16) {
+    av = bf16_bits_to_f32(static_cast<const uint16_t*>(s.a)[i]);
+    bv = bf16_bits_to_f32(static_cast<const uint16_t*>(s.b)[i]);
+  } else {
+    av = static_cast<const float*>(s.a)[i];
+    bv = static_cast<const float*>(s.b)[i];
+  }
+  const float x = av + (s.dt_bias ? s.dt_bias[h] : 0.f);
+  const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+  g = -expf(s.a_log[h]) * sp;
+  const float e = expf(-fabsf(bv));
+  beta = bv >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+
 // Sequence of a token-block slot.  Block j of sequence s (blocks of `blk`
 // tokens restarting at each sequence start) is given slot
 //     floor(cu[s] / blk) + s + j,

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/gdn.h"
+#include "common.hpp"
 
 namespace gdn {
 
@@ -14,7 +15,7 @@ struct ChunkArgs {
   const void *q, *k, *v;
   int64_t q_stride, k_stride, v_stride;
   gdn_dtype dt;
-  const float *g, *beta;
+  GateSrc gate;   // g and beta, or the raw gate projections
   float scale;
   int use_l2;
   float l2_eps;
@@ -37,7 +38,7 @@ struct StepArgs {
   const void *q, *k, *v;
   int64_t q_stride, k_stride, v_stride;
   gdn_dtype dt;
-  const float *g, *beta;
+  GateSrc gate;   // g and beta, or the raw gate projections
   float scale;
   int use_l2;
   float l2_eps;

@@ -51,8 +51,8 @@ __device__ __forceinline__ void load4<F32>(const float* p, float* out) {
 template <class E, class EO, int D, int NT>
 __global__ __launch_bounds__(NT) void k_recurrent_step(
     const typename E::T* __restrict__ q, const typename E::T* __restrict__ k, const typename E::T* __restrict__ v,
-    int64_t q_stride, int64_t k_stride, int64_t v_stride, const float* __restrict__ g,
-    const float* __restrict__ beta, float scale, int use_l2, float l2_eps, int h_qk, int h_v,
+    int64_t q_stride, int64_t k_stride, int64_t v_stride, GateSrc gates, float scale, int use_l2,
+    float l2_eps, int h_qk, int h_v,
     float* __restrict__ state, const int32_t* __restrict__ slots, typename EO::T* __restrict__ o,
     const typename E::T* __restrict__ z, const float* __restrict__ norm_w, float norm_eps) {
   constexpr int TPR = D / 8;                 // lanes per state row
@@ -88,8 +88,8 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
   load4<E>(k + r * k_stride + hq * D + cb, kk + 4);
   load4<E>(q + r * q_stride + hq * D + ca, qq);
   load4<E>(q + r * q_stride + hq * D + cb, qq + 4);
-  const float gv = g[static_cast<int64_t>(r) * h_v + h];
-  const float bt = beta[static_cast<int64_t>(r) * h_v + h];
+  float gv, bt;
+  load_gate(gates, r, h, h_v, gv, bt);
   const int64_t obase = (static_cast<int64_t>(r) * h_v + h) * D;
   // gate of the fused norm, loaded with everything else (thread tid owns row tid)
   typename E::T zraw = 0;
@@ -177,11 +177,11 @@ static hipError_t run_step(const StepArgs& a) {
   const T* z = static_cast<const T*>(a.z);
   if (a.d == 128)
     hipLaunchKernelGGL((k_recurrent_step<E, EO, 128, 256>), dim3(blocks), dim3(256), 0, st, q, k, v, a.q_stride,
-                       a.k_stride, a.v_stride, a.g, a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.state,
+                       a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.state,
                        a.slots, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
   else
     hipLaunchKernelGGL((k_recurrent_step<E, EO, 16, 64>), dim3(blocks), dim3(64), 0, st, q, k, v, a.q_stride,
-                       a.k_stride, a.v_stride, a.g, a.beta, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.state,
+                       a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.state,
                        a.slots, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
   return hipGetLastError();
 }

@@ -97,6 +97,54 @@ def gdn_recurrent_step(q, k, v, g, beta, state, o, *, scale=1.0, use_qk_l2norm=T
     return o
 
 
+def _gate_rows(a: torch.Tensor, b: torch.Tensor) -> int:
+    """Common row stride of the [rows, Hv] gate projection views a and b."""
+    if a.dim() != 2 or b.dim() != 2 or a.shape != b.shape:
+        raise ValueError(f"a and b must be [rows, Hv] views of one shape (got {tuple(a.shape)}, {tuple(b.shape)})")
+    if a.stride(1) != 1 or b.stride(1) != 1 or a.stride(0) != b.stride(0) or a.dtype != b.dtype:
+        raise ValueError("a and b need unit head stride, one row stride and one dtype")
+    return a.stride(0)
+
+
+def gdn_chunk_fwd_gated(q, k, v, a, b, a_log, o, *, chunk, dt_bias=None, scale=1.0, use_qk_l2norm=True,
+                        l2_eps=1e-6, cu_seqlens=None, initial_state=None, final_state=None, z=None,
+                        norm_w=None, norm_eps=1e-6, workspace=None, stream=None):
+    """gdn_chunk_fwd with the gates formed in the kernel from the raw gate projections:
+    g = -exp(a_log) * softplus(a + dt_bias), beta = sigmoid(b).  a, b [T, Hv] (bf16 or
+    fp32, one row stride); a_log, dt_bias [Hv] fp32 (dt_bias None = 0)."""
+    t_total, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n_seq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
+    if workspace is None:
+        nbytes = gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_total, q.dtype, z is not None)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.load().gdn_chunk_fwd_gated(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(a), _ptr(b), _gate_rows(a, b), _dt(a), _ptr(a_log), _ptr(dt_bias),
+        float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, chunk, _ptr(cu_seqlens), n_seq, t_total,
+        _ptr(initial_state), _ptr(final_state), _ptr(o), _dt(o),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(workspace), workspace.numel(), _stream(stream))
+    L.check("gdn_chunk_fwd_gated", st)
+    return o
+
+
+def gdn_recurrent_step_gated(q, k, v, a, b, a_log, state, o, *, dt_bias=None, scale=1.0, use_qk_l2norm=True,
+                             l2_eps=1e-6, state_slots=None, z=None, norm_w=None, norm_eps=1e-6, stream=None):
+    """gdn_recurrent_step with the gates formed in the kernel from a, b [N, Hv] and
+    a_log, dt_bias [Hv] (as gdn_chunk_fwd_gated)."""
+    n_req, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    st = L.load().gdn_recurrent_step_gated(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(a), _ptr(b), _gate_rows(a, b), _dt(a), _ptr(a_log), _ptr(dt_bias),
+        float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, n_req, _ptr(state), state.shape[0], _ptr(state_slots), _ptr(o), _dt(o),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _stream(stream))
+    L.check("gdn_recurrent_step_gated", st)
+    return o
+
+
 def gdn_gated_rmsnorm(x, z, w, y, *, eps=1e-6, stream=None):
     """y = x / sqrt(mean(x^2) + eps) * w * SiLU(z) over the last dim (16 or 128)."""
     d = x.shape[-1]

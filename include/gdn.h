@@ -197,6 +197,54 @@ gdn_status gdn_recurrent_step(const void* q, const void* k, const void* v,
                               const void* z, const float* norm_w, float norm_eps, void* stream);
 
 /*
+ * gdn_chunk_fwd_gated, gdn_recurrent_step_gated -- gdn_chunk_fwd and
+ * gdn_recurrent_step with the gate preparation fused into their prologues.
+ * (The GDN mixer's B/A gate projections: Flare core-design, the paragraph on
+ *  fused projection weights.  The pages give no formula for the gates; the
+ *  reading used here is the one that yields a log-decay g < 0 and a write
+ *  strength beta in (0, 1).)
+ *
+ * Instead of fp32 g and beta, each call reads the raw gate projections and
+ * forms, per token row t and v-head h, in fp32:
+ *     g[t,h]    = -exp(a_log[h]) * softplus(a[t,h] + dt_bias[h])
+ *     beta[t,h] = sigmoid(b[t,h])
+ * No g or beta tensor is written or needed.  Every other argument, the
+ * workspace (gdn_chunk_fwd_workspace_size) and every status are as for the
+ * unfused entry point.
+ *
+ *   a, b        rows of the gate projections: element (t, h) at a[t * ab_stride + h]
+ *               (b likewise), [t_total or n_req rows] of ab_dt; only element
+ *               alignment is required, so a and b may be the two halves of one
+ *               packed [rows, 2 h_v] tensor
+ *   ab_stride   row stride of a and b in elements; 0 = h_v; must be >= h_v
+ *   ab_dt       GDN_BF16 or GDN_F32
+ *   a_log       [h_v] fp32 (4-byte aligned), required
+ *   dt_bias     [h_v] fp32 (4-byte aligned), or NULL for a zero bias
+ * With t_total == 0 (chunk) a and b may be NULL; a_log is always required.
+ */
+gdn_status gdn_chunk_fwd_gated(const void* q, const void* k, const void* v,
+                               int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                               const void* a, const void* b, int64_t ab_stride, gdn_dtype ab_dt,
+                               const float* a_log, const float* dt_bias, float scale,
+                               int32_t use_qk_l2norm, float l2_eps,
+                               int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t chunk,
+                               const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                               const float* initial_state, float* final_state,
+                               void* o, gdn_dtype o_dt,
+                               const void* z, const float* norm_w, float norm_eps,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+gdn_status gdn_recurrent_step_gated(const void* q, const void* k, const void* v,
+                                    int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                                    const void* a, const void* b, int64_t ab_stride, gdn_dtype ab_dt,
+                                    const float* a_log, const float* dt_bias, float scale,
+                                    int32_t use_qk_l2norm, float l2_eps,
+                                    int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t n_req,
+                                    float* state, int32_t n_slots, const int32_t* state_slots,
+                                    void* o, gdn_dtype o_dt,
+                                    const void* z, const float* norm_w, float norm_eps, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * w * SiLU(z), per row of d.
  * (The gated RMSNorm of the GDN layers: haskell-infer-demo README,
  *  "Highlights", hybrid-architecture bullet, and "Architecture", gdn_norm.cu;

@@ -161,3 +161,51 @@ def test_norm_validation(lib):
     assert norm(lib, y=_addr(0) + 16) == L.GDN_ERR_ALIAS      # partial overlap with x
     assert norm(lib, y=_addr(1)) == L.GDN_ERR_ALIAS           # y over z
     assert norm(lib, w=_addr(2) + 4) == L.GDN_ERR_ALIGN
+
+
+def chunk_gated(lib, **kw):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dt=L.GDN_BF16, ga=_addr(3), gb=_addr(4), abs=0,
+             abdt=L.GDN_BF16, alog=_addr(10), bias=None, hq=2, hv=4, c=64, cu=_addr(5), n=1, t=100,
+             fin=_addr(6), o=_addr(7), ws=_addr(8), wsb=1 << 26)
+    a.update(kw)
+    return lib.gdn_chunk_fwd_gated(a["q"], a["k"], a["v"], 0, 0, 0, a["dt"], a["ga"], a["gb"], a["abs"], a["abdt"],
+                                   a["alog"], a["bias"], 1.0, 1, 1e-6, a["hq"], a["hv"], 128, 128, a["c"], a["cu"],
+                                   a["n"], a["t"], None, a["fin"], a["o"], L.GDN_F32, None, None, 1e-6, a["ws"],
+                                   a["wsb"], None)
+
+
+def test_chunk_gated_validation(lib):
+    assert chunk_gated(lib, n=0) == L.GDN_OK
+    assert chunk_gated(lib, ga=None) == L.GDN_ERR_NULL           # a missing
+    assert chunk_gated(lib, gb=None) == L.GDN_ERR_NULL           # b missing
+    assert chunk_gated(lib, alog=None) == L.GDN_ERR_NULL         # a_log is always required
+    assert chunk_gated(lib, abdt=7) == L.GDN_ERR_UNSUPPORTED
+    assert chunk_gated(lib, abs=3) == L.GDN_ERR_INVALID          # row stride below h_v
+    assert chunk_gated(lib, ga=_addr(3) + 1) == L.GDN_ERR_ALIGN  # bf16 needs 2-byte alignment
+    assert chunk_gated(lib, abdt=L.GDN_F32, gb=_addr(4) + 2) == L.GDN_ERR_ALIGN
+    assert chunk_gated(lib, alog=_addr(10) + 2) == L.GDN_ERR_ALIGN
+    assert chunk_gated(lib, bias=_addr(11) + 1) == L.GDN_ERR_ALIGN
+    assert chunk_gated(lib, o=_addr(3) + 64) == L.GDN_ERR_ALIAS  # o overlaps a
+    assert chunk_gated(lib, ws=_addr(10) - 64) == L.GDN_ERR_ALIAS   # workspace covers a_log
+    assert chunk_gated(lib, fin=_addr(11), bias=_addr(11) + 16) == L.GDN_ERR_ALIAS  # state over dt_bias
+    # a packed [t, 2 h_v] b|a tensor: a starts h_v bf16 elements (8 bytes) into the row
+    assert chunk_gated(lib, ga=_addr(3) + 8, gb=_addr(3), abs=8, o=None) == L.GDN_ERR_NULL   # gets past gate checks
+
+
+def step_gated(lib, **kw):
+    a = dict(ga=_addr(3), gb=_addr(4), abs=0, abdt=L.GDN_F32, alog=_addr(10), bias=None, n=3, st=_addr(5),
+             o=_addr(6))
+    a.update(kw)
+    return lib.gdn_recurrent_step_gated(_addr(0), _addr(1), _addr(2), 0, 0, 0, L.GDN_BF16, a["ga"], a["gb"], a["abs"],
+                                        a["abdt"], a["alog"], a["bias"], 1.0, 1, 1e-6, 2, 4, 128, 128, a["n"],
+                                        a["st"], 3, None, a["o"], L.GDN_F32, None, None, 1e-6, None)
+
+
+def test_recurrent_gated_validation(lib):
+    assert step_gated(lib, n=0) == L.GDN_OK
+    assert step_gated(lib, ga=None) == L.GDN_ERR_NULL
+    assert step_gated(lib, alog=None) == L.GDN_ERR_NULL
+    assert step_gated(lib, abs=2) == L.GDN_ERR_INVALID
+    assert step_gated(lib, gb=_addr(4) + 2) == L.GDN_ERR_ALIGN
+    assert step_gated(lib, st=_addr(3) + 16) == L.GDN_ERR_ALIAS   # state overlaps a
+    assert step_gated(lib, o=_addr(10) - 16) == L.GDN_ERR_ALIAS   # o overlaps a_log
