@@ -12,6 +12,11 @@ one token each -- gdn_conv1d_fwd in decode mode then gdn_recurrent_step with
 the fused norm -- on per-request fp32 states of 32 x 128 x 128; reported as
 state GB/s (2 x state bytes per step) and steps/s.
 
+Fused gates (reported beside them): the chunk and decode calls again through
+gdn_chunk_fwd_gated / gdn_recurrent_step_gated, which form g and beta in their
+prologues from bf16 raw gate projections (a packed b|a tensor) and per-head
+a_log, as a model's B/A projections deliver them.
+
 Both legs rotate over `--sets` independent copies of their buffers (as the
 GDN layers of a model would), so the working set exceeds the 256 MB Infinity
 Cache and the numbers are HBM-cold.  Inputs are resident in HBM before the
@@ -46,10 +51,10 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (289_555_661, {"chunk.hip": "38dc2e888efe1c80", "common.hpp": "9789884ded6edf16",
-                                    "launch.hpp": "87391e0d859dd5e0"}),
-    "gdn_recurrent_step": (271_171_379, {"recurrent.hip": "c228b4968470e50e", "common.hpp": "9789884ded6edf16",
-                                         "launch.hpp": "87391e0d859dd5e0"}),
+    "gdn_chunk_fwd": (289_244_690, {"chunk.hip": "7209526d618fbd39", "common.hpp": "f5db633bc62a5de3",
+                                    "launch.hpp": "206799c280670c13"}),
+    "gdn_recurrent_step": (270_943_882, {"recurrent.hip": "c93c24b454d423ec", "common.hpp": "f5db633bc62a5de3",
+                                         "launch.hpp": "206799c280670c13"}),
 }
 
 
@@ -69,8 +74,8 @@ def measured_traffic(entry):
 # traffic above.
 MEASURED_MFMA = {
     "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
-                      {"chunk.hip": "38dc2e888efe1c80", "common.hpp": "9789884ded6edf16",
-                       "launch.hpp": "87391e0d859dd5e0"}),
+                      {"chunk.hip": "7209526d618fbd39", "common.hpp": "f5db633bc62a5de3",
+                       "launch.hpp": "206799c280670c13"}),
 }
 
 
@@ -152,6 +157,9 @@ def prefill_leg(args, torch, np, ops, I):
                                                 torch.bfloat16, True)
     sets = []
     x0 = up(d["x"], torch.bfloat16)
+    gt = I.raw_gate_inputs(11, T, lay.h_v, dtype="bf16")
+    ba0 = up(np.concatenate([gt["b"], gt["a"]], axis=1), torch.bfloat16)
+    a_log = up(gt["a_log"])
     for _ in range(args.sets):
         s = dict(x=x0.clone(), w=up(d["conv_w"], torch.bfloat16), tail=up(d["tail"], torch.bfloat16),
                  cu=torch.from_numpy(d["cu_seqlens"]).to(dev), g=up(d["g"]), beta=up(d["beta"]),
@@ -162,8 +170,10 @@ def prefill_leg(args, torch, np, ops, I):
                  o=torch.empty((T, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev),
                  ws=torch.empty(ws_bytes, dtype=torch.uint8, device=dev))
         s["q"], s["k"], s["v"] = ops.qkv_views(s["y_conv"], lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+        s["ba"] = ba0.clone()
+        s["a"], s["b"] = s["ba"][:, lay.h_v:], s["ba"][:, :lay.h_v]
         sets.append(s)
-    del x0
+    del x0, ba0
 
     def step(i):
         s = sets[i % len(sets)]
@@ -177,10 +187,17 @@ def prefill_leg(args, torch, np, ops, I):
         ops.gdn_chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["o"], chunk=lay.chunk, cu_seqlens=s["cu"],
                           final_state=s["state"], workspace=s["ws"])
 
+    def chunk_gated(i):
+        s = sets[i % len(sets)]
+        ops.gdn_chunk_fwd_gated(s["q"], s["k"], s["v"], s["a"], s["b"], a_log, s["o"], chunk=lay.chunk,
+                                cu_seqlens=s["cu"], final_state=s["state"], workspace=s["ws"])
+
     ms, wall = timed(step, args.steps, args.warmup, torch)
     ms_chunk, _ = timed(chunk_only, args.steps, args.warmup, torch)
     stats = call_stats(chunk_only, max(args.steps, 50), args.warmup + args.steps, torch)
-    return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, chunk_stats=stats, layout=lay)
+    ms_chunk_gated, _ = timed(chunk_gated, args.steps, args.warmup, torch)
+    return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, chunk_stats=stats, layout=lay,
+                ms_chunk_gated=ms_chunk_gated)
 
 
 def decode_leg(args, torch, np, ops, I):
@@ -203,6 +220,11 @@ def decode_leg(args, torch, np, ops, I):
     del state0
     steps_in = [dict(x=up(d["x"][t], torch.bfloat16), g=up(d["g"][t]), beta=up(d["beta"][t]),
                      z=up(d["z"][t], torch.bfloat16)) for t in range(d["x"].shape[0])]
+    gate_in = []
+    for t in range(d["x"].shape[0]):
+        gt = I.raw_gate_inputs(20 + t, n_req, lay.h_v, dtype="bf16")
+        ba = up(np.concatenate([gt["b"], gt["a"]], axis=1), torch.bfloat16)
+        gate_in.append(dict(a=ba[:, lay.h_v:], b=ba[:, :lay.h_v], a_log=up(gt["a_log"])))
 
     def step(i):
         s = sets[i % len(sets)]
@@ -216,14 +238,20 @@ def decode_leg(args, torch, np, ops, I):
         inp = steps_in[i % len(steps_in)]
         ops.gdn_recurrent_step(s["q"], s["k"], s["v"], inp["g"], inp["beta"], s["state"], s["o"])
 
+    def rec_gated(i):
+        s = sets[i % len(sets)]
+        gi = gate_in[i % len(gate_in)]
+        ops.gdn_recurrent_step_gated(s["q"], s["k"], s["v"], gi["a"], gi["b"], gi["a_log"], s["state"], s["o"])
+
     ms, wall = timed(step, args.steps, args.warmup, torch)
     ms_rec, _ = timed(rec_only, args.steps, args.warmup, torch)
     rec_stats = call_stats(rec_only, max(args.steps, 50), args.warmup + args.steps, torch)
+    ms_rec_gated, _ = timed(rec_gated, args.steps, args.warmup, torch)
     state_bytes = n_req * lay.h_v * lay.d_v * lay.d_k * 4
     # per request: q, k, v, z (bf16), g, beta (fp32), o (bf16)
     small = n_req * (2 * lay.h_qk * lay.d_k * 2 + lay.h_v * lay.d_v * 2 + 2 * lay.h_v * 4 + lay.h_v * lay.d_v * 2)
     return dict(ms=ms, wall=wall, ms_rec=ms_rec, rec_stats=rec_stats, n_req=n_req, state_bytes=state_bytes,
-                small=small)
+                small=small, ms_rec_gated=ms_rec_gated)
 
 
 def cpu_baseline(np, I, R):
@@ -323,6 +351,15 @@ def main():
                          "traffic": measured_traffic("gdn_recurrent_step"), "avg_launch_ms": round(dc["ms_rec"], 4),
                          "algorithmic_bytes_per_launch": alg, "per_call": dc["rec_stats"]},
         }
+    out["fused_gates"] = {
+        "what": "gdn_chunk_fwd_gated / gdn_recurrent_step_gated: g = -exp(a_log) softplus(a), beta = sigmoid(b) "
+                "formed in the kernels from bf16 raw a|b projections (no g/beta tensors)",
+        "chunk_fwd_ms": round(pf["ms_chunk_gated"], 4),
+        "chunk_fwd_vs_plain": round(pf["ms_chunk_gated"] / pf["ms_chunk"], 4),
+    }
+    if not args.no_decode:
+        out["fused_gates"]["recurrent_step_ms"] = round(dc["ms_rec_gated"], 4)
+        out["fused_gates"]["recurrent_step_vs_plain"] = round(dc["ms_rec_gated"] / dc["ms_rec"], 4)
     if not args.no_cpu_baseline:
         from oracle import gdn_ref as R
         out["cpu_baseline"] = cpu_baseline(np, I, R)
