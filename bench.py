@@ -51,7 +51,7 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (289_244_690, {"chunk.hip": "7209526d618fbd39", "common.hpp": "f5db633bc62a5de3",
+    "gdn_chunk_fwd": (289_247_337, {"chunk.hip": "a0aa61ff5966bb39", "common.hpp": "f5db633bc62a5de3",
                                     "launch.hpp": "206799c280670c13"}),
     "gdn_recurrent_step": (270_943_882, {"recurrent.hip": "c93c24b454d423ec", "common.hpp": "f5db633bc62a5de3",
                                          "launch.hpp": "206799c280670c13"}),
@@ -74,7 +74,7 @@ def measured_traffic(entry):
 # traffic above.
 MEASURED_MFMA = {
     "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
-                      {"chunk.hip": "7209526d618fbd39", "common.hpp": "f5db633bc62a5de3",
+                      {"chunk.hip": "a0aa61ff5966bb39", "common.hpp": "f5db633bc62a5de3",
                        "launch.hpp": "206799c280670c13"}),
 }
 
