@@ -44,6 +44,12 @@ the design notes of the repository):
     plainest reading that fits the log-decay g < 0 of the rule above and a
     write strength beta in (0, 1).  dt_bias is an optional per-head bias
     (absent = 0).
+  * Speculative verification: a round of W draft tokens starts from the live
+    state and records the state after each token in its own checkpoint column,
+    and the 3-token conv history after each token (Flare core-design,
+    speculative target state: eight recurrent checkpoint columns per request, a
+    round writes the columns of its verification inputs, and a snapshot copies a
+    column with its three-token convolution window).
 
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (closed forms, invariants, brute force, an
@@ -224,6 +230,45 @@ def gated_delta_rule(q, k, v, g, beta, *, scale=1.0, initial_state=None,
             o[t] = scale * np.matmul(S, qt[:, :, None])[:, :, 0]
         final[s] = S
     return o, final
+
+
+# ---------------------------------------------------------------------------
+# Speculative verification: per-token state checkpoints and conv windows
+# ---------------------------------------------------------------------------
+
+def verify_checkpoints(q, k, v, g, beta, *, initial_state, scale=1.0, use_qk_l2norm=True,
+                       l2_eps=1e-6, qk_of_v=None):
+    """The W verification tokens of one request, one at a time from its live
+    state (Flare core-design, speculative target state: one recurrent
+    checkpoint column per verification input).
+
+    q, k [W, Hqk, dk]; v [W, Hv, dv]; g, beta [W, Hv]; initial_state
+    [Hv, dv, dk].  Column t is the state after tokens 0..t.  Each token is one
+    call of gated_delta_rule starting from the previous column.  Returns
+    (o [W, Hv, dv], columns [W, Hv, dv, dk]).
+    """
+    w = np.asarray(q).shape[0]
+    hv, dv = np.asarray(v).shape[1], np.asarray(v).shape[2]
+    dk = np.asarray(q).shape[2]
+    o = np.zeros((w, hv, dv))
+    cols = np.zeros((w, hv, dv, dk))
+    S = np.asarray(initial_state, np.float64)[None]
+    for t in range(w):
+        ot, S = gated_delta_rule(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], beta[t:t + 1],
+                                 scale=scale, initial_state=S, use_qk_l2norm=use_qk_l2norm,
+                                 l2_eps=l2_eps, qk_of_v=qk_of_v)
+        o[t] = ot[0]
+        cols[t] = S[0]
+    return o, cols
+
+
+def conv_windows(tail, x):
+    """The 3-token conv history after each of the W tokens x [W, Ch] of one
+    request whose history before them is tail [3, Ch] (Flare core-design,
+    snapshot of the three-token GDN convolution window of a column): window t
+    is rows t+1 .. t+3 of [tail; x].  Returns [W, 3, Ch]."""
+    full = np.concatenate([np.asarray(tail, np.float64), np.asarray(x, np.float64)], axis=0)
+    return np.stack([full[t + 1:t + 4] for t in range(np.asarray(x).shape[0])])
 
 
 # ---------------------------------------------------------------------------

@@ -494,3 +494,59 @@ def test_gates_match_log_decay_recipe():
     A = rng.uniform(0, math.log(16.0), 2)
     g, _ = R.gates_from_projections(n, np.zeros_like(n), A)
     np.testing.assert_allclose(np.exp(g), (1.0 + np.exp(n)) ** (-np.exp(A)[None, :]), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Speculative verification: checkpoint columns and conv windows
+# ---------------------------------------------------------------------------
+
+def test_verify_checkpoints_match_prefix_runs():
+    # column t equals the final state of the pinned rule over tokens 0..t, and
+    # the outputs equal those of one run over all W tokens
+    rng = np.random.default_rng(11)
+    w, hqk, hv, d = 5, 1, 2, 8
+    q = rng.standard_normal((w, hqk, d))
+    k = rng.standard_normal((w, hqk, d))
+    v = rng.standard_normal((w, hv, d))
+    g = -rng.uniform(0.05, 0.5, (w, hv))
+    beta = rng.uniform(0.1, 0.9, (w, hv))
+    s0 = 0.1 * rng.standard_normal((hv, d, d))
+    o, cols = R.verify_checkpoints(q, k, v, g, beta, initial_state=s0)
+    o_all, _ = R.gated_delta_rule(q, k, v, g, beta, initial_state=s0[None])
+    np.testing.assert_allclose(o, o_all, rtol=0, atol=1e-13)
+    for t in range(w):
+        _, fin = R.gated_delta_rule(q[:t + 1], k[:t + 1], v[:t + 1], g[:t + 1], beta[:t + 1],
+                                    initial_state=s0[None])
+        np.testing.assert_allclose(cols[t], fin[0], rtol=0, atol=1e-13)
+
+
+def test_verify_checkpoint_exact_write():
+    # a = 1, beta = 1, unit-norm key: every column retrieves its own value, S_t k_t = v_t
+    d, hv = 8, 1
+    eye = np.eye(d)
+    q = eye[[0, 1, 2]][:, None, :]
+    k = eye[[3, 4, 3]][:, None, :]
+    v = np.arange(3 * d, dtype=np.float64).reshape(3, hv, d)
+    g = np.zeros((3, hv))
+    beta = np.ones((3, hv))
+    _, cols = R.verify_checkpoints(q, k, v, g, beta, initial_state=np.zeros((hv, d, d)), use_qk_l2norm=False)
+    for t in range(3):
+        np.testing.assert_allclose(cols[t][0] @ k[t, 0], v[t, 0], rtol=0, atol=1e-12)
+    # the third token overwrote key 3: column 2 no longer returns token 0's value for it
+    np.testing.assert_allclose(cols[2][0] @ eye[4], v[1, 0], rtol=0, atol=1e-12)
+
+
+def test_conv_windows_equal_conv_tail():
+    # the last window is the history the conv reports after all W tokens; every
+    # window is made of raw inputs in token order
+    rng = np.random.default_rng(12)
+    ch, w = 16, 4
+    tail = rng.standard_normal((1, 3, ch))
+    x = rng.standard_normal((w, ch))
+    win = R.conv_windows(tail[0], x)
+    _, new_tail = R.causal_conv1d_silu(x, rng.standard_normal((ch, 4)), tail, [0, w], round_to_bf16=False)
+    np.testing.assert_array_equal(win[-1], new_tail[0])
+    np.testing.assert_array_equal(win[0], np.concatenate([tail[0][1:], x[:1]]))
+    for t in range(1, w):
+        np.testing.assert_array_equal(win[t][:2], win[t - 1][1:])
+        np.testing.assert_array_equal(win[t][2], x[t])
