@@ -377,6 +377,99 @@ gdn_status gdn_recurrent_step_gated(const void* q, const void* k, const void* v,
                              h_v, d_k, d_v, n_req, state, n_slots, state_slots, o, o_dt, z, norm_w, norm_eps, stream);
 }
 
+gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                                int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                                int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                int32_t d_v, int32_t n_req, int32_t n_tok, const float* state, int32_t n_slots,
+                                const int32_t* state_slots, float* checkpoints, int32_t n_cols, void* o,
+                                gdn_dtype o_dt, const void* z, const float* norm_w, float norm_eps, void* stream) {
+  if (n_req < 0 || n_slots < 0) return GDN_ERR_INVALID;
+  if (n_req == 0) return GDN_OK;
+  if (n_tok < 1 || n_cols < n_tok) return GDN_ERR_INVALID;
+  const GateArgs ga = plain_gates(g, beta);
+  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, ga.rows_missing(), h_qk, h_v, d_k, d_v);
+  if (st != GDN_OK) return st;
+  const int64_t rows = static_cast<int64_t>(n_req) * n_tok;
+  Gates gt;
+  st = check_gates(ga, rows, h_v, gt);
+  if (st != GDN_OK) return st;
+  if (!state || !checkpoints || !o) return GDN_ERR_NULL;
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!dt_valid(o_dt)) return GDN_ERR_UNSUPPORTED;
+  if (!((d_k == 128 && d_v == 128) || (d_k == 16 && d_v == 16))) return GDN_ERR_UNSUPPORTED;
+  if (!state_slots && n_slots < n_req) return GDN_ERR_INVALID;
+  if (!all_aligned({state, checkpoints, o, z, norm_w, state_slots})) return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const uint64_t slot_bytes = static_cast<uint64_t>(h_v) * d_v * d_k * 4;
+  const Range rq{q, strided_bytes(rows, q_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rk{k, strided_bytes(rows, k_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rv{v, strided_bytes(rows, v_stride, static_cast<int64_t>(h_v) * d_v, eb)};
+  const Range rs{state, static_cast<uint64_t>(n_slots) * slot_bytes};
+  const Range rc{checkpoints, static_cast<uint64_t>(n_slots) * n_cols * slot_bytes};
+  const Range ro{o, static_cast<uint64_t>(rows) * h_v * d_v * dt_bytes(o_dt)};
+  const Range rz{z, z ? static_cast<uint64_t>(rows) * h_v * d_v * eb : 0};
+  const Range rw{norm_w, z ? static_cast<uint64_t>(d_v) * 4 : 0};
+  const Range rsl{state_slots, state_slots ? static_cast<uint64_t>(n_req) * 4 : 0};
+  if (!disjoint(ro, {rq, rk, rv, rs, rc, rz, rw, rsl}) || !disjoint_gates(ro, gt)) return GDN_ERR_ALIAS;
+  if (!disjoint(rc, {rq, rk, rv, rs, rz, rw, rsl}) || !disjoint_gates(rc, gt)) return GDN_ERR_ALIAS;
+
+  gdn::VerifyArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride;
+  a.dt = dt; a.gate = gt.src; a.scale = scale;
+  a.use_l2 = use_qk_l2norm != 0; a.l2_eps = l2_eps;
+  a.h_qk = h_qk; a.h_v = h_v; a.d = d_k; a.n_req = n_req; a.n_tok = n_tok;
+  a.state = state; a.slots = state_slots; a.ckpt = checkpoints; a.n_cols = n_cols;
+  a.o = o; a.o_dt = o_dt; a.z = z; a.norm_w = norm_w; a.norm_eps = norm_eps;
+  a.stream = stream;
+  return finish(gdn::launch_recurrent_verify(a));
+}
+
+gdn_status gdn_conv1d_verify(const void* x, gdn_dtype dt, const void* w, int32_t channels, int32_t n_req,
+                             int32_t n_tok, const void* conv_state, int32_t n_slots, const int32_t* state_slots,
+                             void* y, void* windows, int32_t n_cols, void* stream) {
+  if (n_req < 0 || channels <= 0 || n_slots < 0) return GDN_ERR_INVALID;
+  if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
+  if (channels % 8) return GDN_ERR_INVALID;
+  if (n_req == 0) return GDN_OK;
+  if (n_tok < 1 || n_cols < n_tok) return GDN_ERR_INVALID;
+  if (!x || !w || !conv_state || !y || !windows) return GDN_ERR_NULL;
+  if (!state_slots && n_slots < n_req) return GDN_ERR_INVALID;
+  if (!all_aligned({x, w, conv_state, y, windows, state_slots})) return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const uint64_t rows = static_cast<uint64_t>(n_req) * n_tok;
+  const Range rx{x, rows * channels * eb};
+  const Range ry{y, rows * channels * eb};
+  const Range rw{w, static_cast<uint64_t>(channels) * 4 * eb};
+  const Range rs{conv_state, static_cast<uint64_t>(n_slots) * 3 * channels * eb};
+  const Range rwin{windows, static_cast<uint64_t>(n_slots) * n_cols * 3 * channels * eb};
+  const Range rsl{state_slots, state_slots ? static_cast<uint64_t>(n_req) * 4 : 0};
+  if (!disjoint(ry, {rx, rw, rs, rwin, rsl}) || !disjoint(rwin, {rx, rw, rs, rsl})) return GDN_ERR_ALIAS;
+  return finish(gdn::launch_conv1d_verify(x, dt, w, channels, n_req, n_tok, conv_state, state_slots, y, windows,
+                                          n_cols, stream));
+}
+
+gdn_status gdn_state_rows_copy(void* dst, int64_t n_dst_rows, const int32_t* dst_rows, const void* src,
+                               int64_t n_src_rows, const int32_t* src_rows, int64_t row_bytes, int32_t n,
+                               void* stream) {
+  if (n < 0 || n_dst_rows < 0 || n_src_rows < 0 || row_bytes <= 0) return GDN_ERR_INVALID;
+  if (n == 0) return GDN_OK;
+  if (!dst || !dst_rows) return GDN_ERR_NULL;
+  if (src && !src_rows) return GDN_ERR_NULL;
+  if (row_bytes % 16) return GDN_ERR_ALIGN;
+  if (!all_aligned({dst, dst_rows, src, src_rows})) return GDN_ERR_ALIGN;
+  // one workgroup per 16 KiB of each entry's row: the grid must stay below 2^31
+  const int64_t chunks = (row_bytes / 16 + 1023) / 1024;
+  if (chunks > (int64_t(1) << 31) / n) return GDN_ERR_INVALID;
+  const Range rd{dst, static_cast<uint64_t>(n_dst_rows) * row_bytes};
+  const Range rsrc{src, src ? static_cast<uint64_t>(n_src_rows) * row_bytes : 0};
+  const Range rdi{dst_rows, static_cast<uint64_t>(n) * 4};
+  const Range rsi{src_rows, src ? static_cast<uint64_t>(n) * 4 : 0};
+  if (!disjoint(rd, {rdi, rsi})) return GDN_ERR_ALIAS;
+  if (src && src != dst && overlap(rd, rsrc)) return GDN_ERR_ALIAS;
+  return finish(gdn::launch_rows_copy(dst, n_dst_rows, dst_rows, src, n_src_rows, src_rows, row_bytes, n, stream));
+}
+
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w, float eps,
                              int64_t rows, int32_t d, void* y, gdn_dtype y_dt, void* stream) {
   if (rows < 0) return GDN_ERR_INVALID;

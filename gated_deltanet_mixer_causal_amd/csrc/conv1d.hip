@@ -141,6 +141,51 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_step(
   E::store8(hist + 2 * ld, cur);
 }
 
+// Speculative verification: n_tok tokens per request (rows s n_tok .. s n_tok +
+// n_tok - 1 of x and y) from the live history of the request's slot, which is
+// only read.  The history after token t (its last three raw inputs) is
+// written to column t of the window store, windows[slot][t][0..2][c], as the
+// three-token convolution window of that checkpoint column (Flare
+// core-design, speculative target state).  A negative slot is an inactive
+// lane: nothing is read or written.
+template <class E>
+__global__ __launch_bounds__(kConvThreads) void k_conv1d_verify(
+    const typename E::T* __restrict__ x, const typename E::T* __restrict__ w, int channels, int n_seq,
+    int n_tok, const typename E::T* __restrict__ state, const int32_t* __restrict__ slots,
+    typename E::T* __restrict__ y, typename E::T* __restrict__ windows, int n_cols) {
+  const int groups = channels / 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kConvThreads + threadIdx.x;
+  const int64_t s = gid / groups;
+  if (s >= n_seq) return;
+  const int c0 = static_cast<int>(gid % groups) * 8;
+  const int slot = slots ? slots[s] : static_cast<int>(s);
+  if (slot < 0) return;
+  const int64_t ld = channels;
+  float wt[4][8];
+  load_taps<E>(w, c0, wt);
+  const typename E::T* hist = state + static_cast<int64_t>(slot) * 3 * ld + c0;
+  float h0[8], h1[8], h2[8], cur[8], out[8];
+  E::load8(hist, h0);
+  E::load8(hist + ld, h1);
+  E::load8(hist + 2 * ld, h2);
+  for (int t = 0; t < n_tok; ++t) {
+    const int64_t row = s * n_tok + t;
+    E::load8(x + row * ld + c0, cur);
+    conv_out(wt, h0, h1, h2, cur, out);
+    E::store8(y + row * ld + c0, out);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      h0[i] = h1[i];
+      h1[i] = h2[i];
+      h2[i] = cur[i];
+    }
+    typename E::T* win = windows + (static_cast<int64_t>(slot) * n_cols + t) * 3 * ld + c0;
+    E::store8(win, h0);
+    E::store8(win + ld, h1);
+    E::store8(win + 2 * ld, h2);
+  }
+}
+
 template <class E>
 static hipError_t run_conv(const void* x, const void* w, int channels, const int32_t* cu, int n_seq,
                            int64_t t_total, void* state, const int32_t* slots, void* y, hipStream_t st) {
@@ -159,6 +204,26 @@ static hipError_t run_conv(const void* x, const void* w, int channels, const int
                        static_cast<T*>(y));
   }
   return hipGetLastError();
+}
+
+template <class E>
+static hipError_t run_conv_verify(const void* x, const void* w, int channels, int n_seq, int n_tok, const void* state,
+                                  const int32_t* slots, void* y, void* windows, int n_cols, hipStream_t st) {
+  using T = typename E::T;
+  const int64_t threads = static_cast<int64_t>(n_seq) * (channels / 8);
+  const unsigned blocks = static_cast<unsigned>((threads + kConvThreads - 1) / kConvThreads);
+  hipLaunchKernelGGL((k_conv1d_verify<E>), dim3(blocks), dim3(kConvThreads), 0, st, static_cast<const T*>(x),
+                     static_cast<const T*>(w), channels, n_seq, n_tok, static_cast<const T*>(state), slots,
+                     static_cast<T*>(y), static_cast<T*>(windows), n_cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv1d_verify(const void* x, gdn_dtype dt, const void* w, int channels, int n_seq, int n_tok,
+                                const void* state, const int32_t* slots, void* y, void* windows, int n_cols,
+                                void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == GDN_BF16) return run_conv_verify<BF16>(x, w, channels, n_seq, n_tok, state, slots, y, windows, n_cols, st);
+  return run_conv_verify<F32>(x, w, channels, n_seq, n_tok, state, slots, y, windows, n_cols, st);
 }
 
 hipError_t launch_conv1d(const void* x, gdn_dtype dt, const void* w, int channels, const int32_t* cu,

@@ -53,6 +53,28 @@ struct StepArgs {
   void* stream;
 };
 
+// Speculative verification of n_tok tokens per request (checkpoint columns).
+struct VerifyArgs {
+  const void *q, *k, *v;
+  int64_t q_stride, k_stride, v_stride;
+  gdn_dtype dt;
+  GateSrc gate;
+  float scale;
+  int use_l2;
+  float l2_eps;
+  int h_qk, h_v, d, n_req, n_tok;
+  const float* state;
+  const int32_t* slots;
+  float* ckpt;
+  int n_cols;
+  void* o;
+  gdn_dtype o_dt;
+  const void* z;
+  const float* norm_w;
+  float norm_eps;
+  void* stream;
+};
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
@@ -60,6 +82,12 @@ size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_s
                       int with_norm);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 hipError_t launch_recurrent_step(const StepArgs& a);
+hipError_t launch_recurrent_verify(const VerifyArgs& a);
+hipError_t launch_conv1d_verify(const void* x, gdn_dtype dt, const void* w, int channels, int n_seq, int n_tok,
+                                const void* state, const int32_t* slots, void* y, void* windows, int n_cols,
+                                void* stream);
+hipError_t launch_rows_copy(void* dst, int64_t n_dst, const int32_t* dst_rows, const void* src, int64_t n_src,
+                            const int32_t* src_rows, int64_t row_bytes, int n, void* stream);
 hipError_t launch_conv1d(const void* x, gdn_dtype dt, const void* w, int channels, const int32_t* cu,
                          int n_seq, int64_t t_total, void* state, const int32_t* slots, void* y,
                          void* stream);

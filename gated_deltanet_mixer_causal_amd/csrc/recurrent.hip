@@ -165,6 +165,164 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
   }
 }
 
+// Speculative verification: n_tok tokens per request (rows r n_tok + t of q, k,
+// v, the gates, z and o), starting from the live state of the request's slot,
+// which is only read.  The state after token t is written to checkpoint
+// column t, ckpt[slot][t] (Flare core-design, speculative target state: a
+// round writes the recurrent checkpoint columns of its verification inputs).
+// Per (request, v-head) the state is read once, kept in registers across the
+// tokens, and streamed out once per token.  A negative slot is an inactive
+// lane: nothing is read or written and its o rows stay untouched.
+template <class E, class EO, int D, int NT>
+__global__ __launch_bounds__(NT) void k_recurrent_verify(
+    const typename E::T* __restrict__ q, const typename E::T* __restrict__ k, const typename E::T* __restrict__ v,
+    int64_t q_stride, int64_t k_stride, int64_t v_stride, GateSrc gates, float scale, int use_l2,
+    float l2_eps, int h_qk, int h_v, int n_tok, const float* __restrict__ state, const int32_t* __restrict__ slots,
+    float* __restrict__ ckpt, int n_cols, typename EO::T* __restrict__ o, const typename E::T* __restrict__ z,
+    const float* __restrict__ norm_w, float norm_eps) {
+  constexpr int TPR = D / 8;                 // lanes per state row
+  constexpr int RPP = NT / TPR;              // rows per pass
+  constexpr int PASSES = (D + RPP - 1) / RPP;
+  static_assert(TPR <= 64 && NT % 64 == 0, "row lanes within a wave");
+  constexpr bool FULL = RPP * PASSES == D;
+
+  const int r = blockIdx.x / h_v, h = blockIdx.x % h_v;
+  const int slot = slots ? slots[r] : r;
+  if (slot < 0) return;
+  const int hq = h / (h_v / h_qk);
+  const int tid = threadIdx.x, l = tid % TPR, rg = tid / TPR;
+  const int ca = 4 * l, cb = D / 2 + 4 * l;
+  __shared__ float so[D];
+  __shared__ float sred[NT / 64];
+
+  const float* S = state + (static_cast<int64_t>(slot) * h_v + h) * D * D;
+  float4 sa[PASSES], sb[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = rg + p * RPP;
+    const int rr = (FULL || row < D) ? row : 0;
+    sa[p] = stream_load4(S + rr * D + ca);
+    sb[p] = stream_load4(S + rr * D + cb);
+  }
+
+  for (int t = 0; t < n_tok; ++t) {
+    const int64_t tr = static_cast<int64_t>(r) * n_tok + t;   // token row
+    typename E::T vraw[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = rg + p * RPP;
+      vraw[p] = v[tr * v_stride + h * D + ((FULL || row < D) ? row : 0)];
+    }
+    float kk[8], qq[8];
+    load4<E>(k + tr * k_stride + hq * D + ca, kk);
+    load4<E>(k + tr * k_stride + hq * D + cb, kk + 4);
+    load4<E>(q + tr * q_stride + hq * D + ca, qq);
+    load4<E>(q + tr * q_stride + hq * D + cb, qq + 4);
+    float gv, bt;
+    load_gate(gates, tr, h, h_v, gv, bt);
+    const int64_t obase = (tr * h_v + h) * D;
+    typename E::T zraw = 0;
+    if (z) zraw = z[obase + (tid < D ? tid : 0)];
+    float sk = 0.f, sq = 0.f, kq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
+    sk = group_sum<TPR>(sk);
+    sq = group_sum<TPR>(sq);
+    kq = group_sum<TPR>(kq);
+    const float rk = use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f;
+    const float rq = use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { kk[i] *= rk; qq[i] *= rq; }
+    kq *= rk * rq;
+    const float alpha = __expf(gv);
+
+    float* C = ckpt + ((static_cast<int64_t>(slot) * n_cols + t) * h_v + h) * D * D;
+    float orow[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = rg + p * RPP;
+      float dk = sa[p].x * kk[0] + sa[p].y * kk[1] + sa[p].z * kk[2] + sa[p].w * kk[3] +
+                 sb[p].x * kk[4] + sb[p].y * kk[5] + sb[p].z * kk[6] + sb[p].w * kk[7];
+      float dq = sa[p].x * qq[0] + sa[p].y * qq[1] + sa[p].z * qq[2] + sa[p].w * qq[3] +
+                 sb[p].x * qq[4] + sb[p].y * qq[5] + sb[p].z * qq[6] + sb[p].w * qq[7];
+      dk = group_sum<TPR>(dk);
+      dq = group_sum<TPR>(dq);
+      const float e = E::cvt(vraw[p]) - alpha * dk;
+      const float be = bt * e;
+      orow[p] = scale * (alpha * dq + be * kq);
+      float4 na, nb;
+      na.x = alpha * sa[p].x + be * kk[0]; na.y = alpha * sa[p].y + be * kk[1];
+      na.z = alpha * sa[p].z + be * kk[2]; na.w = alpha * sa[p].w + be * kk[3];
+      nb.x = alpha * sb[p].x + be * kk[4]; nb.y = alpha * sb[p].y + be * kk[5];
+      nb.z = alpha * sb[p].z + be * kk[6]; nb.w = alpha * sb[p].w + be * kk[7];
+      sa[p] = na;
+      sb[p] = nb;
+      if (FULL || row < D) {
+        stream_store4(C + row * D + ca, na);
+        stream_store4(C + row * D + cb, nb);
+      }
+    }
+
+    if (!z) {
+      if (l == 0) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+          const int row = rg + p * RPP;
+          if (FULL || row < D) EO::store(o, obase + row, orow[p]);
+        }
+      }
+      continue;
+    }
+    // fused gated RMSNorm over the head's d_v outputs of this token
+    if (l == 0) {
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int row = rg + p * RPP;
+        if (FULL || row < D) so[row] = orow[p];
+      }
+    }
+    __syncthreads();
+    const float ov = tid < D ? so[tid] : 0.f;
+    const float ss = group_sum<64>(ov * ov);
+    if ((tid & 63) == 0) sred[tid >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) tot += sred[w];
+    if (tid < D) {
+      const float rr = 1.0f / sqrtf(tot * (1.0f / D) + norm_eps);
+      EO::store(o, obase + tid, ov * rr * norm_w[tid] * silu(E::cvt(zraw)));
+    }
+    __syncthreads();   // so and sred are rewritten by the next token
+  }
+}
+
+template <class E, class EO>
+static hipError_t run_verify(const VerifyArgs& a) {
+  using T = typename E::T;
+  using TO = typename EO::T;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(a.n_req) * a.h_v);
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const T* z = static_cast<const T*>(a.z);
+  if (a.d == 128)
+    hipLaunchKernelGGL((k_recurrent_verify<E, EO, 128, 256>), dim3(blocks), dim3(256), 0, st, q, k, v, a.q_stride,
+                       a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.n_tok, a.state,
+                       a.slots, a.ckpt, a.n_cols, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
+  else
+    hipLaunchKernelGGL((k_recurrent_verify<E, EO, 16, 64>), dim3(blocks), dim3(64), 0, st, q, k, v, a.q_stride,
+                       a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.n_tok, a.state,
+                       a.slots, a.ckpt, a.n_cols, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_recurrent_verify(const VerifyArgs& a) {
+  if (a.dt == GDN_BF16) return a.o_dt == GDN_BF16 ? run_verify<BF16, BF16>(a) : run_verify<BF16, F32>(a);
+  return a.o_dt == GDN_BF16 ? run_verify<F32, BF16>(a) : run_verify<F32, F32>(a);
+}
+
 template <class E, class EO>
 static hipError_t run_step(const StepArgs& a) {
   using T = typename E::T;

@@ -145,6 +145,51 @@ def gdn_recurrent_step_gated(q, k, v, a, b, a_log, state, o, *, dt_bias=None, sc
     return o
 
 
+def gdn_recurrent_verify(q, k, v, g, beta, state, checkpoints, o, *, n_tok, scale=1.0, use_qk_l2norm=True,
+                         l2_eps=1e-6, state_slots=None, z=None, norm_w=None, norm_eps=1e-6, stream=None):
+    """Speculative verification of n_tok tokens per request.  q, k [N*W, Hqk, dk]; v [N*W, Hv, dv];
+    g, beta [N*W, Hv] (request r: rows r*W .. r*W+W-1); state [slots, Hv, dv, dk] fp32 (read
+    only); checkpoints [slots, cols, Hv, dv, dk] fp32 (column t = state after token t); o [N*W, Hv, dv]."""
+    rows, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    if rows % n_tok:
+        raise ValueError(f"{rows} token rows are not a multiple of n_tok={n_tok}")
+    st = L.load().gdn_recurrent_verify(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(g), _ptr(beta), float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, rows // n_tok, n_tok, _ptr(state), state.shape[0], _ptr(state_slots),
+        _ptr(checkpoints), checkpoints.shape[1], _ptr(o), _dt(o), _ptr(z), _ptr(norm_w), float(norm_eps),
+        _stream(stream))
+    L.check("gdn_recurrent_verify", st)
+    return o
+
+
+def gdn_conv1d_verify(x, w, conv_state, y, windows, *, n_tok, state_slots=None, stream=None):
+    """Conv + SiLU of n_tok tokens per request from the live histories conv_state [slots, 3, Ch]
+    (read only); windows [slots, cols, 3, Ch] receives the history after each token."""
+    rows, ch = x.shape
+    if rows % n_tok:
+        raise ValueError(f"{rows} token rows are not a multiple of n_tok={n_tok}")
+    st = L.load().gdn_conv1d_verify(_ptr(x), _dt(x), _ptr(w), ch, rows // n_tok, n_tok, _ptr(conv_state),
+                                    conv_state.shape[0], _ptr(state_slots), _ptr(y), _ptr(windows),
+                                    windows.shape[1], _stream(stream))
+    L.check("gdn_conv1d_verify", st)
+    return y
+
+
+def gdn_state_rows_copy(dst, dst_rows, src=None, src_rows=None, *, stream=None):
+    """dst[dst_rows[e]] = src[src_rows[e]] (or zeros when src is None) over rows of the leading
+    dimension; dst and src rows must have the same size in bytes."""
+    row_bytes = dst[0].numel() * dst.element_size()
+    if src is not None and src[0].numel() * src.element_size() != row_bytes:
+        raise ValueError("dst and src rows differ in size")
+    st = L.load().gdn_state_rows_copy(_ptr(dst), dst.shape[0], _ptr(dst_rows), _ptr(src),
+                                      0 if src is None else src.shape[0], _ptr(src_rows), row_bytes,
+                                      dst_rows.numel(), _stream(stream))
+    L.check("gdn_state_rows_copy", st)
+    return dst
+
+
 def gdn_gated_rmsnorm(x, z, w, y, *, eps=1e-6, stream=None):
     """y = x / sqrt(mean(x^2) + eps) * w * SiLU(z) over the last dim (16 or 128)."""
     d = x.shape[-1]

@@ -245,6 +245,90 @@ gdn_status gdn_recurrent_step_gated(const void* q, const void* k, const void* v,
                                     const void* z, const float* norm_w, float norm_eps, void* stream);
 
 /*
+ * gdn_recurrent_verify -- speculative verification: n_tok tokens per request
+ * from the live state, the state after each token kept in a checkpoint column.
+ * (Flare core-design, speculative target state: eight recurrent checkpoint
+ *  columns per request, and a round writes the columns of its verification
+ *  inputs; the recurrence is the one at the top of this header.)
+ *
+ * Request r's tokens are rows r * n_tok + t (t = 0 .. n_tok - 1) of q, k, v,
+ * g, beta, z and o.  The live state[state_slots[r]] is only read; the state
+ * after token t is written to checkpoints[state_slots[r]][t].  Installing an
+ * accepted prefix of a tokens is gdn_state_rows_copy of column a - 1 into the
+ * live slot.
+ *
+ *   q, k, v, strides, dt, g, beta, scale, use_qk_l2norm, l2_eps, h_qk, h_v,
+ *   d_k, d_v: as gdn_recurrent_step, over n_req * n_tok token rows
+ *   n_tok       verification tokens per request, 1 <= n_tok <= n_cols
+ *   state       [n_slots, h_v, d_v, d_k] fp32 live states (read only)
+ *   state_slots [n_req] int32 slot per request, NULL = identity; negative =
+ *               inactive lane (reads nothing, writes nothing, o rows untouched)
+ *   checkpoints [n_slots, n_cols, h_v, d_v, d_k] fp32; columns 0 .. n_tok - 1 of
+ *               each active slot are written
+ *   o           [n_req * n_tok, h_v, d_v] of o_dt (the gated RMSNorm of the
+ *               outputs when z != NULL)
+ * n_req == 0 is a no-op.  Errors as gdn_recurrent_step; n_tok < 1 or
+ * n_tok > n_cols is GDN_ERR_INVALID.
+ */
+gdn_status gdn_recurrent_verify(const void* q, const void* k, const void* v,
+                                int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                                const float* g, const float* beta, float scale,
+                                int32_t use_qk_l2norm, float l2_eps,
+                                int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                                int32_t n_req, int32_t n_tok,
+                                const float* state, int32_t n_slots, const int32_t* state_slots,
+                                float* checkpoints, int32_t n_cols,
+                                void* o, gdn_dtype o_dt,
+                                const void* z, const float* norm_w, float norm_eps, void* stream);
+
+/*
+ * gdn_conv1d_verify -- the width-4 conv + SiLU of a speculative verification
+ * round: n_tok tokens per request from the live history, which is only read,
+ * with the 3-token history after each token kept as that column's window.
+ * (Flare core-design, speculative target state: a snapshot copies a column's
+ *  three-token GDN convolution window.)
+ *
+ *   x, y        [n_req * n_tok, channels] of dt (request r: rows r * n_tok + t)
+ *   w, channels as gdn_conv1d_fwd
+ *   conv_state  [n_slots, 3, channels] of dt, the live histories (read only)
+ *   state_slots [n_req] int32 or NULL (identity); negative = inactive lane
+ *   windows     [n_slots, n_cols, 3, channels] of dt: windows[slot][t] is the
+ *               history after token t (its last three raw inputs, oldest
+ *               first); columns 0 .. n_tok - 1 of each active slot are written
+ * n_req == 0 is a no-op; 1 <= n_tok <= n_cols.
+ */
+gdn_status gdn_conv1d_verify(const void* x, gdn_dtype dt, const void* w, int32_t channels,
+                             int32_t n_req, int32_t n_tok, const void* conv_state, int32_t n_slots,
+                             const int32_t* state_slots, void* y, void* windows, int32_t n_cols,
+                             void* stream);
+
+/*
+ * gdn_state_rows_copy -- indirect row copy for state maintenance: for each
+ * entry e < n, row dst_rows[e] of dst becomes a copy of row src_rows[e] of src,
+ * or zeros when src is NULL.  (Flare core-design, prepared state operations:
+ * initialize, restore, snapshot and reset are indirect copy kernels driven by
+ * device-resident slot-index buffers.)
+ *
+ * A row is a block of row_bytes (a multiple of 16) at dst + row * row_bytes:
+ * a recurrent state slot (h_v * d_v * d_k * 4 bytes), one checkpoint column
+ * (row slot * n_cols + column of the checkpoint array), a conv history
+ * (3 * channels * element bytes) or one window.  The copy is bit-exact.
+ *
+ *   dst, n_dst_rows   destination buffer of n_dst_rows rows (16-byte aligned)
+ *   dst_rows          [n] int32 destination rows (device)
+ *   src, n_src_rows   source buffer of n_src_rows rows, or NULL (zero fill)
+ *   src_rows          [n] int32 source rows (device); required when src != NULL
+ * An entry whose destination or source row lies outside [0, rows) of its
+ * buffer is skipped.  src may be dst itself (copies between rows of one
+ * pool); other overlaps are GDN_ERR_ALIAS.  The caller guarantees that no row
+ * is written by two entries or written by one entry and read by another.
+ * n == 0 is a no-op.
+ */
+gdn_status gdn_state_rows_copy(void* dst, int64_t n_dst_rows, const int32_t* dst_rows,
+                               const void* src, int64_t n_src_rows, const int32_t* src_rows,
+                               int64_t row_bytes, int32_t n, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * w * SiLU(z), per row of d.
  * (The gated RMSNorm of the GDN layers: haskell-infer-demo README,
  *  "Highlights", hybrid-architecture bullet, and "Architecture", gdn_norm.cu;

@@ -209,3 +209,58 @@ def test_recurrent_gated_validation(lib):
     assert step_gated(lib, gb=_addr(4) + 2) == L.GDN_ERR_ALIGN
     assert step_gated(lib, st=_addr(3) + 16) == L.GDN_ERR_ALIAS   # state overlaps a
     assert step_gated(lib, o=_addr(10) - 16) == L.GDN_ERR_ALIAS   # o overlaps a_log
+
+
+def verify(lib, **kw):
+    a = dict(g=_addr(3), n=3, w=4, st=_addr(5), ns=3, sl=None, ck=_addr(9), nc=8, o=_addr(6), z=None, nw=None)
+    a.update(kw)
+    return lib.gdn_recurrent_verify(_addr(0), _addr(1), _addr(2), 0, 0, 0, L.GDN_BF16, a["g"], _addr(4), 1.0, 1,
+                                    1e-6, 2, 4, 128, 128, a["n"], a["w"], a["st"], a["ns"], a["sl"], a["ck"], a["nc"],
+                                    a["o"], L.GDN_F32, a["z"], a["nw"], 1e-6, None)
+
+
+def test_verify_validation(lib):
+    assert verify(lib, n=0) == L.GDN_OK
+    assert verify(lib, w=0) == L.GDN_ERR_INVALID              # no tokens
+    assert verify(lib, w=9) == L.GDN_ERR_INVALID              # more tokens than checkpoint columns
+    assert verify(lib, ck=None) == L.GDN_ERR_NULL
+    assert verify(lib, g=None) == L.GDN_ERR_NULL
+    assert verify(lib, ns=2) == L.GDN_ERR_INVALID             # identity slots need n_slots >= n_req
+    assert verify(lib, ck=_addr(9) + 8) == L.GDN_ERR_ALIGN
+    assert verify(lib, ck=_addr(5) + 1024) == L.GDN_ERR_ALIAS  # checkpoints inside the live states
+    assert verify(lib, o=_addr(9) + 4096) == L.GDN_ERR_ALIAS   # outputs inside the checkpoints
+
+
+def conv_verify(lib, **kw):
+    a = dict(n=2, w=3, st=_addr(3), ns=2, y=_addr(4), win=_addr(5), nc=8)
+    a.update(kw)
+    return lib.gdn_conv1d_verify(_addr(0), L.GDN_BF16, _addr(1), 1024, a["n"], a["w"], a["st"], a["ns"], None,
+                                 a["y"], a["win"], a["nc"], None)
+
+
+def test_conv_verify_validation(lib):
+    assert conv_verify(lib, n=0) == L.GDN_OK
+    assert conv_verify(lib, w=0) == L.GDN_ERR_INVALID
+    assert conv_verify(lib, w=9) == L.GDN_ERR_INVALID
+    assert conv_verify(lib, win=None) == L.GDN_ERR_NULL
+    assert conv_verify(lib, ns=1) == L.GDN_ERR_INVALID
+    assert conv_verify(lib, win=_addr(3) + 64) == L.GDN_ERR_ALIAS   # windows over the live histories
+    assert conv_verify(lib, y=_addr(5) + 16) == L.GDN_ERR_ALIAS     # outputs inside the windows
+
+
+def rows_copy(lib, **kw):
+    a = dict(dst=_addr(0), nd=4, dr=_addr(1), src=_addr(2), ns=8, sr=_addr(3), rb=1 << 20, n=2)
+    a.update(kw)
+    return lib.gdn_state_rows_copy(a["dst"], a["nd"], a["dr"], a["src"], a["ns"], a["sr"], a["rb"], a["n"], None)
+
+
+def test_rows_copy_validation(lib):
+    assert rows_copy(lib, n=0) == L.GDN_OK
+    assert rows_copy(lib, n=-1) == L.GDN_ERR_INVALID
+    assert rows_copy(lib, rb=0) == L.GDN_ERR_INVALID
+    assert rows_copy(lib, rb=1000) == L.GDN_ERR_ALIGN            # rows of a whole number of 16-byte units
+    assert rows_copy(lib, dr=None) == L.GDN_ERR_NULL
+    assert rows_copy(lib, sr=None) == L.GDN_ERR_NULL             # a source needs its rows
+    assert rows_copy(lib, dst=_addr(0) + 8) == L.GDN_ERR_ALIGN
+    assert rows_copy(lib, dr=_addr(0) + 4096) == L.GDN_ERR_ALIAS  # index array inside the destination
+    assert rows_copy(lib, src=_addr(0) + (1 << 20)) == L.GDN_ERR_ALIAS   # partial overlap of two pools
