@@ -234,8 +234,13 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, int64_t q
                           float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t chunk,
                           const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total, const float* initial_state,
                           float* final_state, void* o, gdn_dtype o_dt, const void* z, const float* norm_w,
-                          float norm_eps, void* workspace, size_t ws_bytes, void* stream) {
-  if (n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
+                          float norm_eps, void* workspace, size_t ws_bytes, void* stream,
+                          const int32_t* state_slots = nullptr, const int32_t* fresh = nullptr,
+                          int32_t n_slots = 0) {
+  // With state_slots (the mixed prefill + decode form) initial_state and
+  // final_state are the same state pool of n_slots rows, read and written at
+  // the slot of each sequence.
+  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_INVALID;
   if (n_seq == 0) return GDN_OK;
   gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, ga.rows_missing(), h_qk, h_v, d_k, d_v,
                             t_total > 0);
@@ -252,9 +257,12 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, int64_t q
   st = gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_total, dt, z != nullptr, &need);
   if (st != GDN_OK) return st;
   if (ws_bytes < need) return GDN_ERR_WORKSPACE;
-  if (!all_aligned({o, z, norm_w, initial_state, final_state, workspace, cu_seqlens})) return GDN_ERR_ALIGN;
+  if (!all_aligned({o, z, norm_w, initial_state, final_state, workspace, cu_seqlens, state_slots, fresh}))
+    return GDN_ERR_ALIGN;
   const int eb = dt_bytes(dt);
-  const uint64_t state_bytes = static_cast<uint64_t>(n_seq) * h_v * d_v * d_k * 4;
+  const uint64_t state_bytes = static_cast<uint64_t>(state_slots ? n_slots : n_seq) * h_v * d_v * d_k * 4;
+  const Range rsl{state_slots, state_slots ? static_cast<uint64_t>(n_seq) * 4 : 0};
+  const Range rfr{fresh, fresh ? static_cast<uint64_t>(n_seq) * 4 : 0};
   const Range rq{q, strided_bytes(t_total, q_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
   const Range rk{k, strided_bytes(t_total, k_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
   const Range rv{v, strided_bytes(t_total, v_stride, static_cast<int64_t>(h_v) * d_v, eb)};
@@ -265,9 +273,10 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, int64_t q
   const Range rf{final_state, final_state ? state_bytes : 0};
   const Range rws{workspace, need};
   const Range rcu{cu_seqlens, cu_seqlens ? static_cast<uint64_t>(n_seq + 1) * 4 : 0};
-  if (!disjoint(ro, {rq, rk, rv, rz, rw, ri, rf, rws, rcu}) || !disjoint_gates(ro, gt)) return GDN_ERR_ALIAS;
-  if (!disjoint(rws, {rq, rk, rv, rz, rw, ri, rf, rcu}) || !disjoint_gates(rws, gt)) return GDN_ERR_ALIAS;
-  if (!disjoint(rf, {rq, rk, rv, rz, rw, rcu}) || !disjoint_gates(rf, gt)) return GDN_ERR_ALIAS;
+  if (!disjoint(ro, {rq, rk, rv, rz, rw, ri, rf, rws, rcu, rsl, rfr}) || !disjoint_gates(ro, gt))
+    return GDN_ERR_ALIAS;
+  if (!disjoint(rws, {rq, rk, rv, rz, rw, ri, rf, rcu, rsl, rfr}) || !disjoint_gates(rws, gt)) return GDN_ERR_ALIAS;
+  if (!disjoint(rf, {rq, rk, rv, rz, rw, rcu, rsl, rfr}) || !disjoint_gates(rf, gt)) return GDN_ERR_ALIAS;
   if (initial_state && final_state && initial_state != final_state && overlap(ri, rf)) return GDN_ERR_ALIAS;
 
   gdn::ChunkArgs a;
@@ -278,6 +287,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, int64_t q
   a.h_qk = h_qk; a.h_v = h_v; a.d = d_k; a.chunk = chunk;
   a.cu = cu_seqlens; a.n_seq = n_seq; a.t_total = t_total;
   a.init = initial_state; a.fin = final_state;
+  a.slots = state_slots; a.fresh = fresh;
   a.o = o; a.o_dt = o_dt; a.z = z; a.norm_w = norm_w; a.norm_eps = norm_eps;
   a.workspace = workspace; a.stream = stream;
   return finish(gdn::launch_chunk_fwd(a));
@@ -468,6 +478,44 @@ gdn_status gdn_state_rows_copy(void* dst, int64_t n_dst_rows, const int32_t* dst
   if (!disjoint(rd, {rdi, rsi})) return GDN_ERR_ALIAS;
   if (src && src != dst && overlap(rd, rsrc)) return GDN_ERR_ALIAS;
   return finish(gdn::launch_rows_copy(dst, n_dst_rows, dst_rows, src, n_src_rows, src_rows, row_bytes, n, stream));
+}
+
+gdn_status gdn_conv1d_mixed(const void* x, gdn_dtype dt, const void* w, int32_t channels, const int32_t* cu_seqlens,
+                            int32_t n_seq, int64_t t_total, void* conv_state, int32_t n_slots,
+                            const int32_t* state_slots, const int32_t* fresh, void* y, void* stream) {
+  if (n_seq < 0 || t_total < 0 || channels <= 0 || n_slots < 0) return GDN_ERR_INVALID;
+  if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
+  if (channels % 8) return GDN_ERR_INVALID;
+  if (n_seq == 0) return GDN_OK;
+  if (!cu_seqlens || !state_slots || !w || !conv_state) return GDN_ERR_NULL;
+  if (t_total > 0 && (!x || !y)) return GDN_ERR_NULL;
+  if (!all_aligned({x, w, conv_state, y, cu_seqlens, state_slots, fresh})) return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const Range rx{x, static_cast<uint64_t>(t_total) * channels * eb};
+  const Range ry{y, static_cast<uint64_t>(t_total) * channels * eb};
+  const Range rw{w, static_cast<uint64_t>(channels) * 4 * eb};
+  const Range rs{conv_state, static_cast<uint64_t>(n_slots) * 3 * channels * eb};
+  const Range rcu{cu_seqlens, static_cast<uint64_t>(n_seq + 1) * 4};
+  const Range rsl{state_slots, static_cast<uint64_t>(n_seq) * 4};
+  const Range rfr{fresh, fresh ? static_cast<uint64_t>(n_seq) * 4 : 0};
+  if (!disjoint(ry, {rx, rw, rs, rcu, rsl, rfr}) || !disjoint(rs, {rx, rw, rcu, rsl, rfr})) return GDN_ERR_ALIAS;
+  return finish(gdn::launch_conv1d(x, dt, w, channels, cu_seqlens, n_seq, t_total, conv_state, state_slots, y,
+                                   stream, fresh));
+}
+
+gdn_status gdn_chunk_mixed(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                           int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                           int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                           int32_t chunk, const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total, float* state,
+                           int32_t n_slots, const int32_t* state_slots, const int32_t* fresh, void* o,
+                           gdn_dtype o_dt, const void* z, const float* norm_w, float norm_eps, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  if (n_seq < 0 || t_total < 0 || n_slots < 0) return GDN_ERR_INVALID;
+  if (n_seq == 0) return GDN_OK;
+  if (!cu_seqlens || !state_slots || !state) return GDN_ERR_NULL;
+  return chunk_fwd_impl(q, k, v, q_stride, k_stride, v_stride, dt, plain_gates(g, beta), scale, use_qk_l2norm,
+                        l2_eps, h_qk, h_v, d_k, d_v, chunk, cu_seqlens, n_seq, t_total, state, state, o, o_dt, z,
+                        norm_w, norm_eps, workspace, ws_bytes, stream, state_slots, fresh, n_slots);
 }
 
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w, float eps,

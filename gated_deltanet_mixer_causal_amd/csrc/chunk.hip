@@ -299,7 +299,8 @@ template <class Pol, int D, int C>
 __global__ __launch_bounds__(256) void k_chunk_prep(
     const typename Pol::In::T* __restrict__ q, const typename Pol::In::T* __restrict__ k,
     int64_t q_stride, int64_t k_stride, GateSrc gates, float scale, int use_l2, float l2_eps, int h_qk, int h_v,
-    const int32_t* __restrict__ cu, int n_seq, int64_t t_total, ChunkWs ws, int64_t n_slots) {
+    const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const int32_t* __restrict__ seq_slots, ChunkWs ws,
+    int64_t n_slots) {
   using Elem = typename Pol::Elem;
   using W = WsLayout<Pol, D, C>;
   constexpr int LDK = D + Pol::PAD;
@@ -350,6 +351,7 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
 #define GDN_PREP_FETCH(uu)                                                                              \
   do {                                                                                                 \
     n_ok = (uu) < n_units && locate_block(cu, n_seq, t_total, C, (uu) / h_qk, n_seq_i, n_t0, n_len);     \
+    if (n_ok && seq_slots) n_ok = seq_slots[n_seq_i] >= 0;   /* inactive lane: no scan reads it */        \
     if (n_ok) {                                                                                        \
       const int fq_ = static_cast<int>((uu) % h_qk);                                                   \
       _Pragma("unroll") for (int it = 0; it < NR; ++it) {                                              \
@@ -671,8 +673,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     const typename Pol::In::T* __restrict__ q, const typename Pol::In::T* __restrict__ k,
     const typename Pol::In::T* __restrict__ v, int64_t q_stride, int64_t k_stride, int64_t v_stride,
     int h_qk, int h_v, const int32_t* __restrict__ cu, int n_seq, int64_t t_total,
-    const float* __restrict__ init, float* __restrict__ fin,
-    typename EO::T* __restrict__ o, ChunkWs ws) {
+    const float* __restrict__ init, float* __restrict__ fin, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ fresh, typename EO::T* __restrict__ o, ChunkWs ws) {
   using Elem = typename Pol::Elem;
   using In = typename Pol::In;
   using Frag = typename Pol::Frag;
@@ -721,6 +723,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   const int64_t rank = b / per_seq;
   if (rank >= n_seq) return;
   const int s = ws.order ? ws.order[rank] : static_cast<int>(rank);
+  // State row of the sequence: its slot in the caller's state pool (identity
+  // without a slot map).  A negative slot is an inactive lane, which reads
+  // and writes nothing; a fresh sequence starts from the zero state.
+  const int sslot = slots ? slots[s] : s;
+  if (sslot < 0) return;
+  const bool from_init = init != nullptr && !(fresh && fresh[s] != 0);
   const int64_t lid = xcd_order(b % per_seq, per_seq);
   const int tile = static_cast<int>(lid % NTILE);
   const int h = static_cast<int>(lid / NTILE);
@@ -752,7 +760,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   // fp32 master state: tiles (mt = wave + 4 j, nt) of S^T (rows d_k, columns
   // d_v): lane holds S[dv0 + 16 nt + r16][16 mt + 4 g4 + i].
   floatx4 Sacc[SPW][NV];
-  const int64_t srow = ((int64_t)s * h_v + h) * D + dv0 + r16;   // state row of this lane (nt = 0)
+  const int64_t srow = ((int64_t)sslot * h_v + h) * D + dv0 + r16;   // state row of this lane (nt = 0)
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int mt = wave + 4 * j;
@@ -760,7 +768,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
     for (int nt = 0; nt < NV; ++nt) {
       Sacc[j][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
       if (kAllTiles || mt < NST) {
-        if (init) {
+        if (from_init) {
           const float4 v4 = *reinterpret_cast<const float4*>(init + (srow + 16 * nt) * D + 16 * mt + 4 * g4);
           Sacc[j][nt] = floatx4{v4.x, v4.y, v4.z, v4.w};
         }
@@ -1087,7 +1095,7 @@ static hipError_t run_chunk(const ChunkArgs& a) {
     const int64_t grid = units < resident ? units : resident;
     hipLaunchKernelGGL((k_chunk_prep<Pol, D, C>), dim3(static_cast<unsigned>(grid)), dim3(256), 0, st, q, k,
                        a.q_stride, a.k_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu,
-                       a.n_seq, a.t_total, ws, slots);
+                       a.n_seq, a.t_total, a.slots, ws, slots);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1105,22 +1113,22 @@ static hipError_t run_chunk(const ChunkArgs& a) {
   if (a.z) {
     hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
-                       a.init, a.fin, o_pre, ws);
+                       a.init, a.fin, a.slots, a.fresh, o_pre, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.t_total > 0)
       return launch_gated_rmsnorm(o_pre, GDN_F32, a.z, a.dt, a.norm_w, a.norm_eps, a.t_total * a.h_v, D,
-                                  a.o, a.o_dt, a.stream);
+                                  a.o, a.o_dt, a.stream, a.slots ? a.cu : nullptr, a.n_seq, a.slots, a.h_v);
     return hipSuccess;
   }
   if (a.o_dt == GDN_BF16)
     hipLaunchKernelGGL((k_chunk_scan<Pol, BF16, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
-                       a.init, a.fin, static_cast<uint16_t*>(a.o), ws);
+                       a.init, a.fin, a.slots, a.fresh, static_cast<uint16_t*>(a.o), ws);
   else
     hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
-                       a.init, a.fin, static_cast<float*>(a.o), ws);
+                       a.init, a.fin, a.slots, a.fresh, static_cast<float*>(a.o), ws);
   return hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ struct BF16 {
   // 8 consecutive elements (16 bytes) -> float[8]
   // 8 consecutive elements as raw bits (one 16-byte access)
   using Vec = uint4;
+  __device__ __forceinline__ static Vec zero_vec() { return make_uint4(0u, 0u, 0u, 0u); }
   __device__ __forceinline__ static Vec ld_vec(const T* p) { return *reinterpret_cast<const uint4*>(p); }
   __device__ __forceinline__ static void st_vec(T* p, Vec v) { *reinterpret_cast<uint4*>(p) = v; }
   __device__ __forceinline__ static void unpack8(Vec r, float* out) {
@@ -82,6 +83,9 @@ struct F32 {
   struct Vec {
     float4 a, b;
   };
+  __device__ __forceinline__ static Vec zero_vec() {
+    return Vec{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  }
   __device__ __forceinline__ static Vec ld_vec(const T* p) {
     return Vec{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
   }
@@ -189,6 +193,20 @@ __device__ __forceinline__ bool locate_block(const int32_t* cu, int n_seq, int64
   seq = lo;
   len = static_cast<int>(end - t0 < blk ? end - t0 : blk);
   return true;
+}
+
+// The zero-length sequence whose (only) slot is `slot`, or -1.  Slot keys
+// floor(cu[s]/blk) + s strictly increase with s, so at most one sequence
+// has key == slot.
+__device__ __forceinline__ int empty_seq_at(const int32_t* cu, int n_seq, int64_t t_total, int blk, int64_t slot) {
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq_start(cu, mid, t_total) / blk + mid <= slot) lo = mid; else hi = mid - 1;
+  }
+  const int64_t start = seq_start(cu, lo, t_total);
+  if (start / blk + lo != slot || seq_start(cu, lo + 1, t_total) != start) return -1;
+  return lo;
 }
 
 __host__ __device__ constexpr int64_t block_slots(int64_t t_total, int n_seq, int blk) {

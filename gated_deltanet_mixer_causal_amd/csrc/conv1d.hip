@@ -51,7 +51,8 @@ template <class E>
 __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
     const typename E::T* __restrict__ x, const typename E::T* __restrict__ w, int channels,
     const int32_t* __restrict__ cu, int n_seq, int64_t t_total, typename E::T* __restrict__ state,
-    const int32_t* __restrict__ slots, typename E::T* __restrict__ y, int64_t n_tblk, int n_slices) {
+    const int32_t* __restrict__ slots, const int32_t* __restrict__ fresh, typename E::T* __restrict__ y,
+    int64_t n_tblk, int n_slices) {
   using T = typename E::T;
   const int64_t lid = xcd_order(blockIdx.x, n_tblk * n_slices);
   const int slice = static_cast<int>(lid / n_tblk);
@@ -60,7 +61,19 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
   if (c0 >= channels) return;
   int seq, len;
   int64_t t0;
-  if (!locate_block(cu, n_seq, t_total, kConvBT, tblk, seq, t0, len)) return;
+  if (!locate_block(cu, n_seq, t_total, kConvBT, tblk, seq, t0, len)) {
+    // a fresh zero-length sequence: its history becomes zeros
+    if (fresh) {
+      const int es = empty_seq_at(cu, n_seq, t_total, kConvBT, tblk);
+      const int es_slot = es < 0 ? -1 : (slots ? slots[es] : es);
+      if (es_slot >= 0 && fresh[es] != 0) {
+        T* h = state + static_cast<int64_t>(es_slot) * 3 * channels + c0;
+#pragma unroll
+        for (int r = 0; r < 3; ++r) E::st_vec(h + r * static_cast<int64_t>(channels), E::zero_vec());
+      }
+    }
+    return;
+  }
   const int slot = slots ? slots[seq] : seq;
   if (slot < 0) return;
   const int64_t start = cu[seq];
@@ -69,13 +82,16 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
   T* hist = state + static_cast<int64_t>(slot) * 3 * ld + c0;
 
   // every row this thread reads: raw inputs at local positions p0-3 .. p0-1
-  // (history rows in the first block) and the block's own rows (rows past
-  // the block's end re-read its last row and are not used)
+  // (history rows in the first block; zeros for a fresh sequence, whose
+  // history is not read) and the block's own rows (rows past the block's end
+  // re-read its last row and are not used)
   typename E::Vec raw[3 + kConvBT];
+  const bool zero_hist = p0 < 3 && fresh != nullptr && fresh[seq] != 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
     const int64_t lp = p0 - 3 + r;
-    raw[r] = E::ld_vec(lp >= 0 ? x + (start + lp) * ld + c0 : hist + (3 + lp) * ld);
+    if (lp < 0 && zero_hist) raw[r] = E::zero_vec();
+    else raw[r] = E::ld_vec(lp >= 0 ? x + (start + lp) * ld + c0 : hist + (3 + lp) * ld);
   }
 #pragma unroll
   for (int u = 0; u < kConvBT; ++u) raw[3 + u] = E::ld_vec(x + (t0 + (u < len ? u : len - 1)) * ld + c0);
@@ -188,14 +204,15 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_verify(
 
 template <class E>
 static hipError_t run_conv(const void* x, const void* w, int channels, const int32_t* cu, int n_seq,
-                           int64_t t_total, void* state, const int32_t* slots, void* y, hipStream_t st) {
+                           int64_t t_total, void* state, const int32_t* slots, void* y, hipStream_t st,
+                           const int32_t* fresh) {
   using T = typename E::T;
   if (cu) {
     const int64_t ntblk = block_slots(t_total, n_seq, kConvBT);
     const int nslices = (channels + kConvCh - 1) / kConvCh;
     hipLaunchKernelGGL((k_conv1d_prefill<E>), dim3(static_cast<unsigned>(ntblk * nslices)), dim3(kConvThreads), 0, st,
                        static_cast<const T*>(x), static_cast<const T*>(w), channels, cu, n_seq, t_total,
-                       static_cast<T*>(state), slots, static_cast<T*>(y), ntblk, nslices);
+                       static_cast<T*>(state), slots, fresh, static_cast<T*>(y), ntblk, nslices);
   } else {
     const int64_t threads = static_cast<int64_t>(n_seq) * (channels / 8);
     const unsigned blocks = static_cast<unsigned>((threads + kConvThreads - 1) / kConvThreads);
@@ -228,10 +245,10 @@ hipError_t launch_conv1d_verify(const void* x, gdn_dtype dt, const void* w, int 
 
 hipError_t launch_conv1d(const void* x, gdn_dtype dt, const void* w, int channels, const int32_t* cu,
                          int n_seq, int64_t t_total, void* state, const int32_t* slots, void* y,
-                         void* stream) {
+                         void* stream, const int32_t* fresh) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dt == GDN_BF16) return run_conv<BF16>(x, w, channels, cu, n_seq, t_total, state, slots, y, st);
-  return run_conv<F32>(x, w, channels, cu, n_seq, t_total, state, slots, y, st);
+  if (dt == GDN_BF16) return run_conv<BF16>(x, w, channels, cu, n_seq, t_total, state, slots, y, st, fresh);
+  return run_conv<F32>(x, w, channels, cu, n_seq, t_total, state, slots, y, st, fresh);
 }
 
 }  // namespace gdn

@@ -25,6 +25,8 @@ struct ChunkArgs {
   int64_t t_total;
   const float* init;
   float* fin;
+  const int32_t* slots;   // state row per sequence (NULL = identity); negative = inactive lane
+  const int32_t* fresh;   // per sequence: nonzero = start from the zero state (NULL = none)
   void* o;
   gdn_dtype o_dt;
   const void* z;
@@ -90,8 +92,12 @@ hipError_t launch_rows_copy(void* dst, int64_t n_dst, const int32_t* dst_rows, c
                             const int32_t* src_rows, int64_t row_bytes, int n, void* stream);
 hipError_t launch_conv1d(const void* x, gdn_dtype dt, const void* w, int channels, const int32_t* cu,
                          int n_seq, int64_t t_total, void* state, const int32_t* slots, void* y,
-                         void* stream);
+                         void* stream, const int32_t* fresh = nullptr);
+// With cu != nullptr, rows are (token, v-head) pairs (h_v per token) of packed
+// sequences and only rows of sequences with a non-negative slot are written.
 hipError_t launch_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w,
-                                float eps, int64_t rows, int d, void* y, gdn_dtype y_dt, void* stream);
+                                float eps, int64_t rows, int d, void* y, gdn_dtype y_dt, void* stream,
+                                const int32_t* cu = nullptr, int n_seq = 0, const int32_t* slots = nullptr,
+                                int h_v = 1);
 
 }  // namespace gdn

@@ -190,6 +190,42 @@ def gdn_state_rows_copy(dst, dst_rows, src=None, src_rows=None, *, stream=None):
     return dst
 
 
+def gdn_conv1d_mixed(x, w, conv_state, y, *, cu_seqlens, state_slots, fresh=None, stream=None):
+    """Mixed prefill + decode conv1d + SiLU.  x, y [T_cap, Ch]; cu_seqlens [N_cap + 1]
+    (cu[N_cap] <= T_cap live rows); state_slots, fresh [N_cap] int32; conv_state
+    [slots, 3, Ch] updated in place at each active slot."""
+    t_cap, ch = x.shape
+    n_seq = cu_seqlens.numel() - 1
+    st = L.load().gdn_conv1d_mixed(_ptr(x), _dt(x), _ptr(w), ch, _ptr(cu_seqlens), n_seq, t_cap,
+                                   _ptr(conv_state), conv_state.shape[0], _ptr(state_slots), _ptr(fresh),
+                                   _ptr(y), _stream(stream))
+    L.check("gdn_conv1d_mixed", st)
+    return y
+
+
+def gdn_chunk_mixed(q, k, v, g, beta, state, o, *, chunk, cu_seqlens, state_slots, fresh=None, scale=1.0,
+                    use_qk_l2norm=True, l2_eps=1e-6, z=None, norm_w=None, norm_eps=1e-6, workspace=None,
+                    stream=None):
+    """Mixed prefill + decode gated delta rule over a state pool.  q, k [T_cap, Hqk, dk];
+    v [T_cap, Hv, dv]; g, beta [T_cap, Hv]; state [slots, Hv, dv, dk] fp32 updated in
+    place at each active slot; o [T_cap, Hv, dv] (rows of inactive sequences and
+    padding rows untouched)."""
+    t_cap, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n_seq = cu_seqlens.numel() - 1
+    if workspace is None:
+        nbytes = gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_cap, q.dtype, z is not None)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.load().gdn_chunk_mixed(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(g), _ptr(beta), float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, chunk, _ptr(cu_seqlens), n_seq, t_cap,
+        _ptr(state), state.shape[0], _ptr(state_slots), _ptr(fresh), _ptr(o), _dt(o),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _ptr(workspace), workspace.numel(), _stream(stream))
+    L.check("gdn_chunk_mixed", st)
+    return o
+
+
 def gdn_gated_rmsnorm(x, z, w, y, *, eps=1e-6, stream=None):
     """y = x / sqrt(mean(x^2) + eps) * w * SiLU(z) over the last dim (16 or 128)."""
     d = x.shape[-1]

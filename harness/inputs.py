@@ -146,6 +146,29 @@ def prefill_inputs(seed: int, layout: Layout, lengths, *, state_std: float | Non
                 lengths=lengths, scale=1.0, l2_eps=L2_EPS, norm_eps=NORM_EPS)
 
 
+def mixed_batch_inputs(seed: int, layout: Layout, lengths, n_slots: int, *, t_pad: int = 0) -> dict:
+    """A serving batch packed for the mixed prefill-plus-decode calls: prompt
+    chunks and decode tokens (length-1 sequences) with per-token data drawn as
+    prefill_inputs draws it, t_pad padding rows after the live ones, and state
+    pools of n_slots rows: histories N(0,1), states N(0, 0.02^2).
+
+    Draw order: the prefill_inputs draws for the live tokens (zero states),
+    then the history pool, then the state pool.  Padding rows of x, beta, g
+    and z are zeros here; tests poison them.
+    """
+    rng = np.random.default_rng(seed)
+    d = prefill_inputs(seed, layout, lengths, rng=rng)
+    ch, hv, dv, dk = layout.channels, layout.h_v, layout.d_v, layout.d_k
+    d["tail_pool"] = _cast(_normal(rng, (n_slots, 3, ch)), layout.dtype)
+    d["state_pool"] = _normal(rng, (n_slots, hv, dv, dk), 0.02)
+    if t_pad:
+        for key in ("x", "beta", "g", "z"):
+            a = d[key]
+            d[key] = np.concatenate([a, np.zeros((t_pad,) + a.shape[1:], a.dtype)])
+    d["t_cap"] = int(sum(lengths)) + t_pad
+    return d
+
+
 def raw_gate_inputs(seed: int, t: int, h_v: int, *, dtype: str = "f32",
                     a_log_range=(0.0, math.log(16.0)), bias_std: float | None = None) -> dict:
     """Raw gate projections for the fused gate preparation.

@@ -329,6 +329,61 @@ gdn_status gdn_state_rows_copy(void* dst, int64_t n_dst_rows, const int32_t* dst
                                int64_t row_bytes, int32_t n, void* stream);
 
 /*
+ * gdn_conv1d_mixed, gdn_chunk_mixed -- the mixed prefill-plus-decode form of
+ * gdn_conv1d_fwd and gdn_chunk_fwd for a serving batch: prompt chunks and
+ * single decode tokens packed into one call over caller-owned state pools.
+ * (Flare core-design, the short-convolution paragraph and its prepared
+ *  interface list: caller-owned state, explicit request-to-state-slot
+ *  mapping, a fresh-state flag, device-resident sequence and token counts,
+ *  fixed token and sequence capacities, a mixed prefill-plus-decode mode,
+ *  inactive lanes that write no state; the state-maintenance paragraph:
+ *  padding changes capacity, never logical length, and padded rows take no
+ *  part in convolution or recurrent updates.)
+ *
+ * The host passes capacities only: n_seq is the sequence capacity and
+ * t_total the token capacity of the packed buffers.  The live counts are
+ * device data: cu_seqlens[n_seq] <= t_total is the number of live token rows
+ * (rows past it are padding and keep their contents in every output), and a
+ * padded sequence has length 0 and slot -1.  A decode token is a sequence of
+ * length 1.  For sequence s with slot p = state_slots[s] >= 0:
+ *   - its history / state is zero when fresh[s] != 0 (the pool row is not
+ *     read), else conv_state[p] / state[p];
+ *   - its rows are computed as by gdn_conv1d_fwd / gdn_chunk_fwd;
+ *   - conv_state[p] / state[p] receive its history / state after exactly
+ *     len(s) tokens (zero-length: the initial value, zeros when fresh).
+ * A sequence with p < 0 is an inactive lane: nothing is read or written for
+ * it, and its rows of y / o keep their contents.
+ *
+ *   gdn_conv1d_mixed: x, dt, w, channels, conv_state, n_slots, y as
+ *               gdn_conv1d_fwd; cu_seqlens [n_seq + 1] and state_slots [n_seq]
+ *               int32 required; fresh [n_seq] int32 or NULL (none fresh)
+ *   gdn_chunk_mixed: q, k, v, strides, dt, g, beta, scale, use_qk_l2norm,
+ *               l2_eps, head sizes, chunk, o, o_dt, z, norm_w, norm_eps and
+ *               workspace as gdn_chunk_fwd (workspace sized by
+ *               gdn_chunk_fwd_workspace_size for the capacities);
+ *               state [n_slots, h_v, d_v, d_k] fp32, read and written in place;
+ *               cu_seqlens, state_slots required, fresh optional (as above)
+ * Active slots must be distinct (caller's guarantee, like the contents of
+ * cu_seqlens).  n_seq == 0 is a no-op.  Statuses as the plain entry points;
+ * a missing cu_seqlens, state_slots or state is GDN_ERR_NULL.
+ */
+gdn_status gdn_conv1d_mixed(const void* x, gdn_dtype dt, const void* w, int32_t channels,
+                            const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                            void* conv_state, int32_t n_slots, const int32_t* state_slots,
+                            const int32_t* fresh, void* y, void* stream);
+
+gdn_status gdn_chunk_mixed(const void* q, const void* k, const void* v,
+                           int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                           const float* g, const float* beta, float scale,
+                           int32_t use_qk_l2norm, float l2_eps,
+                           int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t chunk,
+                           const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                           float* state, int32_t n_slots, const int32_t* state_slots, const int32_t* fresh,
+                           void* o, gdn_dtype o_dt,
+                           const void* z, const float* norm_w, float norm_eps,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * w * SiLU(z), per row of d.
  * (The gated RMSNorm of the GDN layers: haskell-infer-demo README,
  *  "Highlights", hybrid-architecture bullet, and "Architecture", gdn_norm.cu;

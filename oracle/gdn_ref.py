@@ -51,6 +51,12 @@ the design notes of the repository):
     round writes the columns of its verification inputs, and a snapshot copies a
     column with its three-token convolution window).
 
+  * Mixed prefill-plus-decode batches over state pools (the prepared
+    interface list under the short-convolution paragraph of Flare
+    core-design): the host knows capacities only; a padded sequence has
+    length 0 and slot -1; a fresh sequence starts from zero history and
+    state without reading its pool row.
+
 Parity status: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py (closed forms, invariants, brute force, an
 independent product-of-matrices form of the recurrence, and a chunked
@@ -342,6 +348,51 @@ def mixer_decode_step(x, conv_w, tail, state, beta, g, z, norm_w, slots, *,
         o[r] = orow[0]
         if z is not None:
             y[r] = gated_rmsnorm(orow[0], z[r], norm_w, norm_eps)
+    return dict(y_conv=y_conv, o=o, y=y)
+
+
+def mixer_mixed(x, conv_w, conv_pool, state_pool, slots, fresh, beta, g, z, norm_w, cu_seqlens, *,
+                h_qk, h_v, d_k, d_v, bf16_boundary: bool, scale=1.0, l2_eps=1e-6, norm_eps=1e-6,
+                qk_of_v=None):
+    """A mixed prefill-plus-decode batch over caller-owned state pools (Flare
+    core-design: the prepared short-convolution interface with state-slot ids,
+    a fresh-state flag, device-resident counts, fixed capacities and a mixed
+    prefill-plus-decode mode; inactive lanes write no state; padding changes
+    capacity, never logical length, and padded rows take no part in any update).
+
+    x [T_cap, Ch] holds cu_seqlens[-1] <= T_cap live rows; the rest is padding.
+    For each sequence s with slot p = slots[s] >= 0: the history and the state
+    it starts from are zeros if fresh[s] else conv_pool[p] and state_pool[p];
+    it runs the mixer (mixer_prefill on its own tokens); the pools' row p then
+    holds its history and state after exactly its tokens.  A sequence with
+    p < 0 is inactive: nothing is read or written.  conv_pool [n_slots, 3, Ch]
+    and state_pool [n_slots, Hv, dv, dk] are float64 arrays updated in place;
+    output rows that no active sequence writes (inactive, padding) are NaN.
+    A decode token is a sequence of length 1.  Returns dict(y_conv, o, y).
+    """
+    cu = np.asarray(cu_seqlens, np.int64)
+    t_cap, ch = np.asarray(x).shape
+    y_conv = np.full((t_cap, ch), np.nan)
+    o = np.full((t_cap, h_v, d_v), np.nan)
+    y = np.full((t_cap, h_v, d_v), np.nan)
+    for s in range(len(cu) - 1):
+        p = int(slots[s])
+        if p < 0:
+            continue
+        a, b = int(cu[s]), int(cu[s + 1])
+        is_fresh = fresh is not None and bool(fresh[s])
+        tail0 = np.zeros((1, 3, ch)) if is_fresh else conv_pool[p:p + 1]
+        state0 = np.zeros((1, h_v, d_v, d_k)) if is_fresh else state_pool[p:p + 1]
+        r = mixer_prefill(x[a:b], conv_w, tail0, state0, beta[a:b], g[a:b],
+                          None if z is None else z[a:b], norm_w, [0, b - a],
+                          h_qk=h_qk, h_v=h_v, d_k=d_k, d_v=d_v, bf16_boundary=bf16_boundary,
+                          scale=scale, l2_eps=l2_eps, norm_eps=norm_eps, qk_of_v=qk_of_v)
+        y_conv[a:b] = r["y_conv"]
+        o[a:b] = r["o"]
+        if z is not None:
+            y[a:b] = r["y"]
+        conv_pool[p] = r["tail"][0]
+        state_pool[p] = r["state"][0]
     return dict(y_conv=y_conv, o=o, y=y)
 
 

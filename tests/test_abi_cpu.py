@@ -105,6 +105,49 @@ def test_chunk_validation(lib):
     assert chunk(lib, init=_addr(6) + 64) == L.GDN_ERR_ALIAS  # partial overlap of the states
 
 
+def conv_mixed(lib, **kw):
+    a = dict(x=_addr(0), dt=L.GDN_BF16, w=_addr(1), ch=1024, cu=_addr(2), n=2, t=10, st=_addr(3), ns=4,
+             sl=_addr(5), fr=_addr(6), y=_addr(4))
+    a.update(kw)
+    return lib.gdn_conv1d_mixed(a["x"], a["dt"], a["w"], a["ch"], a["cu"], a["n"], a["t"], a["st"], a["ns"],
+                                a["sl"], a["fr"], a["y"], None)
+
+
+def test_conv_mixed_validation(lib):
+    assert conv_mixed(lib, n=0) == L.GDN_OK
+    assert conv_mixed(lib, ns=-1) == L.GDN_ERR_INVALID
+    assert conv_mixed(lib, cu=None) == L.GDN_ERR_NULL        # the mixed form always takes cu_seqlens
+    assert conv_mixed(lib, sl=None) == L.GDN_ERR_NULL        # ... and an explicit slot map
+    assert conv_mixed(lib, fr=_addr(6) + 4) == L.GDN_ERR_ALIGN
+    assert conv_mixed(lib, y=_addr(5)) == L.GDN_ERR_ALIAS    # y over the slot map
+    assert conv_mixed(lib, st=_addr(6) - 16) == L.GDN_ERR_ALIAS   # history pool over the fresh flags
+
+
+def chunk_mixed(lib, **kw):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), qs=0, ks=0, vs=0, dt=L.GDN_BF16, g=_addr(3), b=_addr(4),
+             hq=2, hv=4, dk=128, dv=128, c=64, cu=_addr(5), n=3, t=100, st=_addr(6), ns=8, sl=_addr(9),
+             fr=_addr(10), o=_addr(7), odt=L.GDN_F32, z=None, nw=None, ws=_addr(8), wsb=1 << 26)
+    a.update(kw)
+    return lib.gdn_chunk_mixed(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["dt"], a["g"], a["b"], 1.0,
+                               1, 1e-6, a["hq"], a["hv"], a["dk"], a["dv"], a["c"], a["cu"], a["n"], a["t"],
+                               a["st"], a["ns"], a["sl"], a["fr"], a["o"], a["odt"], a["z"], a["nw"], 1e-6, a["ws"],
+                               a["wsb"], None)
+
+
+def test_chunk_mixed_validation(lib):
+    assert chunk_mixed(lib, n=0) == L.GDN_OK
+    assert chunk_mixed(lib, ns=-2) == L.GDN_ERR_INVALID
+    assert chunk_mixed(lib, cu=None) == L.GDN_ERR_NULL
+    assert chunk_mixed(lib, sl=None) == L.GDN_ERR_NULL
+    assert chunk_mixed(lib, st=None) == L.GDN_ERR_NULL
+    assert chunk_mixed(lib, wsb=1024) == L.GDN_ERR_WORKSPACE
+    assert chunk_mixed(lib, sl=_addr(9) + 8) == L.GDN_ERR_ALIGN
+    assert chunk_mixed(lib, o=_addr(9)) == L.GDN_ERR_ALIAS   # o over the slot map
+    # the pool spans n_slots rows of 4 x 128 x 128 fp32 (2 MiB): one ending inside the fresh flags
+    pool = 8 * 4 * 128 * 128 * 4
+    assert chunk_mixed(lib, st=_addr(10) - pool + 16) == L.GDN_ERR_ALIAS
+
+
 def test_chunk_workspace_size(lib):
     out = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0

@@ -550,3 +550,109 @@ def test_conv_windows_equal_conv_tail():
     for t in range(1, w):
         np.testing.assert_array_equal(win[t][:2], win[t - 1][1:])
         np.testing.assert_array_equal(win[t][2], x[t])
+
+
+# ---------------------------------------------------------------------------
+# Mixed prefill-plus-decode batches over state pools
+# ---------------------------------------------------------------------------
+
+def _mixed_case(seed, lengths, t_pad=3):
+    rng = np.random.default_rng(seed)
+    hqk, hv, dk, dv = 1, 2, 4, 4
+    ch = 2 * hqk * dk + hv * dv
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T = int(cu[-1]) + t_pad
+    d = dict(x=rng.standard_normal((T, ch)), w=rng.standard_normal((ch, 4)),
+             g=-rng.uniform(0, 1, (T, hv)), beta=rng.uniform(0, 1, (T, hv)),
+             z=rng.standard_normal((T, hv, dv)), nw=1 + 0.1 * rng.standard_normal(dv), cu=cu)
+    n_slots = len(lengths) + 3
+    d["tails"] = rng.standard_normal((n_slots, 3, ch))
+    d["states"] = 0.1 * rng.standard_normal((n_slots, hv, dv, dk))
+    d["kw"] = dict(h_qk=hqk, h_v=hv, d_k=dk, d_v=dv, bf16_boundary=False)
+    return d
+
+
+def _run_mixed(d, slots, fresh, tails=None, states=None):
+    tails = d["tails"].copy() if tails is None else tails
+    states = d["states"].copy() if states is None else states
+    out = R.mixer_mixed(d["x"], d["w"], tails, states, slots, fresh, d["beta"], d["g"], d["z"], d["nw"],
+                        d["cu"], **d["kw"])
+    return out, tails, states
+
+
+def test_mixed_identity_slots_equal_packed_prefill():
+    d = _mixed_case(31, [5, 1, 7, 1], t_pad=0)
+    n = len(d["cu"]) - 1
+    out, tails, states = _run_mixed(d, list(range(n)), None)
+    ref = R.mixer_prefill(d["x"], d["w"], d["tails"][:n], d["states"][:n], d["beta"], d["g"], d["z"], d["nw"],
+                          d["cu"], **d["kw"])
+    np.testing.assert_array_equal(out["y"], ref["y"])
+    np.testing.assert_array_equal(states[:n], ref["state"])
+    np.testing.assert_array_equal(tails[:n], ref["tail"])
+    np.testing.assert_array_equal(states[n:], d["states"][n:])   # slots no sequence names
+
+
+def test_mixed_decode_tokens_equal_decode_step():
+    # sequences of length 1 are decode tokens: equal to the decode step on those requests
+    d = _mixed_case(32, [1, 1, 1], t_pad=2)
+    slots = [4, 0, 2]
+    out, tails, states = _run_mixed(d, slots, None)
+    tails2, states2 = d["tails"].copy(), d["states"].copy()
+    ref = R.mixer_decode_step(d["x"][:3], d["w"], tails2, states2, d["beta"][:3], d["g"][:3], d["z"][:3],
+                              d["nw"], slots, **d["kw"])
+    np.testing.assert_allclose(out["y"][:3], ref["y"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(states, states2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(tails, tails2)
+    assert np.all(np.isnan(out["y"][3:]))                          # padding rows are not written
+
+
+def test_mixed_fresh_reads_nothing_inactive_writes_nothing():
+    d = _mixed_case(33, [6, 1, 4, 0], t_pad=4)
+    slots = [1, 3, -1, 0]
+    fresh = [1, 0, 0, 1]
+    tails, states = d["tails"].copy(), d["states"].copy()
+    tails[1] = np.nan
+    states[1] = np.nan          # a fresh slot's old contents must not be read
+    out, tails, states = _run_mixed(d, slots, fresh, tails, states)
+    # sequence 0 from zero history and state
+    a, b = d["cu"][0], d["cu"][1]
+    ref = R.mixer_prefill(d["x"][a:b], d["w"], np.zeros((1, 3, d["x"].shape[1])),
+                          np.zeros((1,) + d["states"].shape[1:]), d["beta"][a:b], d["g"][a:b], d["z"][a:b],
+                          d["nw"], [0, b - a], **d["kw"])
+    np.testing.assert_array_equal(out["y"][a:b], ref["y"])
+    np.testing.assert_array_equal(states[1], ref["state"][0])
+    np.testing.assert_array_equal(tails[1], ref["tail"][0])
+    # inactive sequence 2: rows unwritten; slots 2 and 4 (named by no active sequence) untouched
+    a, b = d["cu"][2], d["cu"][3]
+    assert np.all(np.isnan(out["y"][a:b])) and np.all(np.isnan(out["y"][d["cu"][-1]:]))
+    for p in (2, 4, 5, 6):
+        np.testing.assert_array_equal(states[p], d["states"][p])
+        np.testing.assert_array_equal(tails[p], d["tails"][p])
+    # fresh zero-length sequence 3: its slot becomes the zero state and history
+    assert np.all(states[0] == 0.0) and np.all(tails[0] == 0.0)
+
+
+def test_mixed_slot_permutation_and_continuation():
+    d = _mixed_case(34, [9, 1, 5], t_pad=0)
+    out, tails, states = _run_mixed(d, [0, 1, 2], None)
+    perm = [3, 0, 5]
+    tails_p, states_p = d["tails"].copy(), d["states"].copy()
+    tails_p[perm] = d["tails"][[0, 1, 2]]
+    states_p[perm] = d["states"][[0, 1, 2]]
+    out_p, tails_p, states_p = _run_mixed(d, perm, None, tails_p, states_p)
+    np.testing.assert_array_equal(out_p["y"], out["y"])
+    np.testing.assert_array_equal(states_p[perm], states[[0, 1, 2]])
+    np.testing.assert_array_equal(tails_p[perm], tails[[0, 1, 2]])
+    # a prompt split over two batches continues through its pool row exactly
+    d1 = dict(d)
+    cut = 4
+    d1["cu"] = np.array([0, cut]); d1["x"] = d["x"][:cut]; d1["g"] = d["g"][:cut]
+    d1["beta"] = d["beta"][:cut]; d1["z"] = d["z"][:cut]
+    o1, t1, s1 = _run_mixed(d1, [0], None)
+    d2 = dict(d)
+    d2["cu"] = np.array([0, 9 - cut]); d2["x"] = d["x"][cut:9]; d2["g"] = d["g"][cut:9]
+    d2["beta"] = d["beta"][cut:9]; d2["z"] = d["z"][cut:9]
+    o2, t2, s2 = _run_mixed(d2, [0], None, t1, s1)
+    np.testing.assert_array_equal(np.concatenate([o1["y"], o2["y"]]), out["y"][:9])
+    np.testing.assert_array_equal(s2[0], states[0])
+    np.testing.assert_array_equal(t2[0], tails[0])
