@@ -51,10 +51,10 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (289_247_337, {"chunk.hip": "a0aa61ff5966bb39", "common.hpp": "f5db633bc62a5de3",
-                                    "launch.hpp": "206799c280670c13"}),
-    "gdn_recurrent_step": (270_943_882, {"recurrent.hip": "c93c24b454d423ec", "common.hpp": "f5db633bc62a5de3",
-                                         "launch.hpp": "206799c280670c13"}),
+    "gdn_chunk_fwd": (289_254_400, {"chunk.hip": "380d3d12f94df6eb", "common.hpp": "c3ca3f5184368cb5",
+                                    "launch.hpp": "28d1c5ce5d3030f8"}),
+    "gdn_recurrent_step": (270_940_979, {"recurrent.hip": "1d3c270c78d3c8ea", "common.hpp": "c3ca3f5184368cb5",
+                                         "launch.hpp": "28d1c5ce5d3030f8"}),
 }
 
 
@@ -74,8 +74,8 @@ def measured_traffic(entry):
 # traffic above.
 MEASURED_MFMA = {
     "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
-                      {"chunk.hip": "a0aa61ff5966bb39", "common.hpp": "f5db633bc62a5de3",
-                       "launch.hpp": "206799c280670c13"}),
+                      {"chunk.hip": "380d3d12f94df6eb", "common.hpp": "c3ca3f5184368cb5",
+                       "launch.hpp": "28d1c5ce5d3030f8"}),
 }
 
 
