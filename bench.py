@@ -120,6 +120,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent buffer sets rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the speculative-verification and mixed prefill-plus-decode timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before the timed legs, copy 256 MiB device-to-device once (a plain copy of known "
                          "size that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -254,6 +256,87 @@ def decode_leg(args, torch, np, ops, I):
                 small=small, ms_rec_gated=ms_rec_gated)
 
 
+def serving_leg(args, torch, np, ops, I):
+    """Speculative verification (64 requests x 4 draft tokens, eight checkpoint
+    columns per request, then restoring an accepted prefix) and one mixed
+    prefill-plus-decode batch (four 1024-token prompt chunks, two of them fresh,
+    and 60 decode tokens over pools of 128 slots), both with the fused norm and
+    bf16 outputs, on one buffer set."""
+    lay = I.MODEL_LAYOUT
+    dev = "cuda:0"
+
+    def up(a, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dt).to(dev)
+
+    n_req, w_tok, n_cols = 64, 4, 8
+    d = I.decode_inputs(5, lay, n_req, w_tok)
+    rows = n_req * w_tok
+    # request r's tokens are rows r * W .. r * W + W - 1
+    x = up(d["x"].transpose(1, 0, 2).reshape(rows, -1), torch.bfloat16)
+    g = up(d["g"].transpose(1, 0, 2).reshape(rows, -1))
+    beta = up(d["beta"].transpose(1, 0, 2).reshape(rows, -1))
+    z = up(d["z"].transpose(1, 0, 2, 3).reshape(rows, lay.h_v, lay.d_v), torch.bfloat16)
+    state = up(d["state"])
+    tail = up(d["tail"], torch.bfloat16)
+    w = up(d["conv_w"], torch.bfloat16)
+    nw = up(d["norm_w"])
+    ckpt = torch.empty((n_req, n_cols) + tuple(state.shape[1:]), device=dev)
+    win = torch.empty((n_req, n_cols, 3, lay.channels), dtype=torch.bfloat16, device=dev)
+    y_conv = torch.empty((rows, lay.channels), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((rows, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev)
+    q, k, v = ops.qkv_views(y_conv, lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+    live = torch.arange(n_req, dtype=torch.int32, device=dev)
+    accepted = (live * n_cols + 1).to(torch.int32)   # column 1: two of the four tokens accepted
+    ckpt_rows = ckpt.view(n_req * n_cols, *state.shape[1:])
+
+    def verify(i):
+        ops.gdn_conv1d_verify(x, w, tail, y_conv, win, n_tok=w_tok)
+        ops.gdn_recurrent_verify(q, k, v, g, beta, state, ckpt, o, n_tok=w_tok, z=z, norm_w=nw)
+
+    def rec_verify(i):
+        ops.gdn_recurrent_verify(q, k, v, g, beta, state, ckpt, o, n_tok=w_tok, z=z, norm_w=nw)
+
+    def restore(i):
+        ops.gdn_state_rows_copy(state, live, ckpt_rows, accepted)
+
+    ms_verify, _ = timed(verify, args.steps, args.warmup, torch)
+    ms_rec_verify, _ = timed(rec_verify, args.steps, args.warmup, torch)
+    ms_restore, _ = timed(restore, args.steps, args.warmup, torch)
+    del ckpt, win, d
+
+    # mixed batch: sequences 0-3 prompt chunks (0 and 2 fresh), 4-63 single decode tokens
+    lengths = [1024] * 4 + [1] * 60
+    n_slots = 128
+    m = I.mixed_batch_inputs(6, lay, lengths, n_slots)
+    slots = np.random.default_rng(7).permutation(n_slots)[:len(lengths)].astype(np.int32)
+    fresh = np.zeros(len(lengths), np.int32)
+    fresh[[0, 2]] = 1
+    t_cap = m["t_cap"]
+    mx = up(m["x"], torch.bfloat16)
+    mw = up(m["conv_w"], torch.bfloat16)
+    mtail = up(m["tail_pool"], torch.bfloat16)
+    mstate = up(m["state_pool"])
+    cu = torch.from_numpy(m["cu_seqlens"]).to(dev)
+    sl, fr = torch.from_numpy(slots).to(dev), torch.from_numpy(fresh).to(dev)
+    mg, mb = up(m["g"]), up(m["beta"])
+    mz, mnw = up(m["z"], torch.bfloat16), up(m["norm_w"])
+    my_conv = torch.empty((t_cap, lay.channels), dtype=torch.bfloat16, device=dev)
+    mq, mk, mv = ops.qkv_views(my_conv, lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+    my = torch.empty((t_cap, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(ops.gdn_chunk_fwd_workspace_size(lay.h_qk, lay.h_v, lay.d_k, lay.d_v, lay.chunk, len(lengths),
+                                                      t_cap, torch.bfloat16, True), dtype=torch.uint8, device=dev)
+
+    def mixed(i):
+        ops.gdn_conv1d_mixed(mx, mw, mtail, my_conv, cu_seqlens=cu, state_slots=sl, fresh=fr)
+        ops.gdn_chunk_mixed(mq, mk, mv, mg, mb, mstate, my, chunk=lay.chunk, cu_seqlens=cu, state_slots=sl,
+                            fresh=fr, z=mz, norm_w=mnw, workspace=ws)
+
+    ms_mixed, _ = timed(mixed, args.steps, args.warmup, torch)
+    state_bytes = n_req * lay.h_v * lay.d_v * lay.d_k * 4
+    return dict(n_req=n_req, w_tok=w_tok, ms_verify=ms_verify, ms_rec_verify=ms_rec_verify, ms_restore=ms_restore,
+                state_bytes=state_bytes, lengths=lengths, ms_mixed=ms_mixed, t_live=int(sum(lengths)))
+
+
 def cpu_baseline(np, I, R):
     """Float64 oracle (conv -> gated delta rule -> gated norm) on the whole
     prefill workload (4096 tokens, all 32 v-heads), single thread."""
@@ -360,6 +443,26 @@ def main():
     if not args.no_decode:
         out["fused_gates"]["recurrent_step_ms"] = round(dc["ms_rec_gated"], 4)
         out["fused_gates"]["recurrent_step_vs_plain"] = round(dc["ms_rec_gated"] / dc["ms_rec"], 4)
+    if not args.no_serving:
+        sv = serving_leg(args, torch, np, ops, I)
+        # recurrent verify: the live state read once, W checkpoint columns written
+        vbytes = sv["state_bytes"] * (1 + sv["w_tok"])
+        vgbs = vbytes / (sv["ms_rec_verify"] * 1e-3) / 1e9
+        out["serving"] = {
+            "verify": {"workload": f"{sv['n_req']} requests x {sv['w_tok']} draft tokens, eight checkpoint columns, "
+                                   "fused norm, bf16 outputs",
+                       "ms_per_round": round(sv["ms_verify"], 4),
+                       "gdn_recurrent_verify_ms": round(sv["ms_rec_verify"], 4),
+                       "gdn_recurrent_verify_state_GB_per_s": round(vgbs, 1),
+                       "frac_hbm_peak": round(vgbs / PEAK_HBM_GBS, 4),
+                       "restore_ms": round(sv["ms_restore"], 4),
+                       "restore_GB_per_s": round(2 * sv["state_bytes"] / (sv["ms_restore"] * 1e-3) / 1e9, 1)},
+            "mixed": {"workload": "one batch: 4 prompt chunks x 1024 tokens (2 fresh) + 60 decode tokens, "
+                                  "slot-mapped pools of 128 rows, conv + chunked rule + fused norm, bf16 outputs",
+                      "ms_per_batch": round(sv["ms_mixed"], 4),
+                      "tokens_per_s": round(sv["t_live"] / (sv["ms_mixed"] * 1e-3), 1)},
+            "buffer_sets": 1,
+        }
     if not args.no_cpu_baseline:
         from oracle import gdn_ref as R
         out["cpu_baseline"] = cpu_baseline(np, I, R)
