@@ -352,6 +352,8 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
   do {                                                                                                 \
     n_ok = (uu) < n_units && locate_block(cu, n_seq, t_total, C, (uu) / h_qk, n_seq_i, n_t0, n_len);     \
     if (n_ok && seq_slots) n_ok = seq_slots[n_seq_i] >= 0;   /* inactive lane: no scan reads it */        \
+    if (n_ok && n_len == 1)   /* a one-token sequence: the scan runs the plain recurrence */             \
+      n_ok = seq_start(cu, n_seq_i + 1, t_total) - seq_start(cu, n_seq_i, t_total) > 1;                  \
     if (n_ok) {                                                                                        \
       const int fq_ = static_cast<int>((uu) % h_qk);                                                   \
       _Pragma("unroll") for (int it = 0; it < NR; ++it) {                                              \
@@ -666,6 +668,99 @@ __global__ __launch_bounds__(kOrderBins) void k_seq_order(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
+// k_single_token: one-token sequences (the decode tokens of a mixed batch).
+// Their recurrence, a = exp(g), e = v - a S k^, S <- a S + beta e k^^T,
+// o = scale S q^, runs in fp32 on the vector units, as in the decode step:
+// SPLIT workgroups per (sequence, v-head), each over D / SPLIT state rows,
+// D / 8 lanes per row (columns 4l .. 4l+3 and D/2 + 4l ..).  The prep kernel
+// leaves these sequences out and the scan returns at once for them; every
+// other sequence returns here at once.  A separate launch keeps these light
+// workgroups off the scan's register and LDS footprint.
+// ---------------------------------------------------------------------------
+template <class In, class EO, int D, int NT, int SPLIT>
+__global__ __launch_bounds__(NT) void k_single_token(
+    const typename In::T* __restrict__ q, const typename In::T* __restrict__ k,
+    const typename In::T* __restrict__ v, int64_t q_stride, int64_t k_stride, int64_t v_stride, GateSrc gates,
+    float scale, int use_l2, float l2_eps, int h_qk, int h_v, const int32_t* __restrict__ cu, int n_seq,
+    int64_t t_total, const float* __restrict__ init, float* __restrict__ fin, const int32_t* __restrict__ slots,
+    const int32_t* __restrict__ fresh, typename EO::T* __restrict__ o) {
+  constexpr int TPR = D / 8, RPP = NT / TPR, RW = D / SPLIT, PASSES = (RW + RPP - 1) / RPP;
+  static_assert(TPR <= 64 && NT % 64 == 0 && D % SPLIT == 0, "row lanes within a wave");
+  const int part = static_cast<int>(blockIdx.x % SPLIT);
+  const int64_t sh = blockIdx.x / SPLIT;
+  const int s = static_cast<int>(sh / h_v), h = static_cast<int>(sh % h_v);
+  if (s >= n_seq) return;
+  const int64_t t = seq_start(cu, s, t_total);
+  if (seq_start(cu, s + 1, t_total) - t != 1) return;
+  const int sslot = slots ? slots[s] : s;
+  if (sslot < 0) return;
+  const float* src = (init != nullptr && !(fresh && fresh[s] != 0)) ? init : nullptr;
+  const int hq = h / (h_v / h_qk);
+  const int tid = threadIdx.x, l = tid % TPR, rg = tid / TPR;
+  const int ca = 4 * l, cb = D / 2 + 4 * l;
+  const int64_t smat = (static_cast<int64_t>(sslot) * h_v + h) * D * D;
+
+  float sv[PASSES][8], vv[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = part * RW + (rg + p * RPP < RW ? rg + p * RPP : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sv[p][i] = 0.f;
+    if (src) {
+      const float4 a4 = *reinterpret_cast<const float4*>(src + smat + static_cast<int64_t>(row) * D + ca);
+      const float4 b4 = *reinterpret_cast<const float4*>(src + smat + static_cast<int64_t>(row) * D + cb);
+      sv[p][0] = a4.x; sv[p][1] = a4.y; sv[p][2] = a4.z; sv[p][3] = a4.w;
+      sv[p][4] = b4.x; sv[p][5] = b4.y; sv[p][6] = b4.z; sv[p][7] = b4.w;
+    }
+    vv[p] = In::load(v + t * v_stride + static_cast<int64_t>(h) * D, row);
+  }
+  float kk[8], qq[8];
+  const typename In::T* kr = k + t * k_stride + static_cast<int64_t>(hq) * D;
+  const typename In::T* qr = q + t * q_stride + static_cast<int64_t>(hq) * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kk[i] = In::load(kr, ca + i);
+    kk[4 + i] = In::load(kr, cb + i);
+    qq[i] = In::load(qr, ca + i);
+    qq[4 + i] = In::load(qr, cb + i);
+  }
+  float gv, bt;
+  load_gate(gates, t, h, h_v, gv, bt);
+  float sk = 0.f, sq = 0.f, kq = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
+  sk = group_sum<TPR>(sk);
+  sq = group_sum<TPR>(sq);
+  kq = group_sum<TPR>(kq);
+  const float rk = use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f;
+  const float rq = use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { kk[i] *= rk; qq[i] *= rq; }
+  kq *= rk * rq;
+  const float alpha = __expf(gv);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    float dk = 0.f, dq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { dk += sv[p][i] * kk[i]; dq += sv[p][i] * qq[i]; }
+    dk = group_sum<TPR>(dk);
+    dq = group_sum<TPR>(dq);
+    const float e = vv[p] - alpha * dk, be = bt * e;
+    if (rg + p * RPP < RW) {
+      const int64_t row = part * RW + rg + p * RPP;
+      if (fin) {
+        float nv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) nv[i] = alpha * sv[p][i] + be * kk[i];
+        *reinterpret_cast<float4*>(fin + smat + row * D + ca) = make_float4(nv[0], nv[1], nv[2], nv[3]);
+        *reinterpret_cast<float4*>(fin + smat + row * D + cb) = make_float4(nv[4], nv[5], nv[6], nv[7]);
+      }
+      if (l == 0) EO::store(o, (t * h_v + h) * static_cast<int64_t>(D) + row, scale * (alpha * dq + be * kq));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_chunk_scan: one workgroup per (sequence, v-head, d_v slice of 16*NV)
 // ---------------------------------------------------------------------------
 template <class Pol, class EO, int D, int C, int NV>
@@ -734,6 +829,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(
   const int h = static_cast<int>(lid / NTILE);
   const int hq = h / (h_v / h_qk);
   const int dv0 = tile * BV;
+  // one-token sequences belong to k_single_token
+  if (seq_start(cu, s + 1, t_total) - seq_start(cu, s, t_total) == 1) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -1101,6 +1198,30 @@ static hipError_t run_chunk(const ChunkArgs& a) {
   }
   if (ws.order) {
     hipLaunchKernelGGL(k_seq_order, dim3(1), dim3(kOrderBins), 0, st, a.cu, a.n_seq, C, ws.order);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // One-token sequences: skipped only when a single sequence holds all of
+  // several tokens (cu_seqlens ends at t_total, so it has no one-token
+  // sequence); in a mixed call t_total is a capacity.
+  if (a.n_seq > 1 || a.t_total == 1 || a.slots != nullptr) {
+    constexpr int NT1 = D == 128 ? 256 : 64, SPL = D == 128 ? 4 : 1;
+    using In = typename Pol::In;
+    const int64_t nb1 = static_cast<int64_t>(a.n_seq) * a.h_v * SPL;
+    float* const fin1 = a.fin;
+    if (a.z)
+      hipLaunchKernelGGL((k_single_token<In, F32, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
+                         q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk,
+                         a.h_v, a.cu, a.n_seq, a.t_total, a.init, fin1, a.slots, a.fresh, o_pre);
+    else if (a.o_dt == GDN_BF16)
+      hipLaunchKernelGGL((k_single_token<In, BF16, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0,
+                         st, q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps,
+                         a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total, a.init, fin1, a.slots, a.fresh,
+                         static_cast<uint16_t*>(a.o));
+    else
+      hipLaunchKernelGGL((k_single_token<In, F32, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
+                         q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk,
+                         a.h_v, a.cu, a.n_seq, a.t_total, a.init, fin1, a.slots, a.fresh, static_cast<float*>(a.o));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
