@@ -51,9 +51,9 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (289_254_400, {"chunk.hip": "380d3d12f94df6eb", "common.hpp": "c3ca3f5184368cb5",
+    "gdn_chunk_fwd": (289_238_426, {"chunk.hip": "d4c6aa709200f2f4", "common.hpp": "c3ca3f5184368cb5",
                                     "launch.hpp": "28d1c5ce5d3030f8"}),
-    "gdn_recurrent_step": (270_940_979, {"recurrent.hip": "1d3c270c78d3c8ea", "common.hpp": "c3ca3f5184368cb5",
+    "gdn_recurrent_step": (274_537_779, {"recurrent.hip": "bd5d394eb0b8a939", "common.hpp": "c3ca3f5184368cb5",
                                          "launch.hpp": "28d1c5ce5d3030f8"}),
 }
 
@@ -74,7 +74,7 @@ def measured_traffic(entry):
 # traffic above.
 MEASURED_MFMA = {
     "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
-                      {"chunk.hip": "380d3d12f94df6eb", "common.hpp": "c3ca3f5184368cb5",
+                      {"chunk.hip": "d4c6aa709200f2f4", "common.hpp": "c3ca3f5184368cb5",
                        "launch.hpp": "28d1c5ce5d3030f8"}),
 }
 
