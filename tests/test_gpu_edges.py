@@ -46,11 +46,12 @@ def _run(ops, layout, q, k, v, g, beta, cu, state0, *, scale=1.0, z=None, nw=Non
 
 
 def test_chunk_f32_d128(ops):
-    """fp32 inputs at d=128, chunk 64 (fp32 matrix cores), three sequences
-    with ragged tails and nonzero states, model-like decays."""
+    """fp32 inputs at d=128, chunk 64 (fp32 matrix cores), four sequences
+    with ragged tails and nonzero states, model-like decays; the one-token
+    sequence runs in the one-token kernel."""
     lay = I.Layout(h_qk=2, h_v=4, d_k=128, d_v=128, chunk=64, dtype="f32")
     note("chunk fp32 d=128")
-    d = I.prefill_inputs(31, lay, [150, 7, 64], state_std=0.02)
+    d = I.prefill_inputs(31, lay, [150, 7, 1, 64], state_std=0.02)
     q, k, v = I.split_qkv(d["x"], lay)
     o, fin = _run(ops, lay, q, k, v, d["g"], d["beta"], d["cu_seqlens"], d["state"])
     o_ref, f_ref = R.gated_delta_rule(q, k, v, d["g"], d["beta"], initial_state=d["state"],
