@@ -518,6 +518,75 @@ gdn_status gdn_chunk_mixed(const void* q, const void* k, const void* v, int64_t 
                         norm_w, norm_eps, workspace, ws_bytes, stream, state_slots, fresh, n_slots);
 }
 
+gdn_status gdn_chunk_bwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t n_seq,
+                                        int64_t t_total, size_t* bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  if (h_qk <= 0 || h_v <= 0 || h_v % h_qk != 0 || n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
+  if (!((d_k == 128 && d_v == 128) || (d_k == 16 && d_v == 16))) return GDN_ERR_UNSUPPORTED;
+  *bytes = gdn::bwd_ws_bytes(h_v, d_v, n_seq, t_total);
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                         int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                         int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                         const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total, const float* initial_state,
+                         const float* d_o, const float* d_final, float* dq, float* dk, float* dv, float* dg,
+                         float* dbeta, float* d_initial, void* workspace, size_t ws_bytes, void* stream) {
+  if (n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
+  if (n_seq == 0) return GDN_OK;
+  if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
+  if (dt == GDN_BF16 && d_k != 128) return GDN_ERR_UNSUPPORTED;
+  gdn_status st = check_qkv(q, k, v, q_stride, k_stride, v_stride, dt, !g || !beta, h_qk, h_v, d_k, d_v,
+                            t_total > 0);
+  if (st != GDN_OK) return st;
+  Gates gt;
+  st = check_gates(plain_gates(g, beta), t_total, h_v, gt);
+  if (st != GDN_OK) return st;
+  if (t_total > 0 && (!d_o || !dq || !dk || !dv || !dg || !dbeta)) return GDN_ERR_NULL;
+  if (!cu_seqlens && n_seq != 1) return GDN_ERR_NULL;
+  if (!workspace) return GDN_ERR_WORKSPACE;
+  size_t need = 0;
+  st = gdn_chunk_bwd_workspace_size(h_qk, h_v, d_k, d_v, n_seq, t_total, &need);
+  if (st != GDN_OK) return st;
+  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (!all_aligned({initial_state, d_o, d_final, dq, dk, dv, dg, dbeta, d_initial, workspace, cu_seqlens}))
+    return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const uint64_t state_bytes = static_cast<uint64_t>(n_seq) * h_v * d_v * d_k * 4;
+  const Range rq{q, strided_bytes(t_total, q_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rk{k, strided_bytes(t_total, k_stride, static_cast<int64_t>(h_qk) * d_k, eb)};
+  const Range rv{v, strided_bytes(t_total, v_stride, static_cast<int64_t>(h_v) * d_v, eb)};
+  const Range ri{initial_state, initial_state ? state_bytes : 0};
+  const Range rdo{d_o, static_cast<uint64_t>(t_total) * h_v * d_v * 4};
+  const Range rdf{d_final, d_final ? state_bytes : 0};
+  const Range rcu{cu_seqlens, cu_seqlens ? static_cast<uint64_t>(n_seq + 1) * 4 : 0};
+  const Range rws{workspace, need};
+  const Range outs[] = {{dq, static_cast<uint64_t>(t_total) * h_qk * d_k * 4},
+                        {dk, static_cast<uint64_t>(t_total) * h_qk * d_k * 4},
+                        {dv, static_cast<uint64_t>(t_total) * h_v * d_v * 4},
+                        {dg, static_cast<uint64_t>(t_total) * h_v * 4},
+                        {dbeta, static_cast<uint64_t>(t_total) * h_v * 4},
+                        {d_initial, d_initial ? state_bytes : 0},
+                        rws};
+  for (const Range& o : outs) {
+    if (!disjoint(o, {rq, rk, rv, ri, rdo, rdf, rcu}) || !disjoint_gates(o, gt)) return GDN_ERR_ALIAS;
+    for (const Range& o2 : outs)
+      if (&o != &o2 && overlap(o, o2)) return GDN_ERR_ALIAS;
+  }
+  gdn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v;
+  a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride;
+  a.dt = dt; a.gate = gt.src; a.scale = scale;
+  a.use_l2 = use_qk_l2norm != 0; a.l2_eps = l2_eps;
+  a.h_qk = h_qk; a.h_v = h_v; a.d = d_k;
+  a.cu = cu_seqlens; a.n_seq = n_seq; a.t_total = t_total;
+  a.init = initial_state; a.d_o = d_o; a.d_final = d_final;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.d_init = d_initial;
+  a.workspace = workspace; a.stream = stream;
+  return finish(gdn::launch_chunk_bwd(a));
+}
+
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w, float eps,
                              int64_t rows, int32_t d, void* y, gdn_dtype y_dt, void* stream) {
   if (rows < 0) return GDN_ERR_INVALID;

@@ -1,0 +1,477 @@
+// Backward of the gated delta rule (gfx950), from chunk-boundary states.
+//
+// Forward, per sequence and v-head with fp32 state S (d_v x d_k) and each
+// token t (k^, q^ the L2-normalised keys and queries):
+//     S' = a S,  e = v - S' k^,  S_t = S' + beta e k^^T,  o_t = scale S_t q^
+// (the gated delta rule of the GDN layers: haskell-infer-demo README,
+// "Highlights" and "Architecture"/fla_gdn.cu).  With G = dL/dS_t the reverse
+// step is, token by token from the last:
+//     G   += scale do_t q^^T                 dq^_t = scale S_t^T do_t
+//     u    = G k^                            dv_t  = beta u,  dbeta_t = e . u
+//     dk^_t = beta (G^T e - S'^T u)
+//     dS'  = G - beta u k^^T                 dg_t  = <dS', S'>
+//     G    = a dS'                           (dL/dS_{t-1})
+// and dL/dS_0 is the G left after the first token.  Each row of S evolves
+// on its own, so the state is split into 16-row slices; dq^, dk^, dbeta and dg
+// are sums over all rows, formed per slice and added up by a final kernel,
+// which also takes dq^, dk^ back through the L2 normalisation.
+//
+// Kernels:
+//   k_bwd_ckpt    forward over each sequence, writing the state entering
+//                 every 64-token chunk (per slice) to the workspace.
+//   k_bwd_slice   per (sequence, v-head, 16-row slice), chunks last to
+//                 first; inside a chunk, 16-token sub-blocks last to first:
+//                 recompute from the chunk's checkpoint up to the sub-block,
+//                 keeping the state before each of its tokens in LDS, then
+//                 run the reverse step over its tokens.  A sub-block's
+//                 inputs (normalised k, q; v, do of the slice; a, beta) are
+//                 staged in LDS first.
+//   k_bwd_reduce  per (token, q/k head): sums the slice partials over the
+//                 slices and the v-heads that read this q/k head, applies the
+//                 L2-norm backward dx = (dx^ - x^ (x^ . dx^)) / |x|_eps, and
+//                 sums dbeta, dg over slices.
+// All sums run in a fixed order: reruns are bitwise identical.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gdn {
+
+constexpr int kBwdRows = 16;    // state rows per workgroup
+constexpr int kBwdSub = 16;     // tokens per staged sub-block
+constexpr int kBwdChunk = 64;   // tokens between checkpoints
+
+// Workspace carve-up (floats):
+//   ckpt [slots][h_v][D][D]          state entering each 64-token chunk
+//   pdq, pdk [T][h_v][D/16][D]       slice partials of dq^, dk^
+//   pdb, pdg [T][h_v][D/16]          slice partials of dbeta, dg
+struct BwdWs {
+  float* ckpt;
+  float* pdq;
+  float* pdk;
+  float* pdb;
+  float* pdg;
+};
+
+static size_t bwd_al(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t bwd_ws_bytes(int h_v, int d, int n_seq, int64_t t_total) {
+  const int64_t slots = block_slots(t_total, n_seq, kBwdChunk);
+  const int tiles = d / kBwdRows;
+  return bwd_al(sizeof(float) * slots * h_v * d * d) + 2 * bwd_al(sizeof(float) * t_total * h_v * tiles * d) +
+         2 * bwd_al(sizeof(float) * t_total * h_v * tiles);
+}
+
+static BwdWs bwd_carve(void* base, int h_v, int d, int n_seq, int64_t t_total) {
+  const int64_t slots = block_slots(t_total, n_seq, kBwdChunk);
+  const int tiles = d / kBwdRows;
+  char* b = static_cast<char*>(base);
+  BwdWs w;
+  w.ckpt = reinterpret_cast<float*>(b);
+  b += bwd_al(sizeof(float) * slots * h_v * d * d);
+  w.pdq = reinterpret_cast<float*>(b);
+  b += bwd_al(sizeof(float) * t_total * h_v * tiles * d);
+  w.pdk = reinterpret_cast<float*>(b);
+  b += bwd_al(sizeof(float) * t_total * h_v * tiles * d);
+  w.pdb = reinterpret_cast<float*>(b);
+  b += bwd_al(sizeof(float) * t_total * h_v * tiles);
+  w.pdg = reinterpret_cast<float*>(b);
+  return w;
+}
+
+// Inputs of one sub-block, staged in LDS.
+template <int D>
+struct BwdStage {
+  float k[kBwdSub][D];          // normalised keys
+  float q[kBwdSub][D];          // normalised queries
+  float v[kBwdSub][kBwdRows];   // v of the slice's rows
+  float dov[kBwdSub][kBwdRows]; // do of the slice's rows
+  float a[kBwdSub];             // exp(g)
+  float b[kBwdSub];             // beta
+};
+
+// Stage tokens t0 .. t0 + n - 1 (n <= kBwdSub).  Thread layout: token
+// tid / TPR, columns 4l .. 4l+3 and D/2 + 4l .. of it (l = tid % TPR), the same
+// layout as the state rows, so the norms are TPR-lane sums.
+template <class In, int D, int NT>
+__device__ __forceinline__ void bwd_stage(BwdStage<D>& sm, const typename In::T* __restrict__ q,
+                                          const typename In::T* __restrict__ k,
+                                          const typename In::T* __restrict__ v, const float* __restrict__ dout,
+                                          int64_t q_stride, int64_t k_stride, int64_t v_stride, const GateSrc& gates,
+                                          int use_l2, float l2_eps, int h_v, int h, int hq, int dv0, int64_t t0, int n,
+                                          bool with_q) {
+  constexpr int TPR = D / 8;
+  const int tid = threadIdx.x;
+  const int j = tid / TPR, l = tid % TPR;
+  const int ca = 4 * l, cb = D / 2 + 4 * l;
+  if (j < kBwdSub) {
+    const int64_t t = t0 + (j < n ? j : 0);
+    float kk[8], qq[8];
+    const typename In::T* kr = k + t * k_stride + static_cast<int64_t>(hq) * D;
+    const typename In::T* qr = q + t * q_stride + static_cast<int64_t>(hq) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kk[i] = In::load(kr, ca + i);
+      kk[4 + i] = In::load(kr, cb + i);
+      qq[i] = with_q ? In::load(qr, ca + i) : 0.f;
+      qq[4 + i] = with_q ? In::load(qr, cb + i) : 0.f;
+    }
+    float sk = 0.f, sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; }
+    sk = group_sum<TPR>(sk);
+    sq = group_sum<TPR>(sq);
+    const float rk = use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f;
+    const float rq = use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sm.k[j][ca + i] = kk[i] * rk;
+      sm.k[j][cb + i] = kk[4 + i] * rk;
+      sm.q[j][ca + i] = qq[i] * rq;
+      sm.q[j][cb + i] = qq[4 + i] * rq;
+    }
+  }
+  for (int e = tid; e < kBwdSub * kBwdRows; e += NT) {
+    const int jj = e / kBwdRows, r = e % kBwdRows;
+    const int64_t t = t0 + (jj < n ? jj : 0);
+    sm.v[jj][r] = In::load(v + t * v_stride + static_cast<int64_t>(h) * D, dv0 + r);
+    sm.dov[jj][r] = dout ? dout[(t * h_v + h) * static_cast<int64_t>(D) + dv0 + r] : 0.f;
+  }
+  if (tid < kBwdSub) {
+    const int64_t t = t0 + (tid < n ? tid : 0);
+    float gv, bt;
+    load_gate(gates, t, h, h_v, gv, bt);
+    sm.a[tid] = __expf(gv);
+    sm.b[tid] = bt;
+  }
+}
+
+// One forward token on this thread's 8 state values (row r): S <- a S + beta e k^,
+// e = v_r - a (S . k^).
+template <int D>
+__device__ __forceinline__ void bwd_fwd_token(float (&s)[8], const BwdStage<D>& sm, int j, int r, int ca, int cb) {
+  constexpr int TPR = D / 8;
+  float kk[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { kk[i] = sm.k[j][ca + i]; kk[4 + i] = sm.k[j][cb + i]; }
+  float dk = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dk += s[i] * kk[i];
+  dk = group_sum<TPR>(dk);
+  const float a = sm.a[j];
+  const float be = sm.b[j] * (sm.v[j][r < kBwdRows ? r : 0] - a * dk);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = a * s[i] + be * kk[i];
+}
+
+template <class In, int D, int NT>
+__global__ __launch_bounds__(NT) void k_bwd_ckpt(
+    const typename In::T* __restrict__ q, const typename In::T* __restrict__ k, const typename In::T* __restrict__ v,
+    int64_t q_stride, int64_t k_stride, int64_t v_stride, GateSrc gates, int use_l2, float l2_eps, int h_qk,
+    int h_v, const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const float* __restrict__ init, BwdWs ws) {
+  constexpr int TPR = D / 8, TILES = D / kBwdRows;
+  static_assert(NT >= kBwdRows * TPR && NT % 64 == 0, "one thread per (row, lane)");
+  __shared__ BwdStage<D> sm;
+  const int64_t b = blockIdx.x;
+  const int s = static_cast<int>(b / (static_cast<int64_t>(h_v) * TILES));
+  const int h = static_cast<int>((b / TILES) % h_v), tile = static_cast<int>(b % TILES);
+  if (s >= n_seq) return;
+  const int hq = h / (h_v / h_qk), dv0 = tile * kBwdRows;
+  const int tid = threadIdx.x, r = tid / TPR, l = tid % TPR;
+  const int ca = 4 * l, cb = D / 2 + 4 * l;
+  const bool row_ok = r < kBwdRows;
+  const int64_t start = seq_start(cu, s, t_total), end = seq_start(cu, s + 1, t_total);
+  const int64_t srow = (static_cast<int64_t>(s) * h_v + h) * D * D + static_cast<int64_t>(dv0 + (row_ok ? r : 0)) * D;
+  float st[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (init && row_ok) {
+    const float4 x = *reinterpret_cast<const float4*>(init + srow + ca);
+    const float4 y = *reinterpret_cast<const float4*>(init + srow + cb);
+    st[0] = x.x; st[1] = x.y; st[2] = x.z; st[3] = x.w; st[4] = y.x; st[5] = y.y; st[6] = y.z; st[7] = y.w;
+  }
+  const int64_t slot0 = start / kBwdChunk + s;
+  for (int64_t c0 = start; c0 < end; c0 += kBwdChunk) {
+    const int64_t slot = slot0 + (c0 - start) / kBwdChunk;
+    if (row_ok) {
+      float* dst = ws.ckpt + (slot * h_v + h) * static_cast<int64_t>(D) * D + static_cast<int64_t>(dv0 + r) * D;
+      *reinterpret_cast<float4*>(dst + ca) = make_float4(st[0], st[1], st[2], st[3]);
+      *reinterpret_cast<float4*>(dst + cb) = make_float4(st[4], st[5], st[6], st[7]);
+    }
+    const int64_t c1 = c0 + kBwdChunk < end ? c0 + kBwdChunk : end;
+    for (int64_t t0 = c0; t0 < c1; t0 += kBwdSub) {
+      const int n = static_cast<int>(c1 - t0 < kBwdSub ? c1 - t0 : kBwdSub);
+      bwd_stage<In, D, NT>(sm, q, k, v, nullptr, q_stride, k_stride, v_stride, gates, use_l2, l2_eps, h_v, h, hq,
+                           dv0, t0, n, false);
+      __syncthreads();
+      for (int j = 0; j < n; ++j) bwd_fwd_token<D>(st, sm, j, r, ca, cb);
+      __syncthreads();
+    }
+  }
+}
+
+template <class In, int D, int NT>
+__global__ __launch_bounds__(NT) void k_bwd_slice(
+    const typename In::T* __restrict__ q, const typename In::T* __restrict__ k, const typename In::T* __restrict__ v,
+    int64_t q_stride, int64_t k_stride, int64_t v_stride, GateSrc gates, float scale, int use_l2, float l2_eps,
+    int h_qk, int h_v, const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const float* __restrict__ dout,
+    const float* __restrict__ dfin, float* __restrict__ dv_out, float* __restrict__ dinit, BwdWs ws) {
+  constexpr int TPR = D / 8, TILES = D / kBwdRows;
+  static_assert(NT >= kBwdRows * TPR && NT % 64 == 0, "one thread per (row, lane)");
+  static_assert(NT >= D, "one thread per column in the row reductions");
+  __shared__ BwdStage<D> sm;
+  __shared__ float stash[kBwdSub][kBwdRows][D];   // state before each token of the sub-block
+  constexpr int NW = NT / 64;
+  __shared__ float red_q[NW][D];                   // per-wave column sums
+  __shared__ float red_k[NW][D];
+  __shared__ float red_s[NW][2];
+  const int64_t b = blockIdx.x;
+  const int s = static_cast<int>(b / (static_cast<int64_t>(h_v) * TILES));
+  const int h = static_cast<int>((b / TILES) % h_v), tile = static_cast<int>(b % TILES);
+  if (s >= n_seq) return;
+  const int hq = h / (h_v / h_qk), dv0 = tile * kBwdRows;
+  const int tid = threadIdx.x, r = tid / TPR, l = tid % TPR;
+  const int ca = 4 * l, cb = D / 2 + 4 * l;
+  const bool row_ok = r < kBwdRows;
+  const int rr = row_ok ? r : 0;
+  const int64_t start = seq_start(cu, s, t_total), end = seq_start(cu, s + 1, t_total);
+  const int64_t smat = (static_cast<int64_t>(s) * h_v + h) * D * D + static_cast<int64_t>(dv0 + rr) * D;
+
+  float gs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};   // G, this thread's 8 values of row r
+  if (dfin && row_ok) {
+    const float4 x = *reinterpret_cast<const float4*>(dfin + smat + ca);
+    const float4 y = *reinterpret_cast<const float4*>(dfin + smat + cb);
+    gs[0] = x.x; gs[1] = x.y; gs[2] = x.z; gs[3] = x.w; gs[4] = y.x; gs[5] = y.y; gs[6] = y.z; gs[7] = y.w;
+  }
+  const int64_t slot0 = start / kBwdChunk + s;
+  const int64_t nch = (end - start + kBwdChunk - 1) / kBwdChunk;
+  for (int64_t c = nch - 1; c >= 0; --c) {
+    const int64_t c0 = start + c * kBwdChunk;
+    const int64_t c1 = c0 + kBwdChunk < end ? c0 + kBwdChunk : end;
+    const int nsub = static_cast<int>((c1 - c0 + kBwdSub - 1) / kBwdSub);
+    const float* ck = ws.ckpt + ((slot0 + c) * h_v + h) * static_cast<int64_t>(D) * D + static_cast<int64_t>(dv0 + rr) * D;
+    for (int sb = nsub - 1; sb >= 0; --sb) {
+      // recompute from the chunk's checkpoint to the state before sub-block sb,
+      // then through sb keeping the state before each of its tokens
+      float st[8];
+      {
+        const float4 x = *reinterpret_cast<const float4*>(ck + ca);
+        const float4 y = *reinterpret_cast<const float4*>(ck + cb);
+        st[0] = x.x; st[1] = x.y; st[2] = x.z; st[3] = x.w; st[4] = y.x; st[5] = y.y; st[6] = y.z; st[7] = y.w;
+      }
+      int n = 0;
+      for (int bb = 0; bb <= sb; ++bb) {
+        const int64_t t0 = c0 + static_cast<int64_t>(bb) * kBwdSub;
+        n = static_cast<int>(c1 - t0 < kBwdSub ? c1 - t0 : kBwdSub);
+        bwd_stage<In, D, NT>(sm, q, k, v, dout, q_stride, k_stride, v_stride, gates, use_l2, l2_eps, h_v, h, hq, dv0,
+                             t0, n, bb == sb);
+        __syncthreads();
+        for (int j = 0; j < n; ++j) {
+          if (bb == sb && row_ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              stash[j][r][ca + i] = st[i];
+              stash[j][r][cb + i] = st[4 + i];
+            }
+          }
+          bwd_fwd_token<D>(st, sm, j, r, ca, cb);
+        }
+        if (bb < sb) __syncthreads();   // the next sub-block is staged over these inputs
+      }
+      __syncthreads();   // the stash is complete
+      // reverse over the sub-block's tokens
+      const int64_t tb = c0 + static_cast<int64_t>(sb) * kBwdSub;
+      for (int j = n - 1; j >= 0; --j) {
+        const int64_t t = tb + j;
+        float kk[8], qq[8], sp[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          kk[i] = sm.k[j][ca + i]; kk[4 + i] = sm.k[j][cb + i];
+          qq[i] = sm.q[j][ca + i]; qq[4 + i] = sm.q[j][cb + i];
+          sp[i] = stash[j][rr][ca + i]; sp[4 + i] = stash[j][rr][cb + i];
+        }
+        const float a = sm.a[j], bt = sm.b[j];
+        const float vr = sm.v[j][rr], dor = sm.dov[j][rr];
+        float dk = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { sp[i] *= a; dk += sp[i] * kk[i]; }   // sp: S' = a S_{t-1}
+        dk = group_sum<TPR>(dk);
+        const float e = vr - dk;
+        float pq[8], pk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          gs[i] += scale * dor * qq[i];
+          pq[i] = scale * dor * (sp[i] + bt * e * kk[i]);   // scale do_r S_t[r, :]
+        }
+        float u = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u += gs[i] * kk[i];
+        u = group_sum<TPR>(u);
+        float pg = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pk[i] = bt * (gs[i] * e - sp[i] * u);
+          const float ds = gs[i] - bt * u * kk[i];
+          pg += ds * sp[i];
+          gs[i] = a * ds;
+        }
+        pg = group_sum<TPR>(pg);
+        if (row_ok && l == 0) dv_out[(t * h_v + h) * static_cast<int64_t>(D) + dv0 + r] = bt * u;
+        // sums over the slice's rows: first over the rows of this wave (lane
+        // bits at and above TPR; the row scalars are replicated over the row's
+        // lanes), then over the waves through LDS
+        float sbu = row_ok ? e * u : 0.f, sgg = row_ok ? pg : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (!row_ok) pq[i] = pk[i] = 0.f;
+        }
+#pragma unroll
+        for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            pq[i] += __shfl_xor(pq[i], off);
+            pk[i] += __shfl_xor(pk[i], off);
+          }
+          sbu += __shfl_xor(sbu, off);
+          sgg += __shfl_xor(sgg, off);
+        }
+        const int wv = tid >> 6, ln = tid & 63;
+        if (ln < TPR) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            red_q[wv][ca + i] = pq[i]; red_q[wv][cb + i] = pq[4 + i];
+            red_k[wv][ca + i] = pk[i]; red_k[wv][cb + i] = pk[4 + i];
+          }
+          if (ln == 0) {
+            red_s[wv][0] = sbu;
+            red_s[wv][1] = sgg;
+          }
+        }
+        __syncthreads();
+        const int64_t pbase = (t * h_v + h) * TILES + tile;
+        if (tid < D) {
+          float sq = 0.f, sk2 = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) { sq += red_q[w][tid]; sk2 += red_k[w][tid]; }
+          ws.pdq[pbase * D + tid] = sq;
+          ws.pdk[pbase * D + tid] = sk2;
+        }
+        if (tid == 0) {
+          float sb_ = 0.f, sg = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) { sb_ += red_s[w][0]; sg += red_s[w][1]; }
+          ws.pdb[pbase] = sb_;
+          ws.pdg[pbase] = sg;
+        }
+        __syncthreads();
+      }
+    }
+  }
+  if (dinit && row_ok) {
+    *reinterpret_cast<float4*>(dinit + smat + ca) = make_float4(gs[0], gs[1], gs[2], gs[3]);
+    *reinterpret_cast<float4*>(dinit + smat + cb) = make_float4(gs[4], gs[5], gs[6], gs[7]);
+  }
+}
+
+// Block-wide sum over NT threads (NT a multiple of 64).
+template <int NT>
+__device__ __forceinline__ float block_sum(float x, float* scratch) {
+  x = group_sum<64>(x);
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+template <class In, int D, int NT>
+__global__ __launch_bounds__(NT) void k_bwd_reduce(
+    const typename In::T* __restrict__ q, const typename In::T* __restrict__ k, int64_t q_stride, int64_t k_stride,
+    int use_l2, float l2_eps, int h_qk, int h_v, int64_t t_total, BwdWs ws, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dg, float* __restrict__ dbeta) {
+  constexpr int TILES = D / kBwdRows;
+  static_assert(NT >= D && NT % 64 == 0, "one thread per column");
+  __shared__ float scratch[NT / 64];
+  const int64_t t = blockIdx.x / h_qk;
+  const int hq = static_cast<int>(blockIdx.x % h_qk);
+  const int grp = h_v / h_qk;
+  const int c = threadIdx.x;
+  const bool col = c < D;
+  float gq = 0.f, gk = 0.f;
+  if (col) {
+    for (int hh = 0; hh < grp; ++hh) {
+      const int h = hq * grp + hh;
+      for (int ti = 0; ti < TILES; ++ti) {
+        const int64_t p = ((t * h_v + h) * TILES + ti) * D + c;
+        gq += ws.pdq[p];
+        gk += ws.pdk[p];
+      }
+    }
+  }
+  const float xq = col ? In::load(q + t * q_stride + static_cast<int64_t>(hq) * D, c) : 0.f;
+  const float xk = col ? In::load(k + t * k_stride + static_cast<int64_t>(hq) * D, c) : 0.f;
+  if (use_l2) {
+    // x^ = x / r, r = sqrt(sum x^2 + eps):  dx = (dx^ - x^ (x^ . dx^)) / r
+    const float rq = sqrtf(block_sum<NT>(xq * xq, scratch) + l2_eps);
+    const float rk = sqrtf(block_sum<NT>(xk * xk, scratch) + l2_eps);
+    const float dotq = block_sum<NT>((xq / rq) * gq, scratch);
+    const float dotk = block_sum<NT>((xk / rk) * gk, scratch);
+    gq = (gq - (xq / rq) * dotq) / rq;
+    gk = (gk - (xk / rk) * dotk) / rk;
+  }
+  if (col) {
+    dq[(t * h_qk + hq) * static_cast<int64_t>(D) + c] = gq;
+    dk[(t * h_qk + hq) * static_cast<int64_t>(D) + c] = gk;
+  }
+  if (c < grp) {
+    const int h = hq * grp + c;
+    float sb = 0.f, sg = 0.f;
+    for (int ti = 0; ti < TILES; ++ti) {
+      const int64_t p = (t * h_v + h) * TILES + ti;
+      sb += ws.pdb[p];
+      sg += ws.pdg[p];
+    }
+    dbeta[t * h_v + h] = sb;
+    dg[t * h_v + h] = sg;
+  }
+}
+
+template <class In, int D>
+static hipError_t run_bwd(const BwdArgs& a) {
+  using T = typename In::T;
+  constexpr int NT = D == 128 ? 256 : 64;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  BwdWs ws = bwd_carve(a.workspace, a.h_v, D, a.n_seq, a.t_total);
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const int64_t nblk = static_cast<int64_t>(a.n_seq) * a.h_v * (D / kBwdRows);
+  if (a.t_total > 0) {
+    hipLaunchKernelGGL((k_bwd_ckpt<In, D, NT>), dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, st, q, k, v,
+                       a.q_stride, a.k_stride, a.v_stride, a.gate, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu, a.n_seq,
+                       a.t_total, a.init, ws);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((k_bwd_slice<In, D, NT>), dim3(static_cast<unsigned>(nblk)), dim3(NT), 0, st, q, k, v,
+                     a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu,
+                     a.n_seq, a.t_total, a.d_o, a.d_final, a.dv, a.d_init, ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.t_total == 0) return e;
+  constexpr int NTR = D < 64 ? 64 : D;
+  hipLaunchKernelGGL((k_bwd_reduce<In, D, NTR>), dim3(static_cast<unsigned>(a.t_total * a.h_qk)), dim3(NTR), 0, st,
+                     q, k, a.q_stride, a.k_stride, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.t_total, ws, a.dq, a.dk,
+                     a.dg, a.dbeta);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a) {
+  if (a.dt == GDN_BF16) {
+    if (a.d == 128) return run_bwd<BF16, 128>(a);
+  } else {
+    if (a.d == 128) return run_bwd<F32, 128>(a);
+    if (a.d == 16) return run_bwd<F32, 16>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

@@ -77,12 +77,38 @@ struct VerifyArgs {
   void* stream;
 };
 
+// Backward of the gated delta rule over packed sequences.
+struct BwdArgs {
+  const void *q, *k, *v;
+  int64_t q_stride, k_stride, v_stride;
+  gdn_dtype dt;
+  GateSrc gate;
+  float scale;
+  int use_l2;
+  float l2_eps;
+  int h_qk, h_v, d;
+  const int32_t* cu;
+  int n_seq;
+  int64_t t_total;
+  const float* init;      // [n_seq, h_v, d, d] or NULL (zeros)
+  const float* d_o;       // [t_total, h_v, d]
+  const float* d_final;   // [n_seq, h_v, d, d] or NULL (zero)
+  float *dq, *dk;         // [t_total, h_qk, d]
+  float* dv;              // [t_total, h_v, d]
+  float *dg, *dbeta;      // [t_total, h_v]
+  float* d_init;          // [n_seq, h_v, d, d] or NULL
+  void* workspace;
+  void* stream;
+};
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
 size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_seq, int64_t t_total,
                       int with_norm);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
+size_t bwd_ws_bytes(int h_v, int d, int n_seq, int64_t t_total);
+hipError_t launch_chunk_bwd(const BwdArgs& a);
 hipError_t launch_recurrent_step(const StepArgs& a);
 hipError_t launch_recurrent_verify(const VerifyArgs& a);
 hipError_t launch_conv1d_verify(const void* x, gdn_dtype dt, const void* w, int channels, int n_seq, int n_tok,

@@ -226,6 +226,34 @@ def gdn_chunk_mixed(q, k, v, g, beta, state, o, *, chunk, cu_seqlens, state_slot
     return o
 
 
+def gdn_chunk_bwd_workspace_size(h_qk, h_v, d_k, d_v, n_seq, t_total) -> int:
+    out = ctypes.c_size_t(0)
+    st = L.load().gdn_chunk_bwd_workspace_size(h_qk, h_v, d_k, d_v, n_seq, t_total, ctypes.byref(out))
+    L.check("gdn_chunk_bwd_workspace_size", st)
+    return out.value
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta, *, scale=1.0, use_qk_l2norm=True, l2_eps=1e-6,
+                  cu_seqlens=None, initial_state=None, d_final=None, d_initial=None, workspace=None, stream=None):
+    """Gradients of sum(d_o * o) + sum(d_final * S_T) for the chunked gated delta rule.
+    q, k [T, Hqk, dk]; v [T, Hv, dv]; g, beta [T, Hv] fp32; d_o [T, Hv, dv] fp32; outputs
+    dq, dk [T, Hqk, dk], dv [T, Hv, dv], dg, dbeta [T, Hv], d_initial [N, Hv, dv, dk], fp32."""
+    t_total, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n_seq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
+    if workspace is None:
+        nbytes = gdn_chunk_bwd_workspace_size(h_qk, h_v, d_k, d_v, n_seq, t_total)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = L.load().gdn_chunk_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(g), _ptr(beta), float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, _ptr(cu_seqlens), n_seq, t_total, _ptr(initial_state), _ptr(d_o), _ptr(d_final),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(d_initial), _ptr(workspace), workspace.numel(),
+        _stream(stream))
+    L.check("gdn_chunk_bwd", st)
+    return dq, dk, dv, dg, dbeta
+
+
 def gdn_gated_rmsnorm(x, z, w, y, *, eps=1e-6, stream=None):
     """y = x / sqrt(mean(x^2) + eps) * w * SiLU(z) over the last dim (16 or 128)."""
     d = x.shape[-1]

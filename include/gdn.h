@@ -384,6 +384,53 @@ gdn_status gdn_chunk_mixed(const void* q, const void* k, const void* v,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * gdn_chunk_bwd -- gradients of the gated delta rule over packed sequences
+ * (the backward pass for training).  (Recurrence: the formula at the top of
+ * this header, as in gdn_chunk_fwd; gradients from the states at chunk
+ * boundaries: haskell-infer-demo README, the FLA-derived chunked GDN kernels,
+ * and Flare core-design, the chunk-boundary checkpoint paragraph.)
+ *
+ * For L = sum(d_o * o) + sum(d_final * S_T), with o and S_T what gdn_chunk_fwd
+ * returns for the same inputs (no norm epilogue), writes dL/dq, dL/dk (through
+ * the L2 normalisation when use_qk_l2norm), dL/dv, dL/dg, dL/dbeta and
+ * dL/d(initial_state).  The states entering every 64-token chunk are
+ * recomputed into the workspace, then each sequence runs backwards through
+ * its chunks, recomputing the states inside a chunk from its checkpoint.
+ * All arithmetic is fp32; sums run in a fixed order (bitwise reproducible).
+ *
+ *   q, k, v, strides, dt, g, beta, scale, use_qk_l2norm, l2_eps, h_qk, h_v,
+ *   cu_seqlens, n_seq, t_total, initial_state: as gdn_chunk_fwd;
+ *               (d_k, d_v) = (128, 128) (bf16 or fp32) or (16, 16) (fp32)
+ *   d_o         [t_total, h_v, d_v] fp32: gradient of the outputs
+ *   d_final     [n_seq, h_v, d_v, d_k] fp32, or NULL (zero)
+ *   dq, dk      [t_total, h_qk, d_k] fp32 (written)
+ *   dv          [t_total, h_v, d_v] fp32 (written)
+ *   dg, dbeta   [t_total, h_v] fp32 (written)
+ *   d_initial   [n_seq, h_v, d_v, d_k] fp32, or NULL (not wanted)
+ *   workspace   ws_bytes >= gdn_chunk_bwd_workspace_size(...); no
+ *               initialisation needed, contents not preserved
+ * n_seq == 0 is a no-op.  Outputs must not overlap inputs, each other or the
+ * workspace (GDN_ERR_ALIAS).  Other statuses as gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v,
+                         int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                         const float* g, const float* beta, float scale,
+                         int32_t use_qk_l2norm, float l2_eps,
+                         int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v,
+                         const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                         const float* initial_state, const float* d_o, const float* d_final,
+                         float* dq, float* dk, float* dv, float* dg, float* dbeta, float* d_initial,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gdn_chunk_bwd_workspace_size -- (host) bytes of workspace gdn_chunk_bwd
+ * needs: the chunk-boundary states ((t_total / 64 + n_seq) x h_v x d_v x d_k
+ * fp32) and the per-slice partial sums of dq, dk, dbeta, dg.
+ */
+gdn_status gdn_chunk_bwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t n_seq,
+                                        int64_t t_total, size_t* bytes /* host */);
+
+/*
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * w * SiLU(z), per row of d.
  * (The gated RMSNorm of the GDN layers: haskell-infer-demo README,
  *  "Highlights", hybrid-architecture bullet, and "Architecture", gdn_norm.cu;

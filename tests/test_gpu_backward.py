@@ -1,0 +1,86 @@
+"""GPU parity of gdn_chunk_bwd (gradients of the gated delta rule) against the
+float64 gradient oracle (oracle/gdn_grad_ref.py, itself pinned to finite
+differences): packed sequences with ragged tails, a one-token and an empty
+sequence, nonzero initial states, a final-state gradient, scale != 1, and the
+L2 normalisation on and off.
+
+Tolerance: max|gpu - ref| / RMS(ref) <= 1e-4 per gradient tensor.  The kernels
+compute in fp32 on exact inputs; each gradient is a sum of a few thousand fp32
+products per token (two 128-long dot products per row, sums over 128 rows and
+over the later tokens through the state gradient), so a relative error of a
+few 1e-6 of the tensor's RMS is expected, and 1e-4 leaves room for the
+cancellation in dg (a difference of terms larger than itself).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, dev, dev_i32, host, note, rel_max
+from harness import inputs as I
+from oracle import gdn_grad_ref as G
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+SMALL = I.Layout(h_qk=2, h_v=4, d_k=128, d_v=128, chunk=64, dtype="bf16")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from gated_deltanet_mixer_causal_amd import ops as _ops
+    _ops.L.load()
+    return _ops
+
+
+def _run(ops, lay, d, do, dfin, scale, use_l2, want_dinit=True):
+    tdt = torch.bfloat16 if lay.dtype == "bf16" else torch.float32
+    q, k, v = I.split_qkv(d["x"], lay)
+    T, n = q.shape[0], len(d["cu_seqlens"]) - 1
+    out = dict(dq=torch.full((T, lay.h_qk, lay.d_k), float("nan"), device=DEV),
+               dk=torch.full((T, lay.h_qk, lay.d_k), float("nan"), device=DEV),
+               dv=torch.full((T, lay.h_v, lay.d_v), float("nan"), device=DEV),
+               dg=torch.full((T, lay.h_v), float("nan"), device=DEV),
+               dbeta=torch.full((T, lay.h_v), float("nan"), device=DEV))
+    dinit = torch.full((n, lay.h_v, lay.d_v, lay.d_k), float("nan"), device=DEV) if want_dinit else None
+    ops.gdn_chunk_bwd(dev(q, tdt), dev(k, tdt), dev(v, tdt), dev(d["g"]), dev(d["beta"]), dev(do),
+                      out["dq"], out["dk"], out["dv"], out["dg"], out["dbeta"], scale=scale, use_qk_l2norm=use_l2,
+                      cu_seqlens=dev_i32(d["cu_seqlens"]), initial_state=dev(d["state"]),
+                      d_final=None if dfin is None else dev(dfin), d_initial=dinit)
+    torch.cuda.synchronize()
+    out["d_initial"] = dinit
+    return out, (q, k, v)
+
+
+CASES = [
+    ("f32_d16", I.TINY_LAYOUT, [40, 1, 16, 0, 23], 0.7, True),
+    ("f32_d16_nol2", I.TINY_LAYOUT, [33, 17], 1.0, False),
+    ("bf16_d128", SMALL, [150, 1, 64, 0, 70], 1.0, True),
+]
+
+
+@pytest.mark.parametrize("name,lay,lengths,scale,use_l2", CASES, ids=[c[0] for c in CASES])
+def test_chunk_bwd_against_oracle(ops, name, lay, lengths, scale, use_l2):
+    note(f"chunk bwd {name}: lengths {lengths} scale {scale} l2 {use_l2}")
+    d = I.prefill_inputs(50, lay, lengths, state_std=0.02, g_mode="tiny" if lay.dtype == "f32" else "model")
+    rng = np.random.default_rng(51)
+    T, n = int(sum(lengths)), len(lengths)
+    do = rng.standard_normal((T, lay.h_v, lay.d_v)).astype(np.float32)
+    dfin = (0.5 * rng.standard_normal((n, lay.h_v, lay.d_v, lay.d_k))).astype(np.float32)
+    out, (q, k, v) = _run(ops, lay, d, do, dfin, scale, use_l2)
+    ref = G.gated_delta_rule_grads(q, k, v, d["g"], d["beta"], do, dfin, scale=scale, initial_state=d["state"],
+                                   cu_seqlens=d["cu_seqlens"], use_qk_l2norm=use_l2)
+    errs = {key: rel_max(host(out[key]), ref[key]) for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial")}
+    note("  " + ", ".join(f"{k_} {v_:.1e}" for k_, v_ in errs.items()))
+    assert all(e <= TOL for e in errs.values()), errs
+
+    # reruns are bitwise identical; without d_final the final-state term drops out
+    out2, _ = _run(ops, lay, d, do, dfin, scale, use_l2)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial"):
+        assert torch.equal(out[key], out2[key]), key
+    out3, _ = _run(ops, lay, d, do, None, scale, use_l2, want_dinit=False)
+    ref3 = G.gated_delta_rule_grads(q, k, v, d["g"], d["beta"], do, None, scale=scale, initial_state=d["state"],
+                                    cu_seqlens=d["cu_seqlens"], use_qk_l2norm=use_l2)
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert rel_max(host(out3[key]), ref3[key]) <= TOL, key
