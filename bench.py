@@ -120,6 +120,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent buffer sets rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gdn_chunk_bwd timing")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the speculative-verification and mixed prefill-plus-decode timings")
     ap.add_argument("--copy-probe", action="store_true",
@@ -198,8 +199,28 @@ def prefill_leg(args, torch, np, ops, I):
     ms_chunk, _ = timed(chunk_only, args.steps, args.warmup, torch)
     stats = call_stats(chunk_only, max(args.steps, 50), args.warmup + args.steps, torch)
     ms_chunk_gated, _ = timed(chunk_gated, args.steps, args.warmup, torch)
+    ms_bwd = None
+    if not args.no_backward:
+        # gradients of the same call: d_o for every output, a final-state gradient
+        bw = dict(do=torch.randn((T, lay.h_v, lay.d_v), device=dev),
+                  dfin=torch.randn((1, lay.h_v, lay.d_v, lay.d_k), device=dev),
+                  dq=torch.empty((T, lay.h_qk, lay.d_k), device=dev), dk=torch.empty((T, lay.h_qk, lay.d_k), device=dev),
+                  dv=torch.empty((T, lay.h_v, lay.d_v), device=dev), dg=torch.empty((T, lay.h_v), device=dev),
+                  dbeta=torch.empty((T, lay.h_v), device=dev),
+                  dinit=torch.empty((1, lay.h_v, lay.d_v, lay.d_k), device=dev),
+                  ws=torch.empty(ops.gdn_chunk_bwd_workspace_size(lay.h_qk, lay.h_v, lay.d_k, lay.d_v, 1, T),
+                                 dtype=torch.uint8, device=dev))
+
+        def backward(i):
+            s = sets[i % len(sets)]
+            ops.gdn_chunk_bwd(s["q"], s["k"], s["v"], s["g"], s["beta"], bw["do"], bw["dq"], bw["dk"], bw["dv"],
+                              bw["dg"], bw["dbeta"], cu_seqlens=s["cu"], d_final=bw["dfin"], d_initial=bw["dinit"],
+                              workspace=bw["ws"])
+
+        ms_bwd, _ = timed(backward, max(2, args.steps // 4), 1, torch)
+        del bw
     return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, chunk_stats=stats, layout=lay,
-                ms_chunk_gated=ms_chunk_gated)
+                ms_chunk_gated=ms_chunk_gated, ms_bwd=ms_bwd)
 
 
 def decode_leg(args, torch, np, ops, I):
@@ -443,6 +464,13 @@ def main():
     if not args.no_decode:
         out["fused_gates"]["recurrent_step_ms"] = round(dc["ms_rec_gated"], 4)
         out["fused_gates"]["recurrent_step_vs_plain"] = round(dc["ms_rec_gated"] / dc["ms_rec"], 4)
+    if pf["ms_bwd"] is not None:
+        out["backward"] = {
+            "what": "gdn_chunk_bwd: dq, dk, dv, dg, dbeta, d_initial of the same 4096-token call (fp32)",
+            "ms_per_call": round(pf["ms_bwd"], 4),
+            "tokens_per_s": round(T / (pf["ms_bwd"] * 1e-3), 1),
+            "vs_forward_chunk_fwd": round(pf["ms_bwd"] / pf["ms_chunk"], 2),
+        }
     if not args.no_serving:
         sv = serving_leg(args, torch, np, ops, I)
         # recurrent verify: the live state read once, W checkpoint columns written

@@ -18,14 +18,15 @@
 //
 // Kernels:
 //   k_bwd_ckpt    forward over each sequence, writing the state entering
-//                 every 64-token chunk (per slice) to the workspace.
-//   k_bwd_slice   per (sequence, v-head, 16-row slice), chunks last to
-//                 first; inside a chunk, 16-token sub-blocks last to first:
-//                 recompute from the chunk's checkpoint up to the sub-block,
-//                 keeping the state before each of its tokens in LDS, then
-//                 run the reverse step over its tokens.  A sub-block's
+//                 every 16-token block (per slice) to the workspace.
+//   k_bwd_slice   per (sequence, v-head, 16-row slice), blocks last to
+//                 first: recompute from the block's checkpoint through the
+//                 block, keeping the state before each of its tokens in LDS,
+//                 then run the reverse step over its tokens.  A block's
 //                 inputs (normalised k, q; v, do of the slice; a, beta) are
-//                 staged in LDS first.
+//                 staged in LDS first.  (The loop also serves checkpoints
+//                 every kBwdChunk > kBwdSub tokens, recomputing the sub-blocks
+//                 before the current one.)
 //   k_bwd_reduce  per (token, q/k head): sums the slice partials over the
 //                 slices and the v-heads that read this q/k head, applies the
 //                 L2-norm backward dx = (dx^ - x^ (x^ . dx^)) / |x|_eps, and
@@ -38,10 +39,29 @@ namespace gdn {
 
 constexpr int kBwdRows = 16;    // state rows per workgroup
 constexpr int kBwdSub = 16;     // tokens per staged sub-block
-constexpr int kBwdChunk = 64;   // tokens between checkpoints
+constexpr int kBwdChunk = 16;   // tokens between checkpoints (one sub-block: no recompute beyond it)
+
+// Sum over groups of W consecutive lanes (W = 2, 4, 8, 16) with DPP lane moves
+// inside each 16-lane row instead of LDS-crossbar shuffles: quad permutations
+// for lane distances 1 and 2, then the half-row mirror (lane i of each 8 reads
+// lane 7 - i, the other quad) and the row mirror (lane i reads 15 - i, the
+// other half).  Every lane ends with the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int W>
+__device__ __forceinline__ float row_sum(float v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "groups inside one DPP row");
+  v += dpp_move<0xB1>(v);                       // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_move<0x4E>(v); // quad_perm [2,3,0,1]
+  if constexpr (W >= 8) v += dpp_move<0x141>(v);  // row_half_mirror
+  if constexpr (W >= 16) v += dpp_move<0x140>(v); // row_mirror
+  return v;
+}
 
 // Workspace carve-up (floats):
-//   ckpt [slots][h_v][D][D]          state entering each 64-token chunk
+//   ckpt [slots][h_v][D][D]          state entering each kBwdChunk-token block
 //   pdq, pdk [T][h_v][D/16][D]       slice partials of dq^, dk^
 //   pdb, pdg [T][h_v][D/16]          slice partials of dbeta, dg
 struct BwdWs {
@@ -118,8 +138,8 @@ __device__ __forceinline__ void bwd_stage(BwdStage<D>& sm, const typename In::T*
     float sk = 0.f, sq = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; }
-    sk = group_sum<TPR>(sk);
-    sq = group_sum<TPR>(sq);
+    sk = row_sum<TPR>(sk);
+    sq = row_sum<TPR>(sq);
     const float rk = use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f;
     const float rq = use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f;
 #pragma unroll
@@ -156,7 +176,7 @@ __device__ __forceinline__ void bwd_fwd_token(float (&s)[8], const BwdStage<D>& 
   float dk = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) dk += s[i] * kk[i];
-  dk = group_sum<TPR>(dk);
+  dk = row_sum<TPR>(dk);
   const float a = sm.a[j];
   const float be = sm.b[j] * (sm.v[j][r < kBwdRows ? r : 0] - a * dk);
 #pragma unroll
@@ -292,7 +312,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
         float dk = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) { sp[i] *= a; dk += sp[i] * kk[i]; }   // sp: S' = a S_{t-1}
-        dk = group_sum<TPR>(dk);
+        dk = row_sum<TPR>(dk);
         const float e = vr - dk;
         float pq[8], pk[8];
 #pragma unroll
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
         float u = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) u += gs[i] * kk[i];
-        u = group_sum<TPR>(u);
+        u = row_sum<TPR>(u);
         float pg = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -312,7 +332,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
           pg += ds * sp[i];
           gs[i] = a * ds;
         }
-        pg = group_sum<TPR>(pg);
+        pg = row_sum<TPR>(pg);
         if (row_ok && l == 0) dv_out[(t * h_v + h) * static_cast<int64_t>(D) + dv0 + r] = bt * u;
         // sums over the slice's rows: first over the rows of this wave (lane
         // bits at and above TPR; the row scalars are replicated over the row's

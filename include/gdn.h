@@ -393,9 +393,9 @@ gdn_status gdn_chunk_mixed(const void* q, const void* k, const void* v,
  * For L = sum(d_o * o) + sum(d_final * S_T), with o and S_T what gdn_chunk_fwd
  * returns for the same inputs (no norm epilogue), writes dL/dq, dL/dk (through
  * the L2 normalisation when use_qk_l2norm), dL/dv, dL/dg, dL/dbeta and
- * dL/d(initial_state).  The states entering every 64-token chunk are
- * recomputed into the workspace, then each sequence runs backwards through
- * its chunks, recomputing the states inside a chunk from its checkpoint.
+ * dL/d(initial_state).  The states entering every 16-token block are
+ * computed into the workspace, then each sequence runs backwards through
+ * its blocks, recomputing the states inside a block from its checkpoint.
  * All arithmetic is fp32; sums run in a fixed order (bitwise reproducible).
  *
  *   q, k, v, strides, dt, g, beta, scale, use_qk_l2norm, l2_eps, h_qk, h_v,
@@ -424,7 +424,7 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v,
 
 /*
  * gdn_chunk_bwd_workspace_size -- (host) bytes of workspace gdn_chunk_bwd
- * needs: the chunk-boundary states ((t_total / 64 + n_seq) x h_v x d_v x d_k
+ * needs: the block-boundary states ((t_total / 16 + n_seq) x h_v x d_v x d_k
  * fp32) and the per-slice partial sums of dq, dk, dbeta, dg.
  */
 gdn_status gdn_chunk_bwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t n_seq,

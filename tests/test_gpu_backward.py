@@ -84,3 +84,28 @@ def test_chunk_bwd_against_oracle(ops, name, lay, lengths, scale, use_l2):
                                     cu_seqlens=d["cu_seqlens"], use_qk_l2norm=use_l2)
     for key in ("dq", "dk", "dv", "dg", "dbeta"):
         assert rel_max(host(out3[key]), ref3[key]) <= TOL, key
+
+
+def test_chunk_bwd_full_size_sampled_heads(ops):
+    """The model shape (one 4096-token sequence, 16 q/k and 32 v heads, bf16,
+    model-like decays) through gdn_chunk_bwd on all heads; the oracle checks
+    v-heads 0 and 1 and the q/k head 0 they read (its dq, dk sum over both)."""
+    lay = I.MODEL_LAYOUT
+    note("chunk bwd full size T=4096, sampled heads 0-1")
+    d = I.model_prefill_inputs(4096, seed=1)
+    rng = np.random.default_rng(52)
+    T = 4096
+    do = rng.standard_normal((T, lay.h_v, lay.d_v)).astype(np.float32)
+    dfin = (0.5 * rng.standard_normal((1, lay.h_v, lay.d_v, lay.d_k))).astype(np.float32)
+    d["state"] = (0.02 * rng.standard_normal((1, lay.h_v, lay.d_v, lay.d_k))).astype(np.float32)
+    out, (q, k, v) = _run(ops, lay, d, do, dfin, 1.0, True)
+    hs = [0, 1]
+    ref = G.gated_delta_rule_grads(q[:, :1], k[:, :1], v[:, hs], d["g"][:, hs], d["beta"][:, hs], do[:, hs],
+                                   dfin[:, hs], initial_state=d["state"][:, hs], qk_of_v=[0, 0])
+    got = dict(dq=host(out["dq"])[:, :1], dk=host(out["dk"])[:, :1], dv=host(out["dv"])[:, hs],
+               dg=host(out["dg"])[:, hs], dbeta=host(out["dbeta"])[:, hs], d_initial=host(out["d_initial"])[:, hs])
+    errs = {key: rel_max(got[key], ref[key]) for key in got}
+    note("  " + ", ".join(f"{k_} {v_:.1e}" for k_, v_ in errs.items()))
+    assert all(e <= TOL for e in errs.values()), errs
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial"):
+        assert torch.isfinite(out[key]).all(), key
