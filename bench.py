@@ -199,7 +199,7 @@ def prefill_leg(args, torch, np, ops, I):
     ms_chunk, _ = timed(chunk_only, args.steps, args.warmup, torch)
     stats = call_stats(chunk_only, max(args.steps, 50), args.warmup + args.steps, torch)
     ms_chunk_gated, _ = timed(chunk_gated, args.steps, args.warmup, torch)
-    ms_bwd = None
+    ms_bwd = ms_conv_bwd = None
     if not args.no_backward:
         # gradients of the same call: d_o for every output, a final-state gradient
         bw = dict(do=torch.randn((T, lay.h_v, lay.d_v), device=dev),
@@ -219,8 +219,19 @@ def prefill_leg(args, torch, np, ops, I):
 
         ms_bwd, _ = timed(backward, max(2, args.steps // 4), 1, torch)
         del bw
+        cb = dict(dy=torch.randn((T, lay.channels), device=dev), dx=torch.empty((T, lay.channels), device=dev),
+                  dw=torch.empty((lay.channels, 4), device=dev),
+                  dhi=torch.empty((1, 3, lay.channels), device=dev))
+
+        def conv_backward(i):
+            s = sets[i % len(sets)]
+            ops.gdn_conv1d_bwd(s["x"], s["w"], cb["dy"], cb["dx"], cb["dw"], cu_seqlens=s["cu"],
+                               conv_state_in=s["tail"], d_state_in=cb["dhi"])
+
+        ms_conv_bwd, _ = timed(conv_backward, args.steps, args.warmup, torch)
+        del cb
     return dict(T=T, ms=ms, wall=wall, ms_chunk=ms_chunk, chunk_stats=stats, layout=lay,
-                ms_chunk_gated=ms_chunk_gated, ms_bwd=ms_bwd)
+                ms_chunk_gated=ms_chunk_gated, ms_bwd=ms_bwd, ms_conv_bwd=ms_conv_bwd)
 
 
 def decode_leg(args, torch, np, ops, I):
@@ -470,6 +481,8 @@ def main():
             "ms_per_call": round(pf["ms_bwd"], 4),
             "tokens_per_s": round(T / (pf["ms_bwd"] * 1e-3), 1),
             "vs_forward_chunk_fwd": round(pf["ms_bwd"] / pf["ms_chunk"], 2),
+            "gdn_conv1d_bwd_ms": round(pf["ms_conv_bwd"], 4),
+            "gdn_conv1d_bwd_GB_per_s": round(T * lay.channels * (2 + 4 + 4) / (pf["ms_conv_bwd"] * 1e-3) / 1e9, 1),
         }
     if not args.no_serving:
         sv = serving_leg(args, torch, np, ops, I)

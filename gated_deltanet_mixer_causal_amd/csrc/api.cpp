@@ -587,6 +587,54 @@ gdn_status gdn_chunk_bwd(const void* q, const void* k, const void* v, int64_t q_
   return finish(gdn::launch_chunk_bwd(a));
 }
 
+gdn_status gdn_conv1d_bwd_workspace_size(int32_t channels, int32_t n_seq, int64_t t_total, size_t* bytes) {
+  if (!bytes) return GDN_ERR_NULL;
+  if (channels <= 0 || channels % 8 || n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
+  *bytes = gdn::conv_bwd_ws_bytes(channels, n_seq, t_total);
+  return GDN_OK;
+}
+
+gdn_status gdn_conv1d_bwd(const void* x, gdn_dtype dt, const void* w, int32_t channels, const int32_t* cu_seqlens,
+                          int32_t n_seq, int64_t t_total, const void* conv_state_in, const float* dy,
+                          const float* d_state_out, float* dx, float* dw, float* d_state_in, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  if (n_seq < 0 || t_total < 0 || channels <= 0) return GDN_ERR_INVALID;
+  if (!dt_valid(dt)) return GDN_ERR_UNSUPPORTED;
+  if (channels % 8) return GDN_ERR_INVALID;
+  if (n_seq == 0) return GDN_OK;
+  if (!w || !dw) return GDN_ERR_NULL;
+  if (t_total > 0 && (!x || !dy || !dx)) return GDN_ERR_NULL;
+  if (!cu_seqlens && n_seq != 1) return GDN_ERR_NULL;
+  if (!workspace) return GDN_ERR_WORKSPACE;
+  size_t need = 0;
+  gdn_status st = gdn_conv1d_bwd_workspace_size(channels, n_seq, t_total, &need);
+  if (st != GDN_OK) return st;
+  if (ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (!all_aligned({x, w, conv_state_in, dy, d_state_out, dx, dw, d_state_in, workspace, cu_seqlens}))
+    return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const uint64_t rows = static_cast<uint64_t>(t_total) * channels;
+  const uint64_t hist = static_cast<uint64_t>(n_seq) * 3 * channels;
+  const Range rx{x, rows * eb}, rw{w, static_cast<uint64_t>(channels) * 4 * eb};
+  const Range rh{conv_state_in, conv_state_in ? hist * eb : 0};
+  const Range rdy{dy, rows * 4}, rdh{d_state_out, d_state_out ? hist * 4 : 0};
+  const Range rcu{cu_seqlens, cu_seqlens ? static_cast<uint64_t>(n_seq + 1) * 4 : 0};
+  const Range outs[] = {{dx, rows * 4}, {dw, static_cast<uint64_t>(channels) * 4 * 4},
+                        {d_state_in, d_state_in ? hist * 4 : 0}, {workspace, need}};
+  for (const Range& o : outs) {
+    if (!disjoint(o, {rx, rw, rh, rdy, rdh, rcu})) return GDN_ERR_ALIAS;
+    for (const Range& o2 : outs)
+      if (&o != &o2 && overlap(o, o2)) return GDN_ERR_ALIAS;
+  }
+  gdn::ConvBwdArgs a;
+  a.x = x; a.dt = dt; a.w = w; a.channels = channels;
+  a.cu = cu_seqlens; a.n_seq = n_seq; a.t_total = t_total;
+  a.hist = conv_state_in; a.dy = dy; a.dhist_out = d_state_out;
+  a.dx = dx; a.dw = dw; a.dhist_in = d_state_in;
+  a.workspace = workspace; a.stream = stream;
+  return finish(gdn::launch_conv1d_bwd(a));
+}
+
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w, float eps,
                              int64_t rows, int32_t d, void* y, gdn_dtype y_dt, void* stream) {
   if (rows < 0) return GDN_ERR_INVALID;

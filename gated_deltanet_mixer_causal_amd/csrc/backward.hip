@@ -455,6 +455,243 @@ __global__ __launch_bounds__(NT) void k_bwd_reduce(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Conv backward.  Forward, per sequence with padded input p = [history (3
+// rows); x_s]: pre[t] = sum_i w[i] p[t + i], y[t] = SiLU(pre[t]), and the new
+// history is p[L], p[L+1], p[L+2] (the width-4 causal conv: haskell-infer-demo
+// README, "Architecture"; raw-input history: Flare core-design,
+// short-convolution paragraph).  With dpre[t] = dy[t] SiLU'(pre[t]):
+//     dp[j]  = sum_i w[i] dpre[j - i]  (0 <= j - i < L)  + d_hist_out[j - L]
+//     dx[t]  = dp[t + 3],   d_hist_in[j] = dp[j] (j < 3)
+//     dw[i]  = sum over all sequences and t of dpre[t] p[t + i]
+// The rounding of y to the input dtype is not differentiated.
+// ---------------------------------------------------------------------------
+constexpr int kCbBT = 8;            // tokens per block
+constexpr int kCbThreads = 256;     // 8 channels per thread
+
+__device__ __forceinline__ float silu_grad(float x) {
+  const float s = 1.0f / (1.0f + __expf(-x));
+  return s * (1.0f + x * (1.0f - s));
+}
+
+// Block (kCbBT tokens of one sequence, kCbThreads * 8 channels): dx of its
+// rows and its share of dw (the products of its own rows), written as one
+// partial per block.  Empty block slots write zero partials.
+template <class E>
+__global__ __launch_bounds__(kCbThreads) void k_conv_bwd_dx(
+    const typename E::T* __restrict__ x, const typename E::T* __restrict__ w, int channels,
+    const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const typename E::T* __restrict__ hist,
+    const float* __restrict__ dy, const float* __restrict__ dhist_out, float* __restrict__ dx,
+    float* __restrict__ dw_part, int64_t n_tblk) {
+  const int slice = static_cast<int>(blockIdx.x / n_tblk);
+  const int64_t tblk = blockIdx.x % n_tblk;
+  const int c0 = (slice * kCbThreads + threadIdx.x) * 8;
+  if (c0 >= channels) return;
+  const int64_t ld = channels;
+  float* part = dw_part + (tblk * ld + c0) * 4;
+  int seq, len;
+  int64_t t0;
+  if (!locate_block(cu, n_seq, t_total, kCbBT, tblk, seq, t0, len)) {
+#pragma unroll
+    for (int e = 0; e < 32; e += 4) *reinterpret_cast<float4*>(part + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int64_t start = seq_start(cu, seq, t_total), L = seq_start(cu, seq + 1, t_total) - start;
+  const int64_t u0 = t0 - start;   // local index of the block's first token
+  float wt[4][8];
+  {
+    float tmp[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) E::load8(w + static_cast<int64_t>(c0) * 4 + 8 * i, tmp + 8 * i);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wt[i][c] = tmp[4 * c + i];
+  }
+  // padded rows u0 .. u0 + kCbBT + 5 (zeros past the sequence)
+  float pr[kCbBT + 6][8];
+#pragma unroll
+  for (int r = 0; r < kCbBT + 6; ++r) {
+    const int64_t j = u0 + r;   // padded index
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pr[r][c] = 0.f;
+    if (j < 3) {
+      if (hist) E::load8(hist + (static_cast<int64_t>(seq) * 3 + j) * ld + c0, pr[r]);
+    } else if (j - 3 < L) {
+      E::load8(x + (start + j - 3) * ld + c0, pr[r]);
+    }
+  }
+  // dpre for tokens u0 .. u0 + kCbBT + 2 (zero outside [0, L))
+  float dp[kCbBT + 3][8];
+  float dwa[4][8] = {};
+#pragma unroll
+  for (int r = 0; r < kCbBT + 3; ++r) {
+    const int64_t t = u0 + r;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dp[r][c] = 0.f;
+    if (t < L) {
+      float g[8];
+      const float4 a4 = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0);
+      const float4 b4 = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0 + 4);
+      g[0] = a4.x; g[1] = a4.y; g[2] = a4.z; g[3] = a4.w; g[4] = b4.x; g[5] = b4.y; g[6] = b4.z; g[7] = b4.w;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float pre = wt[0][c] * pr[r][c] + wt[1][c] * pr[r + 1][c] + wt[2][c] * pr[r + 2][c] +
+                          wt[3][c] * pr[r + 3][c];
+        dp[r][c] = g[c] * silu_grad(pre);
+      }
+      if (r < kCbBT) {   // the block's own tokens contribute to dw
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) dwa[i][c] += dp[r][c] * pr[r + i][c];
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    *reinterpret_cast<float4*>(part + 4 * c) = make_float4(dwa[0][c], dwa[1][c], dwa[2][c], dwa[3][c]);
+  // dx[u] = dp_pad[u + 3] = sum_i w[i] dpre[u + 3 - i] (+ d_hist_out[u + 3 - L])
+#pragma unroll
+  for (int r = 0; r < kCbBT; ++r) {
+    if (r < len) {
+      const int64_t u = u0 + r;
+      float o[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        o[c] = wt[3][c] * dp[r][c] + wt[2][c] * dp[r + 1][c] + wt[1][c] * dp[r + 2][c] + wt[0][c] * dp[r + 3][c];
+      const int64_t jo = u + 3 - L;
+      if (dhist_out && jo >= 0 && jo < 3) {
+        float e[8];
+        const float* src = dhist_out + (static_cast<int64_t>(seq) * 3 + jo) * ld + c0;
+        const float4 a4 = *reinterpret_cast<const float4*>(src);
+        const float4 b4 = *reinterpret_cast<const float4*>(src + 4);
+        e[0] = a4.x; e[1] = a4.y; e[2] = a4.z; e[3] = a4.w; e[4] = b4.x; e[5] = b4.y; e[6] = b4.z; e[7] = b4.w;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] += e[c];
+      }
+      float* dst = dx + (start + u) * ld + c0;
+      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+// d_hist_in of each sequence: dp_pad[j] for j < 3, one thread per (sequence,
+// 8 channels); handles sequences of any length, including empty ones.
+template <class E>
+__global__ __launch_bounds__(kCbThreads) void k_conv_bwd_hist(
+    const typename E::T* __restrict__ x, const typename E::T* __restrict__ w, int channels,
+    const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const typename E::T* __restrict__ hist,
+    const float* __restrict__ dy, const float* __restrict__ dhist_out, float* __restrict__ dhist_in) {
+  const int groups = channels / 8;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kCbThreads + threadIdx.x;
+  const int64_t s = gid / groups;
+  if (s >= n_seq) return;
+  const int c0 = static_cast<int>(gid % groups) * 8;
+  const int64_t ld = channels;
+  const int64_t start = seq_start(cu, static_cast<int>(s), t_total);
+  const int64_t L = seq_start(cu, static_cast<int>(s) + 1, t_total) - start;
+  float wt[4][8];
+  {
+    float tmp[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) E::load8(w + static_cast<int64_t>(c0) * 4 + 8 * i, tmp + 8 * i);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wt[i][c] = tmp[4 * c + i];
+  }
+  float pr[6][8];
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pr[r][c] = 0.f;
+    if (r < 3) {
+      if (hist) E::load8(hist + (s * 3 + r) * ld + c0, pr[r]);
+    } else if (r - 3 < L) {
+      E::load8(x + (start + r - 3) * ld + c0, pr[r]);
+    }
+  }
+  float dp[3][8];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      dp[t][c] = 0.f;
+      if (t < L) {
+        const float pre = wt[0][c] * pr[t][c] + wt[1][c] * pr[t + 1][c] + wt[2][c] * pr[t + 2][c] + wt[3][c] * pr[t + 3][c];
+        dp[t][c] = dy[(start + t) * ld + c0 + c] * silu_grad(pre);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    float o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      o[c] = 0.f;
+#pragma unroll
+      for (int i = 0; i <= j; ++i) o[c] += wt[i][c] * dp[j - i][c];
+      if (dhist_out && j - L >= 0) o[c] += dhist_out[(s * 3 + (j - L)) * ld + c0 + c];
+    }
+    float* dst = dhist_in + (s * 3 + j) * ld + c0;
+    *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// dw[c][i] = sum over blocks of the partials, in block order.
+__global__ __launch_bounds__(256) void k_conv_bwd_dw(const float* __restrict__ dw_part, int channels, int64_t n_tblk,
+                                                     float* __restrict__ dw) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (channel, tap)
+  if (e >= static_cast<int64_t>(channels) * 4) return;
+  float sacc = 0.f;
+  for (int64_t b = 0; b < n_tblk; ++b) sacc += dw_part[b * channels * 4 + e];
+  dw[e] = sacc;
+}
+
+size_t conv_bwd_ws_bytes(int channels, int n_seq, int64_t t_total) {
+  return sizeof(float) * static_cast<size_t>(block_slots(t_total, n_seq, kCbBT)) * channels * 4;
+}
+
+template <class E>
+static hipError_t run_conv_bwd(const ConvBwdArgs& a) {
+  using T = typename E::T;
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const int64_t ntblk = block_slots(a.t_total, a.n_seq, kCbBT);
+  const int nslices = (a.channels + kCbThreads * 8 - 1) / (kCbThreads * 8);
+  float* part = static_cast<float*>(a.workspace);
+  if (a.t_total > 0) {
+    hipLaunchKernelGGL((k_conv_bwd_dx<E>), dim3(static_cast<unsigned>(ntblk * nslices)), dim3(kCbThreads), 0, st,
+                       static_cast<const T*>(a.x), static_cast<const T*>(a.w), a.channels, a.cu, a.n_seq, a.t_total,
+                       static_cast<const T*>(a.hist), a.dy, a.dhist_out, a.dx, part, ntblk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned nb = static_cast<unsigned>((static_cast<int64_t>(a.channels) * 4 + 255) / 256);
+    hipLaunchKernelGGL(k_conv_bwd_dw, dim3(nb), dim3(256), 0, st, part, a.channels, ntblk, a.dw);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    const unsigned nb = static_cast<unsigned>((static_cast<int64_t>(a.channels) * 4 + 255) / 256);
+    hipLaunchKernelGGL(k_conv_bwd_dw, dim3(nb), dim3(256), 0, st, part, a.channels, int64_t(0), a.dw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.dhist_in) {
+    const int64_t threads = static_cast<int64_t>(a.n_seq) * (a.channels / 8);
+    hipLaunchKernelGGL((k_conv_bwd_hist<E>), dim3(static_cast<unsigned>((threads + kCbThreads - 1) / kCbThreads)),
+                       dim3(kCbThreads), 0, st, static_cast<const T*>(a.x), static_cast<const T*>(a.w), a.channels,
+                       a.cu, a.n_seq, a.t_total, static_cast<const T*>(a.hist), a.dy, a.dhist_out, a.dhist_in);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_conv1d_bwd(const ConvBwdArgs& a) {
+  if (a.dt == GDN_BF16) return run_conv_bwd<BF16>(a);
+  return run_conv_bwd<F32>(a);
+}
+
 template <class In, int D>
 static hipError_t run_bwd(const BwdArgs& a) {
   using T = typename In::T;

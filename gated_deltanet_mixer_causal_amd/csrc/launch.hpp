@@ -101,6 +101,25 @@ struct BwdArgs {
   void* stream;
 };
 
+// Backward of the width-4 conv + SiLU over packed sequences.
+struct ConvBwdArgs {
+  const void* x;
+  gdn_dtype dt;
+  const void* w;
+  int channels;
+  const int32_t* cu;
+  int n_seq;
+  int64_t t_total;
+  const void* hist;        // [n_seq, 3, channels] history before the call, or NULL (zeros)
+  const float* dy;         // [t_total, channels]
+  const float* dhist_out;  // [n_seq, 3, channels] or NULL
+  float* dx;               // [t_total, channels]
+  float* dw;               // [channels, 4]
+  float* dhist_in;         // [n_seq, 3, channels] or NULL
+  void* workspace;
+  void* stream;
+};
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
@@ -109,6 +128,8 @@ size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_s
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 size_t bwd_ws_bytes(int h_v, int d, int n_seq, int64_t t_total);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+size_t conv_bwd_ws_bytes(int channels, int n_seq, int64_t t_total);
+hipError_t launch_conv1d_bwd(const ConvBwdArgs& a);
 hipError_t launch_recurrent_step(const StepArgs& a);
 hipError_t launch_recurrent_verify(const VerifyArgs& a);
 hipError_t launch_conv1d_verify(const void* x, gdn_dtype dt, const void* w, int channels, int n_seq, int n_tok,

@@ -254,6 +254,24 @@ def gdn_chunk_bwd(q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta, *, scale=1.0, us
     return dq, dk, dv, dg, dbeta
 
 
+def gdn_conv1d_bwd(x, w, dy, dx, dw, *, cu_seqlens=None, conv_state_in=None, d_state_out=None, d_state_in=None,
+                   workspace=None, stream=None):
+    """Gradients of the width-4 conv + SiLU.  x [T, Ch] (bf16/fp32); w [Ch, 4]; dy, dx [T, Ch] fp32;
+    dw [Ch, 4] fp32; histories [N, 3, Ch] (conv_state_in of x's dtype, the gradients fp32)."""
+    t_total, ch = x.shape
+    n_seq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
+    if workspace is None:
+        out = ctypes.c_size_t(0)
+        L.check("gdn_conv1d_bwd_workspace_size",
+                L.load().gdn_conv1d_bwd_workspace_size(ch, n_seq, t_total, ctypes.byref(out)))
+        workspace = torch.empty(max(out.value, 1), dtype=torch.uint8, device=x.device)
+    st = L.load().gdn_conv1d_bwd(_ptr(x), _dt(x), _ptr(w), ch, _ptr(cu_seqlens), n_seq, t_total, _ptr(conv_state_in),
+                                 _ptr(dy), _ptr(d_state_out), _ptr(dx), _ptr(dw), _ptr(d_state_in), _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    L.check("gdn_conv1d_bwd", st)
+    return dx, dw
+
+
 def gdn_gated_rmsnorm(x, z, w, y, *, eps=1e-6, stream=None):
     """y = x / sqrt(mean(x^2) + eps) * w * SiLU(z) over the last dim (16 or 128)."""
     d = x.shape[-1]

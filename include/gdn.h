@@ -431,6 +431,40 @@ gdn_status gdn_chunk_bwd_workspace_size(int32_t h_qk, int32_t h_v, int32_t d_k, 
                                         int64_t t_total, size_t* bytes /* host */);
 
 /*
+ * gdn_conv1d_bwd -- gradients of gdn_conv1d_fwd (width-4 causal conv + SiLU over
+ * packed sequences) for training.  (The conv and its raw-input history:
+ * haskell-infer-demo README, "Architecture"; Flare core-design,
+ * short-convolution paragraph.)
+ *
+ * For L = sum(dy * y) + sum(d_state_out * state_out), with y and state_out
+ * what gdn_conv1d_fwd computes from x, w and the history conv_state_in (the
+ * rounding of y to dt is not differentiated), writes dL/dx, dL/dw and
+ * dL/d(conv_state_in).  fp32 arithmetic; dw sums per-block partials in a fixed
+ * order (bitwise reproducible).
+ *
+ *   x, dt, w, channels, cu_seqlens, n_seq, t_total: as gdn_conv1d_fwd (packed
+ *               prefill; cu_seqlens may be NULL only when n_seq == 1)
+ *   conv_state_in [n_seq, 3, channels] of dt (per sequence, oldest first), or
+ *               NULL (zeros)
+ *   dy          [t_total, channels] fp32
+ *   d_state_out [n_seq, 3, channels] fp32, or NULL (zero)
+ *   dx          [t_total, channels] fp32 (written)
+ *   dw          [channels, 4] fp32 (written)
+ *   d_state_in  [n_seq, 3, channels] fp32, or NULL (not wanted)
+ *   workspace   ws_bytes >= gdn_conv1d_bwd_workspace_size(...)
+ * n_seq == 0 is a no-op.  Outputs must not overlap inputs or each other.
+ */
+gdn_status gdn_conv1d_bwd(const void* x, gdn_dtype dt, const void* w, int32_t channels,
+                          const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                          const void* conv_state_in, const float* dy, const float* d_state_out,
+                          float* dx, float* dw, float* d_state_in,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/* gdn_conv1d_bwd_workspace_size -- (host) bytes of workspace gdn_conv1d_bwd needs. */
+gdn_status gdn_conv1d_bwd_workspace_size(int32_t channels, int32_t n_seq, int64_t t_total,
+                                         size_t* bytes /* host */);
+
+/*
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * w * SiLU(z), per row of d.
  * (The gated RMSNorm of the GDN layers: haskell-infer-demo README,
  *  "Highlights", hybrid-architecture bullet, and "Architecture", gdn_norm.cu;

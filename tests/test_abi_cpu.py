@@ -148,6 +148,56 @@ def test_chunk_mixed_validation(lib):
     assert chunk_mixed(lib, st=_addr(10) - pool + 16) == L.GDN_ERR_ALIAS
 
 
+def chunk_bwd(lib, **kw):
+    a = dict(q=_addr(0), k=_addr(1), v=_addr(2), dt=L.GDN_BF16, g=_addr(3), b=_addr(4), hq=2, hv=4, d=128,
+             cu=_addr(5), n=2, t=100, init=None, do=_addr(6), dfin=None, dq=_addr(7), dk=_addr(8), dv=_addr(9),
+             dg=_addr(10), db=_addr(11), dinit=None, ws=_addr(12), wsb=1 << 30)
+    a.update(kw)
+    return lib.gdn_chunk_bwd(a["q"], a["k"], a["v"], 0, 0, 0, a["dt"], a["g"], a["b"], 1.0, 1, 1e-6, a["hq"], a["hv"],
+                             a["d"], a["d"], a["cu"], a["n"], a["t"], a["init"], a["do"], a["dfin"], a["dq"], a["dk"],
+                             a["dv"], a["dg"], a["db"], a["dinit"], a["ws"], a["wsb"], None)
+
+
+def test_chunk_bwd_validation(lib):
+    assert chunk_bwd(lib, n=0) == L.GDN_OK
+    assert chunk_bwd(lib, t=-1) == L.GDN_ERR_INVALID
+    assert chunk_bwd(lib, g=None) == L.GDN_ERR_NULL
+    assert chunk_bwd(lib, do=None) == L.GDN_ERR_NULL
+    assert chunk_bwd(lib, dg=None) == L.GDN_ERR_NULL
+    assert chunk_bwd(lib, cu=None) == L.GDN_ERR_NULL            # several sequences need cu_seqlens
+    assert chunk_bwd(lib, d=16) == L.GDN_ERR_UNSUPPORTED        # bf16 needs d = 128
+    assert chunk_bwd(lib, d=64, dt=L.GDN_F32) == L.GDN_ERR_UNSUPPORTED
+    assert chunk_bwd(lib, ws=None) == L.GDN_ERR_WORKSPACE
+    assert chunk_bwd(lib, wsb=4096) == L.GDN_ERR_WORKSPACE
+    assert chunk_bwd(lib, dq=_addr(7) + 4) == L.GDN_ERR_ALIGN
+    assert chunk_bwd(lib, dq=_addr(0)) == L.GDN_ERR_ALIAS       # dq over q
+    assert chunk_bwd(lib, dk=_addr(7) + 1024) == L.GDN_ERR_ALIAS   # dk over dq
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_bwd_workspace_size(16, 32, 128, 128, 1, 4096, ctypes.byref(out)) == 0
+    slots = 4096 // 16 + 1
+    expect = slots * 32 * 128 * 128 * 4 + 2 * 4096 * 32 * 8 * 128 * 4 + 2 * 4096 * 32 * 8 * 4
+    assert out.value == expect
+
+
+def test_conv1d_bwd_validation(lib):
+    def call(**kw):
+        a = dict(x=_addr(0), dt=L.GDN_BF16, w=_addr(1), ch=1024, cu=_addr(2), n=2, t=10, h=None, dy=_addr(3),
+                 dho=None, dx=_addr(4), dw=_addr(5), dhi=None, ws=_addr(6), wsb=1 << 24)
+        a.update(kw)
+        return lib.gdn_conv1d_bwd(a["x"], a["dt"], a["w"], a["ch"], a["cu"], a["n"], a["t"], a["h"], a["dy"],
+                                  a["dho"], a["dx"], a["dw"], a["dhi"], a["ws"], a["wsb"], None)
+    assert call(n=0) == L.GDN_OK
+    assert call(ch=12) == L.GDN_ERR_INVALID
+    assert call(dw=None) == L.GDN_ERR_NULL
+    assert call(dy=None) == L.GDN_ERR_NULL
+    assert call(ws=None) == L.GDN_ERR_WORKSPACE
+    assert call(wsb=16) == L.GDN_ERR_WORKSPACE
+    assert call(dx=_addr(3)) == L.GDN_ERR_ALIAS                 # dx over dy
+    out = ctypes.c_size_t(0)
+    assert lib.gdn_conv1d_bwd_workspace_size(8192, 1, 4096, ctypes.byref(out)) == 0
+    assert out.value == (4096 // 8 + 1) * 8192 * 4 * 4
+
+
 def test_chunk_workspace_size(lib):
     out = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0

@@ -109,3 +109,38 @@ def test_chunk_bwd_full_size_sampled_heads(ops):
     assert all(e <= TOL for e in errs.values()), errs
     for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial"):
         assert torch.isfinite(out[key]).all(), key
+
+
+@pytest.mark.parametrize("name,lay,lengths", [("f32_tiny", I.TINY_LAYOUT, [40, 1, 2, 0, 23]),
+                                              ("bf16", SMALL, [150, 1, 64, 0, 70, 2])],
+                         ids=["f32_tiny", "bf16"])
+def test_conv1d_bwd_against_oracle(ops, name, lay, lengths):
+    """gdn_conv1d_bwd against the oracle's conv gradients: varlen with one-,
+    two-token and empty sequences, a history before the call and a gradient
+    on the history after it."""
+    note(f"conv bwd {name}: lengths {lengths}")
+    tdt = torch.bfloat16 if lay.dtype == "bf16" else torch.float32
+    d = I.prefill_inputs(53, lay, lengths, tail_std=1.0)
+    rng = np.random.default_rng(54)
+    T, n, ch = int(sum(lengths)), len(lengths), lay.channels
+    dy = rng.standard_normal((T, ch)).astype(np.float32)
+    dto = rng.standard_normal((n, 3, ch)).astype(np.float32)
+    dx = torch.full((T, ch), float("nan"), device=DEV)
+    dw = torch.full((ch, 4), float("nan"), device=DEV)
+    dti = torch.full((n, 3, ch), float("nan"), device=DEV)
+    ops.gdn_conv1d_bwd(dev(d["x"], tdt), dev(d["conv_w"], tdt), dev(dy), dx, dw,
+                       cu_seqlens=dev_i32(d["cu_seqlens"]), conv_state_in=dev(d["tail"], tdt),
+                       d_state_out=dev(dto), d_state_in=dti)
+    torch.cuda.synchronize()
+    ref = G.causal_conv1d_silu_grads(d["x"], d["conv_w"], d["tail"], d["cu_seqlens"], dy, dto)
+    errs = {"dx": rel_max(host(dx), ref["dx"]), "dw": rel_max(host(dw), ref["dw"]),
+            "d_state_in": rel_max(host(dti), ref["d_tail"])}
+    note("  " + ", ".join(f"{k_} {v_:.1e}" for k_, v_ in errs.items()))
+    assert all(e <= TOL for e in errs.values()), errs
+    # bitwise reruns
+    dw2 = torch.empty_like(dw)
+    ops.gdn_conv1d_bwd(dev(d["x"], tdt), dev(d["conv_w"], tdt), dev(dy), torch.empty_like(dx), dw2,
+                       cu_seqlens=dev_i32(d["cu_seqlens"]), conv_state_in=dev(d["tail"], tdt),
+                       d_state_out=dev(dto))
+    torch.cuda.synchronize()
+    assert torch.equal(dw, dw2)
