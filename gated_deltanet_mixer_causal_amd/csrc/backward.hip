@@ -641,14 +641,22 @@ __global__ __launch_bounds__(kCbThreads) void k_conv_bwd_hist(
   }
 }
 
-// dw[c][i] = sum over blocks of the partials, in block order.
+// dw[c][i] = sum over blocks of the partials, in a fixed order: eight running
+// sums over the blocks b = 8 m + j (eight independent loads in flight), then
+// added together.
 __global__ __launch_bounds__(256) void k_conv_bwd_dw(const float* __restrict__ dw_part, int channels, int64_t n_tblk,
                                                      float* __restrict__ dw) {
   const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // (channel, tap)
   if (e >= static_cast<int64_t>(channels) * 4) return;
-  float sacc = 0.f;
-  for (int64_t b = 0; b < n_tblk; ++b) sacc += dw_part[b * channels * 4 + e];
-  dw[e] = sacc;
+  const int64_t stride = static_cast<int64_t>(channels) * 4;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int64_t b = 0;
+  for (; b + 8 <= n_tblk; b += 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += dw_part[(b + j) * stride + e];
+  }
+  for (int j = 0; b + j < n_tblk; ++j) acc[j] += dw_part[(b + j) * stride + e];
+  dw[e] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 }
 
 size_t conv_bwd_ws_bytes(int channels, int n_seq, int64_t t_total) {
