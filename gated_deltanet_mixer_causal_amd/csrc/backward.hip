@@ -20,13 +20,15 @@
 //   k_bwd_ckpt    forward over each sequence, writing the state entering
 //                 every 16-token block (per slice) to the workspace.
 //   k_bwd_slice   per (sequence, v-head, 16-row slice), blocks last to
-//                 first: recompute from the block's checkpoint through the
-//                 block, keeping the state before each of its tokens in LDS,
-//                 then run the reverse step over its tokens.  A block's
-//                 inputs (normalised k, q; v, do of the slice; a, beta) are
-//                 staged in LDS first.  (The loop also serves checkpoints
-//                 every kBwdChunk > kBwdSub tokens, recomputing the sub-blocks
-//                 before the current one.)
+//                 first, and inside a block its second 8 tokens, then its
+//                 first 8: recompute from the block's checkpoint through the
+//                 half, keeping the state before each of its tokens in LDS,
+//                 then run the reverse step over them.  The sums over the
+//                 slice's rows (partial dq^, dk^, dbeta, dg) are left per wave
+//                 in LDS and finished once per half, so the reverse chain
+//                 waits at no barrier between tokens.  A block's inputs
+//                 (normalised k, q; v, do of the slice; a, beta) are staged in
+//                 LDS first.
 //   k_bwd_reduce  per (token, q/k head): sums the slice partials over the
 //                 slices and the v-heads that read this q/k head, applies the
 //                 L2-norm backward dx = (dx^ - x^ (x^ . dx^)) / |x|_eps, and
@@ -234,14 +236,15 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
     int h_qk, int h_v, const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const float* __restrict__ dout,
     const float* __restrict__ dfin, float* __restrict__ dv_out, float* __restrict__ dinit, BwdWs ws) {
   constexpr int TPR = D / 8, TILES = D / kBwdRows;
-  static_assert(NT >= kBwdRows * TPR && NT % 64 == 0, "one thread per (row, lane)");
-  static_assert(NT >= D, "one thread per column in the row reductions");
-  __shared__ BwdStage<D> sm;
-  __shared__ float stash[kBwdSub][kBwdRows][D];   // state before each token of the sub-block
   constexpr int NW = NT / 64;
-  __shared__ float red_q[NW][D];                   // per-wave column sums
-  __shared__ float red_k[NW][D];
-  __shared__ float red_s[NW][2];
+  constexpr int HALF = kBwdSub / 2;   // tokens whose states are stashed at once
+  static_assert(kBwdChunk == kBwdSub, "one staged block per checkpoint");
+  static_assert(NT >= kBwdRows * TPR && NT % 64 == 0, "one thread per (row, lane)");
+  __shared__ BwdStage<D> sm;
+  __shared__ float stash[HALF][kBwdRows][D];   // state before each token of the half block
+  __shared__ float red_q[HALF][NW][D];         // per-wave column sums of each token of the half
+  __shared__ float red_k[HALF][NW][D];
+  __shared__ float red_s[HALF][NW][2];
   const int64_t b = blockIdx.x;
   const int s = static_cast<int>(b / (static_cast<int64_t>(h_v) * TILES));
   const int h = static_cast<int>((b / TILES) % h_v), tile = static_cast<int>(b % TILES);
@@ -251,6 +254,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
   const int ca = 4 * l, cb = D / 2 + 4 * l;
   const bool row_ok = r < kBwdRows;
   const int rr = row_ok ? r : 0;
+  const int wv = tid >> 6, ln = tid & 63;
   const int64_t start = seq_start(cu, s, t_total), end = seq_start(cu, s + 1, t_total);
   const int64_t smat = (static_cast<int64_t>(s) * h_v + h) * D * D + static_cast<int64_t>(dv0 + rr) * D;
 
@@ -261,54 +265,52 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
     gs[0] = x.x; gs[1] = x.y; gs[2] = x.z; gs[3] = x.w; gs[4] = y.x; gs[5] = y.y; gs[6] = y.z; gs[7] = y.w;
   }
   const int64_t slot0 = start / kBwdChunk + s;
-  const int64_t nch = (end - start + kBwdChunk - 1) / kBwdChunk;
-  for (int64_t c = nch - 1; c >= 0; --c) {
+  const int64_t nblk = (end - start + kBwdChunk - 1) / kBwdChunk;
+  for (int64_t c = nblk - 1; c >= 0; --c) {
     const int64_t c0 = start + c * kBwdChunk;
-    const int64_t c1 = c0 + kBwdChunk < end ? c0 + kBwdChunk : end;
-    const int nsub = static_cast<int>((c1 - c0 + kBwdSub - 1) / kBwdSub);
+    const int n = static_cast<int>(end - c0 < kBwdChunk ? end - c0 : kBwdChunk);
     const float* ck = ws.ckpt + ((slot0 + c) * h_v + h) * static_cast<int64_t>(D) * D + static_cast<int64_t>(dv0 + rr) * D;
-    for (int sb = nsub - 1; sb >= 0; --sb) {
-      // recompute from the chunk's checkpoint to the state before sub-block sb,
-      // then through sb keeping the state before each of its tokens
+    bwd_stage<In, D, NT>(sm, q, k, v, dout, q_stride, k_stride, v_stride, gates, use_l2, l2_eps, h_v, h, hq, dv0, c0,
+                         n, true);
+    __syncthreads();
+    // the block's second half first, then its first half
+    for (int hf = (n > HALF ? 1 : 0); hf >= 0; --hf) {
+      const int j0 = hf * HALF;
+      const int nh = (n - j0 < HALF ? n - j0 : HALF);
+      // states: from the block's checkpoint through the half, keeping the
+      // state before each of its tokens
       float st[8];
       {
         const float4 x = *reinterpret_cast<const float4*>(ck + ca);
         const float4 y = *reinterpret_cast<const float4*>(ck + cb);
         st[0] = x.x; st[1] = x.y; st[2] = x.z; st[3] = x.w; st[4] = y.x; st[5] = y.y; st[6] = y.z; st[7] = y.w;
       }
-      int n = 0;
-      for (int bb = 0; bb <= sb; ++bb) {
-        const int64_t t0 = c0 + static_cast<int64_t>(bb) * kBwdSub;
-        n = static_cast<int>(c1 - t0 < kBwdSub ? c1 - t0 : kBwdSub);
-        bwd_stage<In, D, NT>(sm, q, k, v, dout, q_stride, k_stride, v_stride, gates, use_l2, l2_eps, h_v, h, hq, dv0,
-                             t0, n, bb == sb);
-        __syncthreads();
-        for (int j = 0; j < n; ++j) {
-          if (bb == sb && row_ok) {
+      for (int j = 0; j < j0; ++j) bwd_fwd_token<D>(st, sm, j, r, ca, cb);
+      for (int j = 0; j < nh; ++j) {
+        if (row_ok) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              stash[j][r][ca + i] = st[i];
-              stash[j][r][cb + i] = st[4 + i];
-            }
+          for (int i = 0; i < 4; ++i) {
+            stash[j][r][ca + i] = st[i];
+            stash[j][r][cb + i] = st[4 + i];
           }
-          bwd_fwd_token<D>(st, sm, j, r, ca, cb);
         }
-        if (bb < sb) __syncthreads();   // the next sub-block is staged over these inputs
+        if (j + 1 < nh) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
       }
       __syncthreads();   // the stash is complete
-      // reverse over the sub-block's tokens
-      const int64_t tb = c0 + static_cast<int64_t>(sb) * kBwdSub;
-      for (int j = n - 1; j >= 0; --j) {
-        const int64_t t = tb + j;
+      // reverse over the half's tokens; the sums over the slice's rows are left
+      // per wave in LDS and finished once for the whole half
+      for (int j = nh - 1; j >= 0; --j) {
+        const int jt = j0 + j;   // token within the block
+        const int64_t t = c0 + jt;
         float kk[8], qq[8], sp[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          kk[i] = sm.k[j][ca + i]; kk[4 + i] = sm.k[j][cb + i];
-          qq[i] = sm.q[j][ca + i]; qq[4 + i] = sm.q[j][cb + i];
+          kk[i] = sm.k[jt][ca + i]; kk[4 + i] = sm.k[jt][cb + i];
+          qq[i] = sm.q[jt][ca + i]; qq[4 + i] = sm.q[jt][cb + i];
           sp[i] = stash[j][rr][ca + i]; sp[4 + i] = stash[j][rr][cb + i];
         }
-        const float a = sm.a[j], bt = sm.b[j];
-        const float vr = sm.v[j][rr], dor = sm.dov[j][rr];
+        const float a = sm.a[jt], bt = sm.b[jt];
+        const float vr = sm.v[jt][rr], dor = sm.dov[jt][rr];
         float dk = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) { sp[i] *= a; dk += sp[i] * kk[i]; }   // sp: S' = a S_{t-1}
@@ -334,9 +336,8 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
         }
         pg = row_sum<TPR>(pg);
         if (row_ok && l == 0) dv_out[(t * h_v + h) * static_cast<int64_t>(D) + dv0 + r] = bt * u;
-        // sums over the slice's rows: first over the rows of this wave (lane
-        // bits at and above TPR; the row scalars are replicated over the row's
-        // lanes), then over the waves through LDS
+        // sums over the rows of this wave (lane bits at and above TPR; the row
+        // scalars are replicated over the row's lanes)
         float sbu = row_ok ? e * u : 0.f, sgg = row_ok ? pg : 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -352,36 +353,37 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
           sbu += __shfl_xor(sbu, off);
           sgg += __shfl_xor(sgg, off);
         }
-        const int wv = tid >> 6, ln = tid & 63;
         if (ln < TPR) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            red_q[wv][ca + i] = pq[i]; red_q[wv][cb + i] = pq[4 + i];
-            red_k[wv][ca + i] = pk[i]; red_k[wv][cb + i] = pk[4 + i];
+            red_q[j][wv][ca + i] = pq[i]; red_q[j][wv][cb + i] = pq[4 + i];
+            red_k[j][wv][ca + i] = pk[i]; red_k[j][wv][cb + i] = pk[4 + i];
           }
           if (ln == 0) {
-            red_s[wv][0] = sbu;
-            red_s[wv][1] = sgg;
+            red_s[j][wv][0] = sbu;
+            red_s[j][wv][1] = sgg;
           }
         }
-        __syncthreads();
-        const int64_t pbase = (t * h_v + h) * TILES + tile;
-        if (tid < D) {
-          float sq = 0.f, sk2 = 0.f;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) { sq += red_q[w][tid]; sk2 += red_k[w][tid]; }
-          ws.pdq[pbase * D + tid] = sq;
-          ws.pdk[pbase * D + tid] = sk2;
-        }
-        if (tid == 0) {
-          float sb_ = 0.f, sg = 0.f;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) { sb_ += red_s[w][0]; sg += red_s[w][1]; }
-          ws.pdb[pbase] = sb_;
-          ws.pdg[pbase] = sg;
-        }
-        __syncthreads();
       }
+      __syncthreads();   // every wave's sums of the half are in LDS
+      for (int e2 = tid; e2 < nh * D; e2 += NT) {
+        const int j = e2 / D, col = e2 % D;
+        const int64_t pbase = ((c0 + j0 + j) * h_v + h) * TILES + tile;
+        float sq = 0.f, sk2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) { sq += red_q[j][w][col]; sk2 += red_k[j][w][col]; }
+        ws.pdq[pbase * D + col] = sq;
+        ws.pdk[pbase * D + col] = sk2;
+      }
+      if (tid < nh) {
+        const int64_t pbase = ((c0 + j0 + tid) * h_v + h) * TILES + tile;
+        float sb_ = 0.f, sg = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) { sb_ += red_s[tid][w][0]; sg += red_s[tid][w][1]; }
+        ws.pdb[pbase] = sb_;
+        ws.pdg[pbase] = sg;
+      }
+      __syncthreads();   // stash and sums are rewritten by the next half
     }
   }
   if (dinit && row_ok) {
