@@ -144,3 +144,25 @@ def test_conv1d_bwd_against_oracle(ops, name, lay, lengths):
                        d_state_out=dev(dto))
     torch.cuda.synchronize()
     assert torch.equal(dw, dw2)
+
+
+def test_chunk_bwd_single_sequence_without_cu(ops):
+    """One sequence with cu_seqlens NULL and no initial state: the same
+    gradients as the packed form with cu_seqlens = [0, T]."""
+    lay = I.TINY_LAYOUT
+    note("chunk bwd: one sequence, no cu_seqlens")
+    d = I.prefill_inputs(55, lay, [37], g_mode="tiny")
+    rng = np.random.default_rng(56)
+    T = 37
+    do = rng.standard_normal((T, lay.h_v, lay.d_v)).astype(np.float32)
+    q, k, v = I.split_qkv(d["x"], lay)
+    outs = [torch.empty((T, lay.h_qk, lay.d_k), device=DEV), torch.empty((T, lay.h_qk, lay.d_k), device=DEV),
+            torch.empty((T, lay.h_v, lay.d_v), device=DEV), torch.empty((T, lay.h_v), device=DEV),
+            torch.empty((T, lay.h_v), device=DEV)]
+    dinit = torch.empty((1, lay.h_v, lay.d_v, lay.d_k), device=DEV)
+    ops.gdn_chunk_bwd(dev(q), dev(k), dev(v), dev(d["g"]), dev(d["beta"]), dev(do), *outs, d_initial=dinit)
+    torch.cuda.synchronize()
+    ref = G.gated_delta_rule_grads(q, k, v, d["g"], d["beta"], do)
+    for name, got in zip(("dq", "dk", "dv", "dg", "dbeta"), outs):
+        assert rel_max(host(got), ref[name]) <= TOL, name
+    assert rel_max(host(dinit), ref["d_initial"]) <= TOL

@@ -167,3 +167,35 @@ def test_mixed_batch(ops, name):
     torch.cuda.synchronize()
     assert torch.equal(o2, o[rows_d]), "mixed call differs from the compacted plain call"
     assert torch.equal(fin, state[dev_i32([slots[s] for s in act_seq]).long()])
+
+
+def test_mixed_batch_all_inactive_or_empty(ops):
+    """Capacity-only calls: every sequence inactive or empty (fresh ones zero
+    their slots), no live token rows; nothing else is written."""
+    lay = SMALL
+    note("mixed batch: all inactive or empty")
+    n_slots, t_cap = 6, 10
+    lengths = [0, 0, 0, 0]
+    slots = np.array([2, -1, 4, -1], np.int32)
+    fresh = np.array([1, 0, 0, 1], np.int32)
+    d = I.mixed_batch_inputs(71, lay, [1], n_slots, t_pad=t_cap - 1)   # pools and row shapes only
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32, device="cuda:0")
+    x = dev(d["x"], torch.bfloat16)
+    tail = dev(d["tail_pool"], torch.bfloat16)
+    tail0 = tail.clone()
+    y_conv = torch.full((t_cap, lay.channels), float("nan"), dtype=torch.bfloat16, device=x.device)
+    ops.gdn_conv1d_mixed(x, dev(d["conv_w"], torch.bfloat16), tail, y_conv, cu_seqlens=cu, state_slots=dev_i32(slots),
+                         fresh=dev_i32(fresh))
+    q, k, v = ops.qkv_views(y_conv, lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+    state = dev(d["state_pool"])
+    state0 = state.clone()
+    o = torch.full((t_cap, lay.h_v, lay.d_v), float("nan"), device=x.device)
+    ops.gdn_chunk_mixed(q, k, v, dev(d["g"]), dev(d["beta"]), state, o, chunk=lay.chunk, cu_seqlens=cu,
+                        state_slots=dev_i32(slots), fresh=dev_i32(fresh), z=dev(d["z"], torch.bfloat16),
+                        norm_w=dev(d["norm_w"]))
+    torch.cuda.synchronize()
+    assert torch.isnan(y_conv.float()).all() and torch.isnan(o).all()
+    assert (state[2] == 0).all() and (tail[2] == 0).all()         # fresh, empty, active
+    for p in (0, 1, 3, 5):
+        assert torch.equal(state[p], state0[p]) and torch.equal(tail[p], tail0[p])
+    assert torch.equal(state[4], state0[4]) and torch.equal(tail[4], tail0[4])   # empty, not fresh
