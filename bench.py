@@ -10,7 +10,9 @@ RMSNorm epilogue writing bf16.  value = tokens/s.
 Decode (reported beside it): one step is the decode mixer for 64 requests,
 one token each -- gdn_conv1d_fwd in decode mode then gdn_recurrent_step with
 the fused norm -- on per-request fp32 states of 32 x 128 x 128; reported as
-state GB/s (2 x state bytes per step) and steps/s.
+state GB/s (2 x state bytes per step) and steps/s, and the same step through
+gdn_mixer_decode_step, which does the conv, the recurrence and the norm in one
+launch (bit-identical results).
 
 Fused gates (reported beside them): the chunk and decode calls again through
 gdn_chunk_fwd_gated / gdn_recurrent_step_gated, which form g and beta in their
@@ -267,6 +269,12 @@ def decode_leg(args, torch, np, ops, I):
         ops.gdn_recurrent_step(s["q"], s["k"], s["v"], inp["g"], inp["beta"], s["state"], s["o"], z=inp["z"],
                                norm_w=s["nw"])
 
+    def fused_step(i):
+        s = sets[i % len(sets)]
+        inp = steps_in[i % len(steps_in)]
+        ops.gdn_mixer_decode_step(inp["x"], s["w"], s["tail"], inp["g"], inp["beta"], s["state"], s["o"],
+                                  h_qk=lay.h_qk, z=inp["z"], norm_w=s["nw"])
+
     def rec_only(i):
         s = sets[i % len(sets)]
         inp = steps_in[i % len(steps_in)]
@@ -278,6 +286,7 @@ def decode_leg(args, torch, np, ops, I):
         ops.gdn_recurrent_step_gated(s["q"], s["k"], s["v"], gi["a"], gi["b"], gi["a_log"], s["state"], s["o"])
 
     ms, wall = timed(step, args.steps, args.warmup, torch)
+    ms_fused, _ = timed(fused_step, args.steps, args.warmup, torch)
     ms_rec, _ = timed(rec_only, args.steps, args.warmup, torch)
     rec_stats = call_stats(rec_only, max(args.steps, 50), args.warmup + args.steps, torch)
     ms_rec_gated, _ = timed(rec_gated, args.steps, args.warmup, torch)
@@ -292,7 +301,7 @@ def decode_leg(args, torch, np, ops, I):
     # per request: q, k, v, z (bf16), g, beta (fp32), o (bf16)
     small = n_req * (2 * lay.h_qk * lay.d_k * 2 + lay.h_v * lay.d_v * 2 + 2 * lay.h_v * 4 + lay.h_v * lay.d_v * 2)
     return dict(ms=ms, wall=wall, ms_rec=ms_rec, rec_stats=rec_stats, n_req=n_req, state_bytes=state_bytes,
-                small=small, ms_rec_gated=ms_rec_gated, ms_rec_warm=ms_rec_warm)
+                small=small, ms_rec_gated=ms_rec_gated, ms_rec_warm=ms_rec_warm, ms_fused=ms_fused)
 
 
 def serving_leg(args, torch, np, ops, I):
@@ -468,6 +477,8 @@ def main():
             "mixer_steps_per_s": round(1e3 / dc["ms"], 1),
             "mall_warm_state_GB_per_s": round(2 * dc["state_bytes"] / (dc["ms_rec_warm"] * 1e-3) / 1e9, 1),
             "ms_per_mixer_step": round(dc["ms"], 4),
+            "ms_per_mixer_step_one_launch": round(dc["ms_fused"], 4),
+            "one_launch_vs_two_launch": round(dc["ms_fused"] / dc["ms"], 4),
             "roofline": {"kernel": "gdn_recurrent_step", "bound": "hbm",
                          "achieved": round(alg / (dc["ms_rec"] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(alg / (dc["ms_rec"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

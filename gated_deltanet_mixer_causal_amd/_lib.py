@@ -64,6 +64,8 @@ PROTOTYPES = {
     "gdn_chunk_bwd_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i64, ctypes.POINTER(_sz)]),
     "gdn_conv1d_bwd": (_i32, [_p, _i32, _p, _i32, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "gdn_conv1d_bwd_workspace_size": (_i32, [_i32, _i32, _i64, ctypes.POINTER(_sz)]),
+    "gdn_mixer_decode_step": (_i32, [_p, _i32, _p, _p, _p, _p, _f32, _i32, _f32, _i32, _i32, _i32, _i32, _i32,
+                                     _p, _i32, _p, _p, _i32, _p, _p, _f32, _p]),
     "gdn_gated_rmsnorm": (_i32, [_p, _i32, _p, _i32, _p, _f32, _i64, _i32, _p, _i32, _p]),
     "gdn_status_string": (ctypes.c_char_p, [_i32]),
     "gdn_last_hip_error": (_i32, []),

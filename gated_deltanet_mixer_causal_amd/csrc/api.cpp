@@ -9,6 +9,7 @@
 
 #include "../../include/gdn.h"
 #include "launch.hpp"
+#include "mixer_decode.hpp"
 
 namespace {
 
@@ -633,6 +634,45 @@ gdn_status gdn_conv1d_bwd(const void* x, gdn_dtype dt, const void* w, int32_t ch
   a.dx = dx; a.dw = dw; a.dhist_in = d_state_in;
   a.workspace = workspace; a.stream = stream;
   return finish(gdn::launch_conv1d_bwd(a));
+}
+
+gdn_status gdn_mixer_decode_step(const void* x, gdn_dtype dt, const void* conv_w, void* conv_state,
+                                 const float* g, const float* beta, float scale, int32_t use_qk_l2norm, float l2_eps,
+                                 int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t n_req, float* state,
+                                 int32_t n_slots, const int32_t* state_slots, void* o, gdn_dtype o_dt, const void* z,
+                                 const float* norm_w, float norm_eps, void* stream) {
+  if (n_req < 0 || n_slots < 0) return GDN_ERR_INVALID;
+  if (n_req == 0) return GDN_OK;
+  if (!dt_valid(dt) || !dt_valid(o_dt)) return GDN_ERR_UNSUPPORTED;
+  if (h_qk <= 0 || h_v <= 0 || h_v % h_qk != 0) return GDN_ERR_INVALID;
+  if (d_k != 128 || d_v != 128 || h_v / h_qk > gdn::kMixerDecodeMaxGroup) return GDN_ERR_UNSUPPORTED;
+  if (!x || !conv_w || !conv_state || !g || !beta || !state || !o) return GDN_ERR_NULL;
+  if (z && !norm_w) return GDN_ERR_NULL;
+  if (!state_slots && n_slots < n_req) return GDN_ERR_INVALID;
+  if (!all_aligned({x, conv_w, conv_state, g, beta, state, state_slots, o, z, norm_w})) return GDN_ERR_ALIGN;
+  const int eb = dt_bytes(dt);
+  const int64_t ch = 2 * static_cast<int64_t>(h_qk) * d_k + static_cast<int64_t>(h_v) * d_v;
+  const Range rx{x, static_cast<uint64_t>(n_req) * ch * eb};
+  const Range rw{conv_w, static_cast<uint64_t>(ch) * 4 * eb};
+  const Range rh{conv_state, static_cast<uint64_t>(n_slots) * 3 * ch * eb};
+  const Range rs{state, static_cast<uint64_t>(n_slots) * h_v * d_v * d_k * 4};
+  const Range rg{g, static_cast<uint64_t>(n_req) * h_v * 4}, rb{beta, static_cast<uint64_t>(n_req) * h_v * 4};
+  const Range ro{o, static_cast<uint64_t>(n_req) * h_v * d_v * dt_bytes(o_dt)};
+  const Range rz{z, z ? static_cast<uint64_t>(n_req) * h_v * d_v * eb : 0};
+  const Range rnw{norm_w, z ? static_cast<uint64_t>(d_v) * 4 : 0};
+  const Range rsl{state_slots, state_slots ? static_cast<uint64_t>(n_req) * 4 : 0};
+  if (!disjoint(ro, {rx, rw, rh, rs, rg, rb, rz, rnw, rsl})) return GDN_ERR_ALIAS;
+  if (!disjoint(rh, {rx, rw, rs, rg, rb, rz, rnw, rsl})) return GDN_ERR_ALIAS;
+  if (!disjoint(rs, {rx, rw, rg, rb, rz, rnw, rsl})) return GDN_ERR_ALIAS;
+  gdn::MixerDecodeArgs a;
+  a.x = x; a.dt = dt; a.w = conv_w; a.conv_state = conv_state;
+  a.gate = gdn::GateSrc{g, beta, nullptr, nullptr, 0, 0, nullptr, nullptr};
+  a.scale = scale; a.use_l2 = use_qk_l2norm != 0; a.l2_eps = l2_eps;
+  a.h_qk = h_qk; a.h_v = h_v; a.n_req = n_req;
+  a.state = state; a.slots = state_slots;
+  a.o = o; a.o_dt = o_dt; a.z = z; a.norm_w = norm_w; a.norm_eps = norm_eps;
+  a.stream = stream;
+  return finish(gdn::launch_mixer_decode(a));
 }
 
 gdn_status gdn_gated_rmsnorm(const void* x, gdn_dtype x_dt, const void* z, gdn_dtype z_dt, const float* w, float eps,

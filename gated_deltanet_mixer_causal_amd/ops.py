@@ -272,6 +272,21 @@ def gdn_conv1d_bwd(x, w, dy, dx, dw, *, cu_seqlens=None, conv_state_in=None, d_s
     return dx, dw
 
 
+def gdn_mixer_decode_step(x, conv_w, conv_state, g, beta, state, o, *, h_qk, scale=1.0, use_qk_l2norm=True,
+                          l2_eps=1e-6, state_slots=None, z=None, norm_w=None, norm_eps=1e-6, stream=None):
+    """Conv step + recurrent step (+ gated RMSNorm with z) of one decode token per request
+    in one launch.  x [N, 2 Hqk dk + Hv dv] raw q|k|v; conv_w [Ch, 4]; conv_state
+    [slots, 3, Ch]; state [slots, Hv, dv, dk] fp32; o [N, Hv, dv]."""
+    n_req = x.shape[0]
+    h_v, d_v, d_k = state.shape[1], state.shape[2], state.shape[3]
+    st = L.load().gdn_mixer_decode_step(
+        _ptr(x), _dt(x), _ptr(conv_w), _ptr(conv_state), _ptr(g), _ptr(beta), float(scale),
+        int(bool(use_qk_l2norm)), float(l2_eps), h_qk, h_v, d_k, d_v, n_req, _ptr(state), state.shape[0],
+        _ptr(state_slots), _ptr(o), _dt(o), _ptr(z), _ptr(norm_w), float(norm_eps), _stream(stream))
+    L.check("gdn_mixer_decode_step", st)
+    return o
+
+
 def gdn_gated_rmsnorm(x, z, w, y, *, eps=1e-6, stream=None):
     """y = x / sqrt(mean(x^2) + eps) * w * SiLU(z) over the last dim (16 or 128)."""
     d = x.shape[-1]

@@ -465,6 +465,46 @@ gdn_status gdn_conv1d_bwd_workspace_size(int32_t channels, int32_t n_seq, int64_
                                          size_t* bytes /* host */);
 
 /*
+ * gdn_mixer_decode_step -- one decode token of the mixer in one launch: the
+ * width-4 conv step with SiLU over the raw projected q|k|v, then the gated
+ * delta rule step and, with z, the gated RMSNorm.
+ * (Conv: haskell-infer-demo README, "Architecture", and Flare core-design,
+ *  short-convolution paragraph; recurrence: the formula at the top of this
+ *  header; norm: haskell-infer-demo README, "Highlights".)
+ *
+ * The results are bit-identical to gdn_conv1d_fwd in decode form (cu_seqlens
+ * NULL) into a [n_req, channels] buffer of dt, followed by gdn_recurrent_step
+ * on the q, k and v column blocks of that buffer: the conv output is rounded
+ * to dt exactly as that buffer would hold it, and the recurrence and norm use
+ * the same arithmetic.  The conv output itself is not written.  One workgroup
+ * per (request, q/k head) does the conv of the channels it owns and then the
+ * recurrent step of the h_v / h_qk v-heads that read that q/k head.
+ *
+ *   x           [n_req, channels] of dt, channels = 2 h_qk d_k + h_v d_v: the
+ *               raw projected q | k | v of one token per request (read)
+ *   conv_w      [channels, 4] of dt (read)
+ *   conv_state  [n_slots, 3, channels] of dt, updated in place
+ *   g, beta, scale, use_qk_l2norm, l2_eps, h_qk, h_v: as gdn_recurrent_step
+ *   d_k, d_v    128 and 128; h_v / h_qk at most 8
+ *   state       [n_slots, h_v, d_v, d_k] fp32, updated in place
+ *   n_slots     rows of conv_state and of state (>= n_req when state_slots is NULL)
+ *   state_slots [n_req] int32 slot per request into both conv_state and state,
+ *               in [0, n_slots); NULL = identity; negative = inactive lane
+ *               (nothing read or written, o rows untouched)
+ *   o, o_dt, z, norm_w, norm_eps: as gdn_recurrent_step
+ * o must not overlap any input; conv_state and state must not overlap each
+ * other or the inputs.  n_req == 0 is a no-op.  Other d_k, d_v or a larger
+ * group return GDN_ERR_UNSUPPORTED (the two-call form covers them).
+ */
+gdn_status gdn_mixer_decode_step(const void* x, gdn_dtype dt, const void* conv_w, void* conv_state,
+                                 const float* g, const float* beta, float scale,
+                                 int32_t use_qk_l2norm, float l2_eps,
+                                 int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t n_req,
+                                 float* state, int32_t n_slots, const int32_t* state_slots,
+                                 void* o, gdn_dtype o_dt,
+                                 const void* z, const float* norm_w, float norm_eps, void* stream);
+
+/*
  * gdn_gated_rmsnorm -- y = x / sqrt(mean(x^2) + eps) * w * SiLU(z), per row of d.
  * (The gated RMSNorm of the GDN layers: haskell-infer-demo README,
  *  "Highlights", hybrid-architecture bullet, and "Architecture", gdn_norm.cu;

@@ -357,3 +357,27 @@ def test_rows_copy_validation(lib):
     assert rows_copy(lib, dst=_addr(0) + 8) == L.GDN_ERR_ALIGN
     assert rows_copy(lib, dr=_addr(0) + 4096) == L.GDN_ERR_ALIAS  # index array inside the destination
     assert rows_copy(lib, src=_addr(0) + (1 << 20)) == L.GDN_ERR_ALIAS   # partial overlap of two pools
+
+
+def mixer_step(lib, **kw):
+    a = dict(x=_addr(0), dt=L.GDN_BF16, w=_addr(1), cs=_addr(2), g=_addr(3), b=_addr(4), hq=2, hv=4, d=128, n=4,
+             st=_addr(5), ns=4, sl=None, o=_addr(6), odt=L.GDN_F32, z=None, nw=None)
+    a.update(kw)
+    return lib.gdn_mixer_decode_step(a["x"], a["dt"], a["w"], a["cs"], a["g"], a["b"], 1.0, 1, 1e-6, a["hq"],
+                                     a["hv"], a["d"], a["d"], a["n"], a["st"], a["ns"], a["sl"], a["o"], a["odt"],
+                                     a["z"], a["nw"], 1e-6, None)
+
+
+def test_mixer_decode_validation(lib):
+    assert mixer_step(lib, n=0) == L.GDN_OK
+    assert mixer_step(lib, n=-1) == L.GDN_ERR_INVALID
+    assert mixer_step(lib, hv=5) == L.GDN_ERR_INVALID           # h_v not a multiple of h_qk
+    assert mixer_step(lib, d=16) == L.GDN_ERR_UNSUPPORTED       # the fused form is for 128-wide heads
+    assert mixer_step(lib, hq=1, hv=16) == L.GDN_ERR_UNSUPPORTED  # group above 8
+    assert mixer_step(lib, ns=2) == L.GDN_ERR_INVALID           # identity slots need n_slots >= n_req
+    assert mixer_step(lib, cs=None) == L.GDN_ERR_NULL
+    assert mixer_step(lib, z=_addr(7)) == L.GDN_ERR_NULL        # z without norm_w
+    assert mixer_step(lib, sl=_addr(8) + 2) == L.GDN_ERR_ALIGN
+    assert mixer_step(lib, o=_addr(5) + 4096) == L.GDN_ERR_ALIAS   # o inside the state
+    assert mixer_step(lib, cs=_addr(0) + 256) == L.GDN_ERR_ALIAS   # history pool over x
+    assert mixer_step(lib, st=_addr(2) + 64) == L.GDN_ERR_ALIAS    # state over the history pool
