@@ -24,7 +24,7 @@
 //                 first 8: recompute from the block's checkpoint through the
 //                 half, keeping the state before each of its tokens in LDS,
 //                 then run the reverse step over them.  The sums over the
-//                 slice's rows (partial dq^, dk^, dbeta, dg) are left per wave
+//                 slice's rows (partial dq^, dk^, dbeta, dg) are left per half wave
 //                 in LDS and finished once per half, so the reverse chain
 //                 waits at no barrier between tokens.  A block's inputs
 //                 (normalised k, q; v, do of the slice; a, beta) are staged in
@@ -52,6 +52,16 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
+// v of lane i plus v of lane i ^ 16 without the LDS crossbar: gfx950's
+// v_permlane16_swap trades the odd 16-lane rows of its first operand with the
+// even rows of its second; given v twice, it leaves a lane's own value in one
+// result and its partner's in the other (lane layout checked on the device),
+// so their sum is the pair's sum, the same in both lanes of a pair.
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int W>
 __device__ __forceinline__ float row_sum(float v) {
   static_assert(W == 2 || W == 4 || W == 8 || W == 16, "groups inside one DPP row");
@@ -242,9 +252,11 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
   static_assert(NT >= kBwdRows * TPR && NT % 64 == 0, "one thread per (row, lane)");
   __shared__ BwdStage<D> sm;
   __shared__ float stash[HALF][kBwdRows][D];   // state before each token of the half block
-  __shared__ float red_q[HALF][NW][D];         // per-wave column sums of each token of the half
-  __shared__ float red_k[HALF][NW][D];
-  __shared__ float red_s[HALF][NW][2];
+  // column sums of each token of the half, two per wave (its 16-lane rows
+  // 0 + 1 and 2 + 3)
+  __shared__ float red_q[HALF][2 * NW][D];
+  __shared__ float red_k[HALF][2 * NW][D];
+  __shared__ float red_s[HALF][2 * NW][2];
   const int64_t b = blockIdx.x;
   const int s = static_cast<int>(b / (static_cast<int64_t>(h_v) * TILES));
   const int h = static_cast<int>((b / TILES) % h_v), tile = static_cast<int>(b % TILES);
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
         }
         pg = row_sum<TPR>(pg);
         if (row_ok && l == 0) dv_out[(t * h_v + h) * static_cast<int64_t>(D) + dv0 + r] = bt * u;
-        // sums over the rows of this wave (lane bits at and above TPR; the row
+        // sums over the rows of each half wave (lane bits TPR .. 4; the row
         // scalars are replicated over the row's lanes)
         float sbu = row_ok ? e * u : 0.f, sgg = row_ok ? pg : 0.f;
 #pragma unroll
@@ -344,7 +356,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
           if (!row_ok) pq[i] = pk[i] = 0.f;
         }
 #pragma unroll
-        for (int off = TPR; off < 64; off <<= 1) {
+        for (int off = TPR; off < 16; off <<= 1) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             pq[i] += __shfl_xor(pq[i], off);
@@ -353,15 +365,24 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
           sbu += __shfl_xor(sbu, off);
           sgg += __shfl_xor(sgg, off);
         }
-        if (ln < TPR) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pq[i] = pair_sum16(pq[i]);
+          pk[i] = pair_sum16(pk[i]);
+        }
+        sbu = pair_sum16(sbu);
+        sgg = pair_sum16(sgg);
+        // the two halves of the wave are summed with the other waves' partials
+        if ((ln & 31) < TPR) {
+          const int pw = 2 * wv + (ln >> 5);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            red_q[j][wv][ca + i] = pq[i]; red_q[j][wv][cb + i] = pq[4 + i];
-            red_k[j][wv][ca + i] = pk[i]; red_k[j][wv][cb + i] = pk[4 + i];
+            red_q[j][pw][ca + i] = pq[i]; red_q[j][pw][cb + i] = pq[4 + i];
+            red_k[j][pw][ca + i] = pk[i]; red_k[j][pw][cb + i] = pk[4 + i];
           }
-          if (ln == 0) {
-            red_s[j][wv][0] = sbu;
-            red_s[j][wv][1] = sgg;
+          if ((ln & 31) == 0) {
+            red_s[j][pw][0] = sbu;
+            red_s[j][pw][1] = sgg;
           }
         }
       }
@@ -371,7 +392,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
         const int64_t pbase = ((c0 + j0 + j) * h_v + h) * TILES + tile;
         float sq = 0.f, sk2 = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) { sq += red_q[j][w][col]; sk2 += red_k[j][w][col]; }
+        for (int w = 0; w < 2 * NW; ++w) { sq += red_q[j][w][col]; sk2 += red_k[j][w][col]; }
         ws.pdq[pbase * D + col] = sq;
         ws.pdk[pbase * D + col] = sk2;
       }
@@ -379,7 +400,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
         const int64_t pbase = ((c0 + j0 + tid) * h_v + h) * TILES + tile;
         float sb_ = 0.f, sg = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) { sb_ += red_s[tid][w][0]; sg += red_s[tid][w][1]; }
+        for (int w = 0; w < 2 * NW; ++w) { sb_ += red_s[tid][w][0]; sg += red_s[tid][w][1]; }
         ws.pdb[pbase] = sb_;
         ws.pdg[pbase] = sg;
       }
