@@ -52,13 +52,14 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// v of lane i plus v of lane i ^ 16 without the LDS crossbar: gfx950's
+// Two row-pair sums in one instruction, without the LDS crossbar: gfx950's
 // v_permlane16_swap trades the odd 16-lane rows of its first operand with the
-// even rows of its second; given v twice, it leaves a lane's own value in one
-// result and its partner's in the other (lane layout checked on the device),
-// so their sum is the pair's sum, the same in both lanes of a pair.
-__device__ __forceinline__ float pair_sum16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+// even rows of its second (lane layout checked on the device).  Given x and y
+// it leaves x0 | y0 | x2 | y2 in one result and x1 | y1 | x3 | y3 in the other
+// (rows of 16 lanes), so their sum holds x0 + x1 in row 0, y0 + y1 in row 1,
+// x2 + x3 in row 2 and y2 + y3 in row 3.
+__device__ __forceinline__ float pair_sums16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
   const int hq = h / (h_v / h_qk), dv0 = tile * kBwdRows;
   const int tid = threadIdx.x, r = tid / TPR, l = tid % TPR;
   const int ca = 4 * l, cb = D / 2 + 4 * l;
-  const bool row_ok = r < kBwdRows;
+  const bool row_ok = NT == kBwdRows * TPR || r < kBwdRows;
   const int rr = row_ok ? r : 0;
   const int wv = tid >> 6, ln = tid & 63;
   const int64_t start = seq_start(cu, s, t_total), end = seq_start(cu, s + 1, t_total);
@@ -365,25 +366,22 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
           sbu += __shfl_xor(sbu, off);
           sgg += __shfl_xor(sgg, off);
         }
+        // rows 0 and 2 of 16 lanes now hold the q partials of the wave's two
+        // halves, rows 1 and 3 the k partials; the halves are summed with the
+        // other waves' partials
+        float ps[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pq[i] = pair_sum16(pq[i]);
-          pk[i] = pair_sum16(pk[i]);
-        }
-        sbu = pair_sum16(sbu);
-        sgg = pair_sum16(sgg);
-        // the two halves of the wave are summed with the other waves' partials
-        if ((ln & 31) < TPR) {
-          const int pw = 2 * wv + (ln >> 5);
+        for (int i = 0; i < 8; ++i) ps[i] = pair_sums16(pq[i], pk[i]);
+        const float ps2 = pair_sums16(sbu, sgg);
+        if ((ln & 15) < TPR) {
+          const int pw = 2 * wv + (ln >> 5), odd = (ln >> 4) & 1;
+          float* dst = odd ? red_k[j][pw] : red_q[j][pw];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            red_q[j][pw][ca + i] = pq[i]; red_q[j][pw][cb + i] = pq[4 + i];
-            red_k[j][pw][ca + i] = pk[i]; red_k[j][pw][cb + i] = pk[4 + i];
+            dst[ca + i] = ps[i];
+            dst[cb + i] = ps[4 + i];
           }
-          if ((ln & 31) == 0) {
-            red_s[j][pw][0] = sbu;
-            red_s[j][pw][1] = sgg;
-          }
+          if ((ln & 15) == 0) red_s[j][pw][odd] = ps2;
         }
       }
       __syncthreads();   // every wave's sums of the half are in LDS
