@@ -298,8 +298,12 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
         const float4 y = *reinterpret_cast<const float4*>(ck + cb);
         st[0] = x.x; st[1] = x.y; st[2] = x.z; st[3] = x.w; st[4] = y.x; st[5] = y.y; st[6] = y.z; st[7] = y.w;
       }
-      for (int j = 0; j < j0; ++j) bwd_fwd_token<D>(st, sm, j, r, ca, cb);
-      for (int j = 0; j < nh; ++j) {
+      // (j0 is 0 or HALF; full halves run unrolled, without per-token branches)
+      if (j0 == HALF) {
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) bwd_fwd_token<D>(st, sm, j, r, ca, cb);
+      }
+      auto keep = [&](int j) {
         if (row_ok) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -307,12 +311,25 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
             stash[j][r][cb + i] = st[4 + i];
           }
         }
-        if (j + 1 < nh) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
+      };
+      if (nh == HALF) {
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+          keep(j);
+          if (j + 1 < HALF) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
+        }
+      } else {
+        for (int j = 0; j < nh; ++j) {
+          keep(j);
+          if (j + 1 < nh) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
+        }
       }
       __syncthreads();   // the stash is complete
       // reverse over the half's tokens; the sums over the slice's rows are left
       // per wave in LDS and finished once for the whole half
-      for (int j = nh - 1; j >= 0; --j) {
+      // (a full half runs unrolled without per-token branches, so one token's
+      // partial sums and stores can overlap the next token's dependent chain)
+      auto rev = [&](int j) {
         const int jt = j0 + j;   // token within the block
         const int64_t t = c0 + jt;
         float kk[8], qq[8], sp[8];
@@ -383,6 +400,12 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
           }
           if ((ln & 15) == 0) red_s[j][pw][odd] = ps2;
         }
+      };
+      if (nh == HALF) {
+#pragma unroll
+        for (int j = HALF - 1; j >= 0; --j) rev(j);
+      } else {
+        for (int j = nh - 1; j >= 0; --j) rev(j);
       }
       __syncthreads();   // every wave's sums of the half are in LDS
       for (int e2 = tid; e2 < nh * D; e2 += NT) {
