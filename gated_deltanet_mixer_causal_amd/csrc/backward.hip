@@ -28,7 +28,8 @@
 //                 in LDS and finished once per half, so the reverse chain
 //                 waits at no barrier between tokens.  A block's inputs
 //                 (normalised k, q; v, do of the slice; a, beta) are staged in
-//                 LDS first.
+//                 LDS first; both kernels load the next block's inputs into
+//                 registers while the current block runs.
 //   k_bwd_reduce  per (token, q/k head): sums the slice partials over the
 //                 slices and the v-heads that read this q/k head, applies the
 //                 L2-norm backward dx = (dx^ - x^ (x^ . dx^)) / |x|_eps, and
@@ -122,59 +123,89 @@ struct BwdStage {
   float b[kBwdSub];             // beta
 };
 
-// Stage tokens t0 .. t0 + n - 1 (n <= kBwdSub).  Thread layout: token
-// tid / TPR, columns 4l .. 4l+3 and D/2 + 4l .. of it (l = tid % TPR), the same
-// layout as the state rows, so the norms are TPR-lane sums.
+// Staging of tokens t0 .. t0 + n - 1 (n <= kBwdSub; rows past n repeat row
+// t0) in two parts, so that a block's global loads are in flight while the
+// previous block is computed: stage_fetch reads this thread's raw inputs into
+// registers, stage_put normalises k and q and writes the LDS block.  Thread
+// layout of k, q: token tid / TPR, columns 4l .. 4l+3 and D/2 + 4l .. of it
+// (l = tid % TPR), the same layout as the state rows, so the norms are
+// TPR-lane sums.
 template <class In, int D, int NT>
-__device__ __forceinline__ void bwd_stage(BwdStage<D>& sm, const typename In::T* __restrict__ q,
-                                          const typename In::T* __restrict__ k,
-                                          const typename In::T* __restrict__ v, const float* __restrict__ dout,
-                                          int64_t q_stride, int64_t k_stride, int64_t v_stride, const GateSrc& gates,
-                                          int use_l2, float l2_eps, int h_v, int h, int hq, int dv0, int64_t t0, int n,
-                                          bool with_q) {
+struct StageRegs {
+  static constexpr int kPer = (kBwdSub * kBwdRows + NT - 1) / NT;   // v, do entries per thread
+  float kk[8], qq[8], vv[kPer], dd[kPer], gv, bt;
+};
+
+template <class In, int D, int NT>
+__device__ __forceinline__ void stage_fetch(StageRegs<In, D, NT>& R, const typename In::T* __restrict__ q,
+                                            const typename In::T* __restrict__ k,
+                                            const typename In::T* __restrict__ v, const float* __restrict__ dout,
+                                            int64_t q_stride, int64_t k_stride, int64_t v_stride,
+                                            const GateSrc& gates, int h_v, int h, int hq, int dv0, int64_t t0, int n,
+                                            bool with_q) {
   constexpr int TPR = D / 8;
   const int tid = threadIdx.x;
   const int j = tid / TPR, l = tid % TPR;
   const int ca = 4 * l, cb = D / 2 + 4 * l;
   if (j < kBwdSub) {
     const int64_t t = t0 + (j < n ? j : 0);
-    float kk[8], qq[8];
     const typename In::T* kr = k + t * k_stride + static_cast<int64_t>(hq) * D;
     const typename In::T* qr = q + t * q_stride + static_cast<int64_t>(hq) * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kk[i] = In::load(kr, ca + i);
-      kk[4 + i] = In::load(kr, cb + i);
-      qq[i] = with_q ? In::load(qr, ca + i) : 0.f;
-      qq[4 + i] = with_q ? In::load(qr, cb + i) : 0.f;
+      R.kk[i] = In::load(kr, ca + i);
+      R.kk[4 + i] = In::load(kr, cb + i);
+      R.qq[i] = with_q ? In::load(qr, ca + i) : 0.f;
+      R.qq[4 + i] = with_q ? In::load(qr, cb + i) : 0.f;
     }
+  }
+#pragma unroll
+  for (int u = 0; u < R.kPer; ++u) {
+    const int e = tid + u * NT;
+    if (e < kBwdSub * kBwdRows) {
+      const int jj = e / kBwdRows, r = e % kBwdRows;
+      const int64_t t = t0 + (jj < n ? jj : 0);
+      R.vv[u] = In::load(v + t * v_stride + static_cast<int64_t>(h) * D, dv0 + r);
+      R.dd[u] = dout ? dout[(t * h_v + h) * static_cast<int64_t>(D) + dv0 + r] : 0.f;
+    }
+  }
+  if (tid < kBwdSub) load_gate(gates, t0 + (tid < n ? tid : 0), h, h_v, R.gv, R.bt);
+}
+
+template <class In, int D, int NT>
+__device__ __forceinline__ void stage_put(BwdStage<D>& sm, const StageRegs<In, D, NT>& R, int use_l2,
+                                          float l2_eps) {
+  constexpr int TPR = D / 8;
+  const int tid = threadIdx.x;
+  const int j = tid / TPR, l = tid % TPR;
+  const int ca = 4 * l, cb = D / 2 + 4 * l;
+  if (j < kBwdSub) {
     float sk = 0.f, sq = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; }
+    for (int i = 0; i < 8; ++i) { sk += R.kk[i] * R.kk[i]; sq += R.qq[i] * R.qq[i]; }
     sk = row_sum<TPR>(sk);
     sq = row_sum<TPR>(sq);
     const float rk = use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f;
     const float rq = use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sm.k[j][ca + i] = kk[i] * rk;
-      sm.k[j][cb + i] = kk[4 + i] * rk;
-      sm.q[j][ca + i] = qq[i] * rq;
-      sm.q[j][cb + i] = qq[4 + i] * rq;
+      sm.k[j][ca + i] = R.kk[i] * rk;
+      sm.k[j][cb + i] = R.kk[4 + i] * rk;
+      sm.q[j][ca + i] = R.qq[i] * rq;
+      sm.q[j][cb + i] = R.qq[4 + i] * rq;
     }
   }
-  for (int e = tid; e < kBwdSub * kBwdRows; e += NT) {
-    const int jj = e / kBwdRows, r = e % kBwdRows;
-    const int64_t t = t0 + (jj < n ? jj : 0);
-    sm.v[jj][r] = In::load(v + t * v_stride + static_cast<int64_t>(h) * D, dv0 + r);
-    sm.dov[jj][r] = dout ? dout[(t * h_v + h) * static_cast<int64_t>(D) + dv0 + r] : 0.f;
+#pragma unroll
+  for (int u = 0; u < R.kPer; ++u) {
+    const int e = tid + u * NT;
+    if (e < kBwdSub * kBwdRows) {
+      sm.v[e / kBwdRows][e % kBwdRows] = R.vv[u];
+      sm.dov[e / kBwdRows][e % kBwdRows] = R.dd[u];
+    }
   }
   if (tid < kBwdSub) {
-    const int64_t t = t0 + (tid < n ? tid : 0);
-    float gv, bt;
-    load_gate(gates, t, h, h_v, gv, bt);
-    sm.a[tid] = __expf(gv);
-    sm.b[tid] = bt;
+    sm.a[tid] = __expf(R.gv);
+    sm.b[tid] = R.bt;
   }
 }
 
@@ -211,7 +242,7 @@ __global__ __launch_bounds__(NT) void k_bwd_ckpt(
   const int hq = h / (h_v / h_qk), dv0 = tile * kBwdRows;
   const int tid = threadIdx.x, r = tid / TPR, l = tid % TPR;
   const int ca = 4 * l, cb = D / 2 + 4 * l;
-  const bool row_ok = r < kBwdRows;
+  const bool row_ok = NT == kBwdRows * TPR || r < kBwdRows;
   const int64_t start = seq_start(cu, s, t_total), end = seq_start(cu, s + 1, t_total);
   const int64_t srow = (static_cast<int64_t>(s) * h_v + h) * D * D + static_cast<int64_t>(dv0 + (row_ok ? r : 0)) * D;
   float st[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -220,7 +251,16 @@ __global__ __launch_bounds__(NT) void k_bwd_ckpt(
     const float4 y = *reinterpret_cast<const float4*>(init + srow + cb);
     st[0] = x.x; st[1] = x.y; st[2] = x.z; st[3] = x.w; st[4] = y.x; st[5] = y.y; st[6] = y.z; st[7] = y.w;
   }
+  static_assert(kBwdChunk == kBwdSub, "one staged block per checkpoint");
   const int64_t slot0 = start / kBwdChunk + s;
+  // block c + 1's inputs are fetched into registers while block c is computed
+  StageRegs<In, D, NT> nx;
+  auto fetch = [&](int64_t c0) {
+    const int n = static_cast<int>(end - c0 < kBwdSub ? end - c0 : kBwdSub);
+    stage_fetch<In, D, NT>(nx, q, k, v, nullptr, q_stride, k_stride, v_stride, gates, h_v, h, hq, dv0, c0, n,
+                           false);
+  };
+  if (start < end) fetch(start);
   for (int64_t c0 = start; c0 < end; c0 += kBwdChunk) {
     const int64_t slot = slot0 + (c0 - start) / kBwdChunk;
     if (row_ok) {
@@ -228,15 +268,17 @@ __global__ __launch_bounds__(NT) void k_bwd_ckpt(
       *reinterpret_cast<float4*>(dst + ca) = make_float4(st[0], st[1], st[2], st[3]);
       *reinterpret_cast<float4*>(dst + cb) = make_float4(st[4], st[5], st[6], st[7]);
     }
-    const int64_t c1 = c0 + kBwdChunk < end ? c0 + kBwdChunk : end;
-    for (int64_t t0 = c0; t0 < c1; t0 += kBwdSub) {
-      const int n = static_cast<int>(c1 - t0 < kBwdSub ? c1 - t0 : kBwdSub);
-      bwd_stage<In, D, NT>(sm, q, k, v, nullptr, q_stride, k_stride, v_stride, gates, use_l2, l2_eps, h_v, h, hq,
-                           dv0, t0, n, false);
-      __syncthreads();
+    const int n = static_cast<int>(end - c0 < kBwdSub ? end - c0 : kBwdSub);
+    stage_put<In, D, NT>(sm, nx, use_l2, l2_eps);
+    __syncthreads();
+    if (c0 + kBwdChunk < end) fetch(c0 + kBwdChunk);
+    if (n == kBwdSub) {
+#pragma unroll
+      for (int j = 0; j < kBwdSub; ++j) bwd_fwd_token<D>(st, sm, j, r, ca, cb);
+    } else {
       for (int j = 0; j < n; ++j) bwd_fwd_token<D>(st, sm, j, r, ca, cb);
-      __syncthreads();
     }
+    __syncthreads();
   }
 }
 
@@ -279,13 +321,21 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
   }
   const int64_t slot0 = start / kBwdChunk + s;
   const int64_t nblk = (end - start + kBwdChunk - 1) / kBwdChunk;
+  // block c - 1's inputs are fetched into registers while block c is computed
+  StageRegs<In, D, NT> nx;
+  auto fetch = [&](int64_t c) {
+    const int64_t c0 = start + c * kBwdChunk;
+    const int n = static_cast<int>(end - c0 < kBwdChunk ? end - c0 : kBwdChunk);
+    stage_fetch<In, D, NT>(nx, q, k, v, dout, q_stride, k_stride, v_stride, gates, h_v, h, hq, dv0, c0, n, true);
+  };
+  if (nblk > 0) fetch(nblk - 1);
   for (int64_t c = nblk - 1; c >= 0; --c) {
     const int64_t c0 = start + c * kBwdChunk;
     const int n = static_cast<int>(end - c0 < kBwdChunk ? end - c0 : kBwdChunk);
     const float* ck = ws.ckpt + ((slot0 + c) * h_v + h) * static_cast<int64_t>(D) * D + static_cast<int64_t>(dv0 + rr) * D;
-    bwd_stage<In, D, NT>(sm, q, k, v, dout, q_stride, k_stride, v_stride, gates, use_l2, l2_eps, h_v, h, hq, dv0, c0,
-                         n, true);
+    stage_put<In, D, NT>(sm, nx, use_l2, l2_eps);
     __syncthreads();
+    if (c > 0) fetch(c - 1);
     // the block's second half first, then its first half
     for (int hf = (n > HALF ? 1 : 0); hf >= 0; --hf) {
       const int j0 = hf * HALF;
