@@ -337,41 +337,57 @@ __global__ __launch_bounds__(NT) void k_bwd_slice(
     __syncthreads();
     if (c > 0) fetch(c - 1);
     // the block's second half first, then its first half
+    // The second half's pass computes the states before tokens 0 .. HALF-1 on
+    // its way from the checkpoint; they are kept in registers for the first
+    // half, which then needs no recompute.
+    float early[HALF][8];
+    bool have_early = false;
     for (int hf = (n > HALF ? 1 : 0); hf >= 0; --hf) {
       const int j0 = hf * HALF;
       const int nh = (n - j0 < HALF ? n - j0 : HALF);
-      // states: from the block's checkpoint through the half, keeping the
-      // state before each of its tokens
-      float st[8];
-      {
-        const float4 x = *reinterpret_cast<const float4*>(ck + ca);
-        const float4 y = *reinterpret_cast<const float4*>(ck + cb);
-        st[0] = x.x; st[1] = x.y; st[2] = x.z; st[3] = x.w; st[4] = y.x; st[5] = y.y; st[6] = y.z; st[7] = y.w;
-      }
-      // (j0 is 0 or HALF; full halves run unrolled, without per-token branches)
-      if (j0 == HALF) {
-#pragma unroll
-        for (int j = 0; j < HALF; ++j) bwd_fwd_token<D>(st, sm, j, r, ca, cb);
-      }
-      auto keep = [&](int j) {
+      auto put_stash = [&](int j, const float (&v8)[8]) {
         if (row_ok) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            stash[j][r][ca + i] = st[i];
-            stash[j][r][cb + i] = st[4 + i];
+            stash[j][r][ca + i] = v8[i];
+            stash[j][r][cb + i] = v8[4 + i];
           }
         }
       };
-      if (nh == HALF) {
+      if (have_early) {
+        // first half of a block whose second half ran: nh == HALF
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-          keep(j);
-          if (j + 1 < HALF) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
-        }
+        for (int j = 0; j < HALF; ++j) put_stash(j, early[j]);
       } else {
-        for (int j = 0; j < nh; ++j) {
-          keep(j);
-          if (j + 1 < nh) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
+        // states: from the block's checkpoint through the half, keeping the
+        // state before each of its tokens
+        float st[8];
+        {
+          const float4 x = *reinterpret_cast<const float4*>(ck + ca);
+          const float4 y = *reinterpret_cast<const float4*>(ck + cb);
+          st[0] = x.x; st[1] = x.y; st[2] = x.z; st[3] = x.w; st[4] = y.x; st[5] = y.y; st[6] = y.z; st[7] = y.w;
+        }
+        // (j0 is 0 or HALF; full halves run unrolled, without per-token branches)
+        if (j0 == HALF) {
+#pragma unroll
+          for (int j = 0; j < HALF; ++j) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) early[j][i] = st[i];
+            bwd_fwd_token<D>(st, sm, j, r, ca, cb);
+          }
+          have_early = true;
+        }
+        if (nh == HALF) {
+#pragma unroll
+          for (int j = 0; j < HALF; ++j) {
+            put_stash(j, st);
+            if (j + 1 < HALF) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
+          }
+        } else {
+          for (int j = 0; j < nh; ++j) {
+            put_stash(j, st);
+            if (j + 1 < nh) bwd_fwd_token<D>(st, sm, j0 + j, r, ca, cb);
+          }
         }
       }
       __syncthreads();   // the stash is complete
