@@ -700,17 +700,15 @@ __global__ __launch_bounds__(NT) void k_single_token(
   const int ca = 4 * l, cb = D / 2 + 4 * l;
   const int64_t smat = (static_cast<int64_t>(sslot) * h_v + h) * D * D;
 
-  float sv[PASSES][8], vv[PASSES];
+  float4 sa[PASSES], sb[PASSES];
+  float vv[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = part * RW + (rg + p * RPP < RW ? rg + p * RPP : 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sv[p][i] = 0.f;
+    sa[p] = sb[p] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (src) {
-      const float4 a4 = *reinterpret_cast<const float4*>(src + smat + static_cast<int64_t>(row) * D + ca);
-      const float4 b4 = *reinterpret_cast<const float4*>(src + smat + static_cast<int64_t>(row) * D + cb);
-      sv[p][0] = a4.x; sv[p][1] = a4.y; sv[p][2] = a4.z; sv[p][3] = a4.w;
-      sv[p][4] = b4.x; sv[p][5] = b4.y; sv[p][6] = b4.z; sv[p][7] = b4.w;
+      sa[p] = *reinterpret_cast<const float4*>(src + smat + static_cast<int64_t>(row) * D + ca);
+      sb[p] = *reinterpret_cast<const float4*>(src + smat + static_cast<int64_t>(row) * D + cb);
     }
     vv[p] = In::load(v + t * v_stride + static_cast<int64_t>(h) * D, row);
   }
@@ -726,9 +724,8 @@ __global__ __launch_bounds__(NT) void k_single_token(
   }
   float gv, bt;
   load_gate(gates, t, h, h_v, gv, bt);
-  float sk = 0.f, sq = 0.f, kq = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
+  float sk, sq, kq;
+  tok_sums8(kk, qq, sk, sq, kq);
   sk = group_sum<TPR>(sk);
   sq = group_sum<TPR>(sq);
   kq = group_sum<TPR>(kq);
@@ -740,22 +737,18 @@ __global__ __launch_bounds__(NT) void k_single_token(
   const float alpha = __expf(gv);
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    float dk = 0.f, dq = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { dk += sv[p][i] * kk[i]; dq += sv[p][i] * qq[i]; }
+    float dk = tok_dot8(sa[p], sb[p], kk);
+    float dq = tok_dot8(sa[p], sb[p], qq);
     dk = group_sum<TPR>(dk);
     dq = group_sum<TPR>(dq);
-    const float e = vv[p] - alpha * dk, be = bt * e;
+    const float e = tok_err(vv[p], alpha, dk), be = bt * e;
     if (rg + p * RPP < RW) {
       const int64_t row = part * RW + rg + p * RPP;
       if (fin) {
-        float nv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) nv[i] = alpha * sv[p][i] + be * kk[i];
-        *reinterpret_cast<float4*>(fin + smat + row * D + ca) = make_float4(nv[0], nv[1], nv[2], nv[3]);
-        *reinterpret_cast<float4*>(fin + smat + row * D + cb) = make_float4(nv[4], nv[5], nv[6], nv[7]);
+        *reinterpret_cast<float4*>(fin + smat + row * D + ca) = tok_upd4(alpha, sa[p], be, kk);
+        *reinterpret_cast<float4*>(fin + smat + row * D + cb) = tok_upd4(alpha, sb[p], be, kk + 4);
       }
-      if (l == 0) EO::store(o, (t * h_v + h) * static_cast<int64_t>(D) + row, scale * (alpha * dq + be * kq));
+      if (l == 0) EO::store(o, (t * h_v + h) * static_cast<int64_t>(D) + row, tok_out(scale, alpha, dq, be, kq));
     }
   }
 }

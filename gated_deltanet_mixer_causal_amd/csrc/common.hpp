@@ -119,6 +119,65 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ---- arithmetic of one recurrent token --------------------------------------
+//
+// Every kernel that runs the plain recurrence of one token (the decode step,
+// the verification columns, the one-launch decode mixer and the chunk path's
+// one-token sequences) forms these quantities with the helpers below.  Each
+// multiply-add is an explicit fused multiply-add and each other product is
+// rounded on its own, so the kernels round alike whatever contractions the
+// compiler would choose, and results that the interface promises to be
+// bit-identical across entry points stay so.
+
+// Partial sums of |k|^2, |q|^2 and k.q over one lane's 8 columns.
+__device__ __forceinline__ void tok_sums8(const float* kk, const float* qq, float& sk, float& sq, float& kq) {
+  sk = kk[0] * kk[0];
+  sq = qq[0] * qq[0];
+  kq = kk[0] * qq[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    sk = __builtin_fmaf(kk[i], kk[i], sk);
+    sq = __builtin_fmaf(qq[i], qq[i], sq);
+    kq = __builtin_fmaf(kk[i], qq[i], kq);
+  }
+}
+
+// One lane's part of a state row (columns a: 4, b: 4) dotted with x[8].
+__device__ __forceinline__ float tok_dot8(const float4& a, const float4& b, const float* x) {
+  float s = a.x * x[0];
+  s = __builtin_fmaf(a.y, x[1], s);
+  s = __builtin_fmaf(a.z, x[2], s);
+  s = __builtin_fmaf(a.w, x[3], s);
+  s = __builtin_fmaf(b.x, x[4], s);
+  s = __builtin_fmaf(b.y, x[5], s);
+  s = __builtin_fmaf(b.z, x[6], s);
+  return __builtin_fmaf(b.w, x[7], s);
+}
+
+// e = v - a (S k^)_row: the row's prediction error after the decay.
+__device__ __forceinline__ float tok_err(float v, float alpha, float sk_row) {
+  return __builtin_fmaf(-alpha, sk_row, v);
+}
+
+// o_row = scale (a (S q^)_row + (beta e) (k^ . q^)).
+__device__ __forceinline__ float tok_out(float scale, float alpha, float sq_row, float be, float kq) {
+  return scale * __builtin_fmaf(kq, be, alpha * sq_row);
+}
+
+// New state element a s + (beta e) k^_col.
+__device__ __forceinline__ float tok_upd(float alpha, float s, float be, float kcol) {
+  return __builtin_fmaf(be, kcol, alpha * s);
+}
+__device__ __forceinline__ float4 tok_upd4(float alpha, const float4& s, float be, const float* kc) {
+  return make_float4(tok_upd(alpha, s.x, be, kc[0]), tok_upd(alpha, s.y, be, kc[1]),
+                     tok_upd(alpha, s.z, be, kc[2]), tok_upd(alpha, s.w, be, kc[3]));
+}
+
+// 1 / sqrt(mean of the d squares + eps) from their sum.
+__device__ __forceinline__ float norm_rinv(float sum_sq, float inv_d, float eps) {
+  return 1.0f / sqrtf(__builtin_fmaf(sum_sq, inv_d, eps));
+}
+
 // ---- per-(token, v-head) gates ---------------------------------------------
 
 // Where the log-decay g and the write strength beta of the gated delta rule

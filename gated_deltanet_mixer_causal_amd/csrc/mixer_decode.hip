@@ -117,8 +117,7 @@ __global__ __launch_bounds__(NT * PAR) void k_mixer_decode(
     qq[i] = yq[ca + i]; qq[4 + i] = yq[cb + i];
   }
   float sk = 0.f, sq = 0.f, kq = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
+  tok_sums8(kk, qq, sk, sq, kq);
   sk = group_sum<TPR>(sk);
   sq = group_sum<TPR>(sq);
   kq = group_sum<TPR>(kq);
@@ -147,22 +146,16 @@ __global__ __launch_bounds__(NT * PAR) void k_mixer_decode(
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         const int row = rg + p * RPP;
-        float dk = sa[p].x * kk[0] + sa[p].y * kk[1] + sa[p].z * kk[2] + sa[p].w * kk[3] +
-                   sb[p].x * kk[4] + sb[p].y * kk[5] + sb[p].z * kk[6] + sb[p].w * kk[7];
-        float dq = sa[p].x * qq[0] + sa[p].y * qq[1] + sa[p].z * qq[2] + sa[p].w * qq[3] +
-                   sb[p].x * qq[4] + sb[p].y * qq[5] + sb[p].z * qq[6] + sb[p].w * qq[7];
+        float dk = tok_dot8(sa[p], sb[p], kk);
+        float dq = tok_dot8(sa[p], sb[p], qq);
         dk = group_sum<TPR>(dk);
         dq = group_sum<TPR>(dq);
-        const float e = yv[hh][row] - alpha * dk;
+        const float e = tok_err(yv[hh][row], alpha, dk);
         const float be = bt * e;
-        // the contraction the unfused step's compiled code takes: kq * be fused,
-        // alpha * dq rounded (spelled out so both forms round alike)
-        orow[p] = scale * __builtin_fmaf(kq, be, alpha * dq);
+        orow[p] = tok_out(scale, alpha, dq, be, kq);
         float4 na, nb;
-        na.x = alpha * sa[p].x + be * kk[0]; na.y = alpha * sa[p].y + be * kk[1];
-        na.z = alpha * sa[p].z + be * kk[2]; na.w = alpha * sa[p].w + be * kk[3];
-        nb.x = alpha * sb[p].x + be * kk[4]; nb.y = alpha * sb[p].y + be * kk[5];
-        nb.z = alpha * sb[p].z + be * kk[6]; nb.w = alpha * sb[p].w + be * kk[7];
+        na = tok_upd4(alpha, sa[p], be, kk);
+        nb = tok_upd4(alpha, sb[p], be, kk + 4);
         md_stream_store4(S + row * D + ca, na);
         md_stream_store4(S + row * D + cb, nb);
       }
@@ -186,7 +179,7 @@ __global__ __launch_bounds__(NT * PAR) void k_mixer_decode(
 #pragma unroll
     for (int wv = 0; wv < NT / 64; ++wv) tot += sred[sub][wv];
     if (live && t2 < D) {
-      const float rr = 1.0f / sqrtf(tot * (1.0f / D) + norm_eps);
+      const float rr = norm_rinv(tot, 1.0f / D, norm_eps);
       EO::store(o, obase + t2, ov * rr * norm_w[t2] * silu(E::cvt(zraw)));
     }
     __syncthreads();   // so and sred are rewritten by the next round of v-heads

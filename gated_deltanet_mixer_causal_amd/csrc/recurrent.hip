@@ -109,8 +109,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
   typename E::T zraw = 0;
   if (z) zraw = z[obase + (tid < D ? tid : 0)];
   float sk = 0.f, sq = 0.f, kq = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
+  tok_sums8(kk, qq, sk, sq, kq);
   sk = group_sum<TPR>(sk);
   sq = group_sum<TPR>(sq);
   kq = group_sum<TPR>(kq);
@@ -125,21 +124,17 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = row0 + rg + p * RPP;
-    float dk = sa[p].x * kk[0] + sa[p].y * kk[1] + sa[p].z * kk[2] + sa[p].w * kk[3] +
-               sb[p].x * kk[4] + sb[p].y * kk[5] + sb[p].z * kk[6] + sb[p].w * kk[7];
-    float dq = sa[p].x * qq[0] + sa[p].y * qq[1] + sa[p].z * qq[2] + sa[p].w * qq[3] +
-               sb[p].x * qq[4] + sb[p].y * qq[5] + sb[p].z * qq[6] + sb[p].w * qq[7];
+    float dk = tok_dot8(sa[p], sb[p], kk);
+    float dq = tok_dot8(sa[p], sb[p], qq);
     dk = group_sum<TPR>(dk);
     dq = group_sum<TPR>(dq);
-    const float e = E::cvt(vraw[p]) - alpha * dk;
+    const float e = tok_err(E::cvt(vraw[p]), alpha, dk);
     const float be = bt * e;
-    orow[p] = scale * (alpha * dq + be * kq);
+    orow[p] = tok_out(scale, alpha, dq, be, kq);
     if (FULL || rg + p * RPP < RW) {
       float4 na, nb;
-      na.x = alpha * sa[p].x + be * kk[0]; na.y = alpha * sa[p].y + be * kk[1];
-      na.z = alpha * sa[p].z + be * kk[2]; na.w = alpha * sa[p].w + be * kk[3];
-      nb.x = alpha * sb[p].x + be * kk[4]; nb.y = alpha * sb[p].y + be * kk[5];
-      nb.z = alpha * sb[p].z + be * kk[6]; nb.w = alpha * sb[p].w + be * kk[7];
+      na = tok_upd4(alpha, sa[p], be, kk);
+      nb = tok_upd4(alpha, sb[p], be, kk + 4);
       stream_store4(S + row * D + ca, na);
       stream_store4(S + row * D + cb, nb);
     }
@@ -174,7 +169,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_step(
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) tot += sred[w];
   if (tid < D) {
-    const float rr = 1.0f / sqrtf(tot * (1.0f / D) + norm_eps);
+    const float rr = norm_rinv(tot, 1.0f / D, norm_eps);
     EO::store(o, obase + tid, ov * rr * norm_w[tid] * silu(E::cvt(zraw)));
   }
 }
@@ -238,8 +233,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_verify(
     typename E::T zraw = 0;
     if (z) zraw = z[obase + (tid < D ? tid : 0)];
     float sk = 0.f, sq = 0.f, kq = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) { sk += kk[i] * kk[i]; sq += qq[i] * qq[i]; kq += kk[i] * qq[i]; }
+    tok_sums8(kk, qq, sk, sq, kq);
     sk = group_sum<TPR>(sk);
     sq = group_sum<TPR>(sq);
     kq = group_sum<TPR>(kq);
@@ -255,20 +249,16 @@ __global__ __launch_bounds__(NT) void k_recurrent_verify(
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = rg + p * RPP;
-      float dk = sa[p].x * kk[0] + sa[p].y * kk[1] + sa[p].z * kk[2] + sa[p].w * kk[3] +
-                 sb[p].x * kk[4] + sb[p].y * kk[5] + sb[p].z * kk[6] + sb[p].w * kk[7];
-      float dq = sa[p].x * qq[0] + sa[p].y * qq[1] + sa[p].z * qq[2] + sa[p].w * qq[3] +
-                 sb[p].x * qq[4] + sb[p].y * qq[5] + sb[p].z * qq[6] + sb[p].w * qq[7];
+      float dk = tok_dot8(sa[p], sb[p], kk);
+      float dq = tok_dot8(sa[p], sb[p], qq);
       dk = group_sum<TPR>(dk);
       dq = group_sum<TPR>(dq);
-      const float e = E::cvt(vraw[p]) - alpha * dk;
+      const float e = tok_err(E::cvt(vraw[p]), alpha, dk);
       const float be = bt * e;
-      orow[p] = scale * (alpha * dq + be * kq);
+      orow[p] = tok_out(scale, alpha, dq, be, kq);
       float4 na, nb;
-      na.x = alpha * sa[p].x + be * kk[0]; na.y = alpha * sa[p].y + be * kk[1];
-      na.z = alpha * sa[p].z + be * kk[2]; na.w = alpha * sa[p].w + be * kk[3];
-      nb.x = alpha * sb[p].x + be * kk[4]; nb.y = alpha * sb[p].y + be * kk[5];
-      nb.z = alpha * sb[p].z + be * kk[6]; nb.w = alpha * sb[p].w + be * kk[7];
+      na = tok_upd4(alpha, sa[p], be, kk);
+      nb = tok_upd4(alpha, sb[p], be, kk + 4);
       sa[p] = na;
       sb[p] = nb;
       if (FULL || row < D) {
@@ -304,7 +294,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_verify(
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) tot += sred[w];
     if (tid < D) {
-      const float rr = 1.0f / sqrtf(tot * (1.0f / D) + norm_eps);
+      const float rr = norm_rinv(tot, 1.0f / D, norm_eps);
       EO::store(o, obase + tid, ov * rr * norm_w[tid] * silu(E::cvt(zraw)));
     }
     __syncthreads();   // so and sred are rewritten by the next token

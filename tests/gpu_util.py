@@ -70,3 +70,19 @@ def bf16_ulp_check(got, ref_rounded, ref_exact, max_frac=1e-3, abs_sum=None):
     frac = float(np.mean(diff > 0))
     assert frac <= max_frac, f"one-ulp disagreements {frac:.2e}"
     return frac
+
+
+def conv_check_all_channels(x, w, tail, cu, got, oracle, block=1024, max_frac=1e-3):
+    """bf16 conv output `got` [T, Ch] against the oracle's conv on every
+    channel, in blocks of channels so the float64 temporaries stay bounded.
+    Returns the fraction of one-ulp disagreements over all elements."""
+    x = np.asarray(x)
+    ch = x.shape[1]
+    n_diff = 0
+    for c0 in range(0, ch, block):
+        sl = slice(c0, min(ch, c0 + block))
+        exact, _ = oracle.causal_conv1d_silu(x[:, sl], w[sl], tail[:, :, sl], cu, round_to_bf16=False)
+        frac = bf16_ulp_check(got[:, sl], oracle.bf16_nearest(exact), exact, max_frac=max_frac,
+                              abs_sum=conv_abs_sum(x[:, sl], w[sl], tail[:, :, sl], cu))
+        n_diff += frac * exact.size
+    return n_diff / x.size

@@ -53,10 +53,18 @@ def _run(ops, lay, d, do, dfin, scale, use_l2, want_dinit=True):
     return out, (q, k, v)
 
 
+SMALL_F32 = I.Layout(h_qk=2, h_v=4, d_k=128, d_v=128, chunk=64, dtype="f32")
+
+# The reverse kernel walks 16-token blocks as two 8-token halves; a sequence's
+# last block holds 1..16 tokens.  The lengths below end blocks in 1, 5, 6, 7,
+# 8, 9, 13, 15 and 16 tokens, so the partial second half (9..15) is covered.
 CASES = [
     ("f32_d16", I.TINY_LAYOUT, [40, 1, 16, 0, 23], 0.7, True),
     ("f32_d16_nol2", I.TINY_LAYOUT, [33, 17], 1.0, False),
+    ("f32_d16_tails", I.TINY_LAYOUT, [25, 31, 1, 0, 45], 1.0, True),
     ("bf16_d128", SMALL, [150, 1, 64, 0, 70], 1.0, True),
+    ("bf16_d128_tails", SMALL, [25, 31, 1, 0, 45], 1.0, True),
+    ("f32_d128", SMALL_F32, [57, 1, 0, 40], 0.8, True),
 ]
 
 
@@ -89,9 +97,12 @@ def test_chunk_bwd_against_oracle(ops, name, lay, lengths, scale, use_l2):
 def test_chunk_bwd_full_size_sampled_heads(ops):
     """The model shape (one 4096-token sequence, 16 q/k and 32 v heads, bf16,
     model-like decays) through gdn_chunk_bwd on all heads; the oracle checks
-    v-heads 0 and 1 and the q/k head 0 they read (its dq, dk sum over both)."""
+    eight v-heads, the two of each of q/k heads 0, 5, 10 and 15 (so their dq,
+    dk, which sum over both v-heads, are compared too)."""
     lay = I.MODEL_LAYOUT
-    note("chunk bwd full size T=4096, sampled heads 0-1")
+    qk_heads = [0, 5, 10, 15]
+    hs = [2 * j + i for j in qk_heads for i in (0, 1)]
+    note(f"chunk bwd full size T=4096, v-heads {hs}")
     d = I.model_prefill_inputs(4096, seed=1)
     rng = np.random.default_rng(52)
     T = 4096
@@ -99,16 +110,17 @@ def test_chunk_bwd_full_size_sampled_heads(ops):
     dfin = (0.5 * rng.standard_normal((1, lay.h_v, lay.d_v, lay.d_k))).astype(np.float32)
     d["state"] = (0.02 * rng.standard_normal((1, lay.h_v, lay.d_v, lay.d_k))).astype(np.float32)
     out, (q, k, v) = _run(ops, lay, d, do, dfin, 1.0, True)
-    hs = [0, 1]
-    ref = G.gated_delta_rule_grads(q[:, :1], k[:, :1], v[:, hs], d["g"][:, hs], d["beta"][:, hs], do[:, hs],
-                                   dfin[:, hs], initial_state=d["state"][:, hs], qk_of_v=[0, 0])
-    got = dict(dq=host(out["dq"])[:, :1], dk=host(out["dk"])[:, :1], dv=host(out["dv"])[:, hs],
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial"):
+        assert torch.isfinite(out[key]).all(), key
+    note("  gradient oracle (about a minute)")
+    ref = G.gated_delta_rule_grads(q[:, qk_heads], k[:, qk_heads], v[:, hs], d["g"][:, hs], d["beta"][:, hs],
+                                   do[:, hs], dfin[:, hs], initial_state=d["state"][:, hs],
+                                   qk_of_v=[i // 2 for i in range(len(hs))])
+    got = dict(dq=host(out["dq"])[:, qk_heads], dk=host(out["dk"])[:, qk_heads], dv=host(out["dv"])[:, hs],
                dg=host(out["dg"])[:, hs], dbeta=host(out["dbeta"])[:, hs], d_initial=host(out["d_initial"])[:, hs])
     errs = {key: rel_max(got[key], ref[key]) for key in got}
     note("  " + ", ".join(f"{k_} {v_:.1e}" for k_, v_ in errs.items()))
     assert all(e <= TOL for e in errs.values()), errs
-    for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial"):
-        assert torch.isfinite(out[key]).all(), key
 
 
 @pytest.mark.parametrize("name,lay,lengths", [("f32_tiny", I.TINY_LAYOUT, [40, 1, 2, 0, 23]),

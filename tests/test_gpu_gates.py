@@ -132,9 +132,9 @@ def test_gated_recurrent_slots(ops, layout):
             np.testing.assert_array_equal(gs[s], ref_state[s])
 
 
-def test_gated_chunk_full_size_sampled_heads(ops):
+def test_gated_chunk_full_size_all_heads(ops):
     """T=4096, 16 q/k heads, 32 v heads, d=128, chunk 64, bf16 q/k/v and bf16
-    raw gates (the model workload's decay distribution), oracle on 3 v-heads."""
+    raw gates (the model workload's decay distribution), oracle on every v-head."""
     lay = I.MODEL_LAYOUT
     note("gated chunk T=4096 full model layout")
     T = 4096
@@ -150,13 +150,10 @@ def test_gated_chunk_full_size_sampled_heads(ops):
     ops.gdn_chunk_fwd_gated(q, k, v, ta, tb, dev(gt["a_log"]), o, chunk=64, cu_seqlens=dev_i32([0, T]),
                             final_state=fin)
     torch.cuda.synchronize()
-    heads = [3, 20, 30]
-    qk_heads = sorted({h // lay.group for h in heads})
     qh, kh, vh = I.split_qkv(qkv, lay)
-    g, beta = R.gates_from_projections(gt["a"][:, heads], gt["b"][:, heads], gt["a_log"][heads])
-    qk_of_v = [qk_heads.index(h // lay.group) for h in heads]
-    o_ref, f_ref = R.gated_delta_rule(qh[:, qk_heads], kh[:, qk_heads], vh[:, heads], g, beta, qk_of_v=qk_of_v)
-    eo = rel_max(host(o)[:, heads], o_ref)
-    ef = rel_max(host(fin)[0, heads], f_ref[0])
+    g, beta = R.gates_from_projections(gt["a"], gt["b"], gt["a_log"])
+    o_ref, f_ref = R.gated_delta_rule(qh, kh, vh, g, beta)
+    eo = rel_max(host(o), o_ref)
+    ef = rel_max(host(fin)[0], f_ref[0])
     note(f"  o {eo:.2e} state {ef:.2e}")
     assert eo <= TOL_BF16 and ef <= TOL_BF16

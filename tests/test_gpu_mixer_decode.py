@@ -73,7 +73,7 @@ def test_mixer_decode_step(ops, name, lay, fused_norm, odt):
         o_u = o_f.clone()
         ops.gdn_mixer_decode_step(x, w, tail_f, g, beta, state_f, o_f, h_qk=lay.h_qk, state_slots=sl, z=z,
                                   norm_w=nw if fused_norm else None)
-        y = torch.empty((n_req, ch), dtype=tdt, device=DEV)
+        y = torch.full((n_req, ch), 5.0, dtype=tdt, device=DEV)   # the inactive lane's row must stay 5
         ops.gdn_conv1d_fwd(x, w, tail_u, y, state_slots=sl)
         q = y[:, :nq].view(n_req, lay.h_qk, lay.d_k)
         k = y[:, nq:2 * nq].view(n_req, lay.h_qk, lay.d_k)
@@ -93,6 +93,7 @@ def test_mixer_decode_step(ops, name, lay, fused_norm, odt):
         for r, s in enumerate(slots):
             if s < 0:
                 assert np.all(got[r] == 3.0)
+                assert np.all(yh[r] == 5.0)
                 continue
             _, nt = R.causal_conv1d_silu(d["x"][step][r:r + 1], d["conv_w"], tail_r[s:s + 1], [0, 1],
                                          round_to_bf16=False)

@@ -656,3 +656,59 @@ def test_mixed_slot_permutation_and_continuation():
     np.testing.assert_array_equal(np.concatenate([o1["y"], o2["y"]]), out["y"][:9])
     np.testing.assert_array_equal(s2[0], states[0])
     np.testing.assert_array_equal(t2[0], tails[0])
+
+
+# ---------------------------------------------------------------------------
+# The whole mixer's channel split and head map, fixed by hand
+# ---------------------------------------------------------------------------
+
+def test_mixer_channel_split_and_head_map_by_hand():
+    """mixer_prefill's split of the conv output into q | k | v blocks and its
+    v-head -> q/k-head map, checked without split_heads.
+
+    With identity conv taps (tap 3 = 1), zero history, alpha = 1, beta = 1,
+    l2_eps = 0 and one-hot q and k rows, every token overwrites one column of
+    each v-head's state with that head's v row, and o reads one column:
+        S_h[:, ik(t, h // 2)] <- v_t,h    then    o_t,h = S_h[:, iq(t, h // 2)].
+    (x / sqrt(x^2) == 1 exactly in binary floating point, so the one-hot rows
+    stay one-hot through the L2 norm.)  The expected values are read from the
+    conv output at channel offsets written out here: q head j component i at
+    channel j*dk + i, k head j at Hqk*dk + j*dk + i, v head h component i at
+    2*Hqk*dk + h*dv + i.  Swapping the q and k blocks, misplacing v, swapping
+    d_k and d_v in a reshape or a different head grouping fails this test.
+    """
+    rng = np.random.default_rng(31)
+    hqk, hv, dk, dv, T = 2, 4, 4, 3, 9
+    ch = 2 * hqk * dk + hv * dv
+    iq = rng.integers(0, dk, (T, hqk))
+    ik = rng.integers(0, dk, (T, hqk))
+    x = np.zeros((T, ch))
+    for t in range(T):
+        for j in range(hqk):
+            x[t, j * dk + iq[t, j]] = 1.5 + j                    # q head j: one-hot
+            x[t, hqk * dk + j * dk + ik[t, j]] = 2.5 + j         # k head j: one-hot
+    x[:, 2 * hqk * dk:] = rng.standard_normal((T, hv * dv))     # v: dense, distinct
+    w = np.tile([0.0, 0.0, 0.0, 1.0], (ch, 1))
+    tail = np.zeros((1, 3, ch))
+    S0 = rng.standard_normal((1, hv, dv, dk))
+    g = np.zeros((T, hv))
+    beta = np.ones((T, hv))
+    z = rng.standard_normal((T, hv, dv))
+    nw = 1 + 0.1 * rng.standard_normal(dv)
+    out = R.mixer_prefill(x, w, tail, S0, beta, g, z, nw, [0, T], h_qk=hqk, h_v=hv, d_k=dk, d_v=dv,
+                          bf16_boundary=False, l2_eps=0.0)
+    yc = out["y_conv"]
+    S = S0[0].copy()
+    o_exp = np.zeros((T, hv, dv))
+    for t in range(T):
+        for h in range(hv):
+            j = h // (hv // hqk)
+            v_row = yc[t, 2 * hqk * dk + h * dv: 2 * hqk * dk + (h + 1) * dv]
+            S[h][:, ik[t, j]] = v_row
+            o_exp[t, h] = S[h][:, iq[t, j]]
+    np.testing.assert_allclose(out["o"], o_exp, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out["state"][0], S, rtol=0, atol=1e-14)
+    # the gate of the norm is read per (token, v-head) in the same order
+    np.testing.assert_allclose(out["y"], R.gated_rmsnorm(o_exp, z, nw, 1e-6), rtol=1e-14, atol=1e-15)
+    # and the hand-built q, k rows really are one-hot after the conv and SiLU
+    assert np.count_nonzero(yc[:, :2 * hqk * dk]) == 2 * hqk * T
