@@ -26,6 +26,9 @@ STATUS_NAMES = {0: "GDN_OK", 1: "GDN_ERR_NULL", 2: "GDN_ERR_INVALID", 3: "GDN_ER
 GDN_F32 = 0
 GDN_BF16 = 1
 
+# Size of the library-owned scratch array used by gdn_chunk_fwd_noalloc.
+GDN_NOALLOC_SCRATCH_BYTES = 128 << 20
+
 _p = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
@@ -38,6 +41,9 @@ PROTOTYPES = {
     "gdn_chunk_fwd": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _f32, _i32, _f32,
                              _i32, _i32, _i32, _i32, _i32, _p, _i32, _i64, _p, _p, _p, _i32,
                              _p, _p, _f32, _p, _sz, _p]),
+    "gdn_chunk_fwd_noalloc": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _f32, _i32, _f32,
+                                     _i32, _i32, _i32, _i32, _i32, _p, _i32, _i64, _p, _p, _p, _i32,
+                                     _p, _p, _f32, _p]),
     "gdn_chunk_fwd_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i64, _i32, _i32,
                                             ctypes.POINTER(_sz)]),
     "gdn_recurrent_step": (_i32, [_p, _p, _p, _i64, _i64, _i64, _i32, _p, _p, _f32, _i32, _f32,

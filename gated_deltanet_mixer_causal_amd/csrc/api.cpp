@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/gdn.h"
 #include "launch.hpp"
@@ -56,6 +57,44 @@ gdn_status finish(hipError_t e) {
     return GDN_ERR_HIP;
   }
   return GDN_OK;
+}
+
+// Workspace of gdn_chunk_fwd_noalloc: a library-owned device array, one copy
+// per GPU (the loader places it when the code object is first loaded on a
+// device, and it stays until the process ends).  In host code `scratch` names
+// a host-side stand-in, not device memory, so its device address is taken
+// once per device with hipGetSymbolAddress and only that address is used.
+static_assert(GDN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of this device's scratch (looked up on the first call on the
+// device), or nullptr with the HIP error recorded.
+void* device_scratch() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = static_cast<int32_t>(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    g_last_hip_error = static_cast<int32_t>(hipErrorInvalidDevice);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_hip_error = static_cast<int32_t>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
 }
 
 // The gates of a recurrence call as the caller passed them: fp32 g and beta,
@@ -350,6 +389,25 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v, int64_t q_
   return chunk_fwd_impl(q, k, v, q_stride, k_stride, v_stride, dt, plain_gates(g, beta), scale, use_qk_l2norm,
                         l2_eps, h_qk, h_v, d_k, d_v, chunk, cu_seqlens, n_seq, t_total, initial_state,
                         final_state, o, o_dt, z, norm_w, norm_eps, workspace, ws_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,
+                                 int64_t v_stride, gdn_dtype dt, const float* g, const float* beta, float scale,
+                                 int32_t use_qk_l2norm, float l2_eps, int32_t h_qk, int32_t h_v, int32_t d_k,
+                                 int32_t d_v, int32_t chunk, const int32_t* cu_seqlens, int32_t n_seq,
+                                 int64_t t_total, const float* initial_state, float* final_state, void* o,
+                                 gdn_dtype o_dt, const void* z, const float* norm_w, float norm_eps, void* stream) {
+  if (n_seq < 0 || t_total < 0) return GDN_ERR_INVALID;
+  if (n_seq == 0) return GDN_OK;
+  size_t need = 0;
+  gdn_status st = gdn_chunk_fwd_workspace_size(h_qk, h_v, d_k, d_v, chunk, n_seq, t_total, dt, z != nullptr, &need);
+  if (st != GDN_OK) return st;
+  if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return GDN_ERR_HIP;
+  return chunk_fwd_impl(q, k, v, q_stride, k_stride, v_stride, dt, plain_gates(g, beta), scale, use_qk_l2norm,
+                        l2_eps, h_qk, h_v, d_k, d_v, chunk, cu_seqlens, n_seq, t_total, initial_state,
+                        final_state, o, o_dt, z, norm_w, norm_eps, ws, GDN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 gdn_status gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,

@@ -82,6 +82,24 @@ def gdn_chunk_fwd(q, k, v, g, beta, o, *, chunk, scale=1.0, use_qk_l2norm=True, 
     return o
 
 
+def gdn_chunk_fwd_noalloc(q, k, v, g, beta, o, *, chunk, scale=1.0, use_qk_l2norm=True, l2_eps=1e-6,
+                          cu_seqlens=None, initial_state=None, final_state=None, z=None, norm_w=None,
+                          norm_eps=1e-6, stream=None):
+    """gdn_chunk_fwd with the library's own device scratch instead of a workspace
+    (for callers that cannot allocate); calls on one device must not overlap."""
+    t_total, h_qk, d_k = q.shape
+    h_v, d_v = v.shape[1], v.shape[2]
+    n_seq = cu_seqlens.numel() - 1 if cu_seqlens is not None else 1
+    st = L.load().gdn_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _rows_view(q, "q"), _rows_view(k, "k"), _rows_view(v, "v"), _dt(q),
+        _ptr(g), _ptr(beta), float(scale), int(bool(use_qk_l2norm)), float(l2_eps),
+        h_qk, h_v, d_k, d_v, chunk, _ptr(cu_seqlens), n_seq, t_total,
+        _ptr(initial_state), _ptr(final_state), _ptr(o), _dt(o),
+        _ptr(z), _ptr(norm_w), float(norm_eps), _stream(stream))
+    L.check("gdn_chunk_fwd_noalloc", st)
+    return o
+
+
 def gdn_recurrent_step(q, k, v, g, beta, state, o, *, scale=1.0, use_qk_l2norm=True, l2_eps=1e-6,
                        state_slots=None, z=None, norm_w=None, norm_eps=1e-6, stream=None):
     """One decode token per request.  q, k [N, Hqk, dk]; v [N, Hv, dv]; g, beta [N, Hv];

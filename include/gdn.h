@@ -31,8 +31,12 @@
  *   - A negative state slot marks an inactive lane: nothing is read for it
  *     and nothing is written, neither state nor output rows.
  *   - Device faults surface at the caller's next synchronisation.
- *   - The library is thread-safe across streams; it holds no global mutable
- *     state other than a thread-local last HIP error.
+ *   - The library is thread-safe across streams.  Its host-side state is a
+ *     thread-local last HIP error and caches filled on first use: the compute
+ *     unit count of each device, the resident workgroups per compute unit of
+ *     one kernel, and the device address of the scratch array of
+ *     gdn_chunk_fwd_noalloc on each device (which that entry point, and only
+ *     it, shares between calls).
  *
  * Layouts (row-major, last index fastest)
  *   conv input/output x, y   [t_total, channels], channels ordered q | k | v
@@ -155,6 +159,39 @@ gdn_status gdn_chunk_fwd(const void* q, const void* k, const void* v,
                          void* o, gdn_dtype o_dt,
                          const void* z, const float* norm_w, float norm_eps,
                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.
+ *
+ * Every argument and result is as for gdn_chunk_fwd, except that there is no
+ * workspace argument: the call uses a library-owned device array of
+ * GDN_NOALLOC_SCRATCH_BYTES on the current device instead, and allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).  The
+ * array is placed on each device when the library's code object is first
+ * loaded there and is held until the process ends; its address is looked up
+ * on the first call on each device.  The kernels need no initialised
+ * contents, so nothing is cleared between calls.
+ *
+ * A call whose workspace (gdn_chunk_fwd_workspace_size for the same
+ * arguments) exceeds GDN_NOALLOC_SCRATCH_BYTES returns GDN_ERR_WORKSPACE and
+ * writes nothing.  All calls on one device share that device's array: two
+ * calls that overlap in time on one device (different streams, threads or
+ * processes' copies aside) race and give undefined results, so the caller
+ * orders them, e.g. on one stream.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                 int64_t q_stride, int64_t k_stride, int64_t v_stride, gdn_dtype dt,
+                                 const float* g, const float* beta, float scale,
+                                 int32_t use_qk_l2norm, float l2_eps,
+                                 int32_t h_qk, int32_t h_v, int32_t d_k, int32_t d_v, int32_t chunk,
+                                 const int32_t* cu_seqlens, int32_t n_seq, int64_t t_total,
+                                 const float* initial_state, float* final_state,
+                                 void* o, gdn_dtype o_dt,
+                                 const void* z, const float* norm_w, float norm_eps, void* stream);
 
 /*
  * gdn_chunk_fwd_workspace_size -- (host) bytes of workspace gdn_chunk_fwd needs.
