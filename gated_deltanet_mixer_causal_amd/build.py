@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["api.cpp", "conv1d.hip", "norm.hip", "recurrent.hip", "chunk.hip", "state_ops.hip", "backward.hip", "mixer_decode.hip"]
+SOURCES = ["api.cpp", "conv1d.hip", "norm.hip", "recurrent.hip", "chunk.hip", "chunk_bf16.hip", "state_ops.hip", "backward.hip", "mixer_decode.hip"]
 ARCH = "gfx950"
 
 
@@ -35,6 +35,10 @@ def _flags(debug: bool) -> list[str]:
     f = [f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall",
          # packed fp32 instructions are kept out of generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # matrix-core accumulators in ordinary VGPRs: the kernels read them
+         # with vector instructions, which accumulation registers would need
+         # a copy for
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
     f += ["-O1", "-g"] if debug else ["-O3"]
     return f

@@ -1154,9 +1154,45 @@ static size_t ws_bytes_for(int h_qk, int h_v, int n_seq, int64_t t_total, int wi
 
 size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_seq, int64_t t_total,
                       int with_norm) {
-  if (dt == GDN_BF16) return ws_bytes_for<PolBF16, 128, 64>(h_qk, h_v, n_seq, t_total, with_norm);
+  if (dt == GDN_BF16) return chunk_bf16_ws_bytes(h_qk, h_v, n_seq, t_total, with_norm);
   if (d == 128) return ws_bytes_for<PolF32, 128, 64>(h_qk, h_v, n_seq, t_total, with_norm);
   return ws_bytes_for<PolF32, 16, 16>(h_qk, h_v, n_seq, t_total, with_norm);
+}
+
+hipError_t launch_seq_order(const int32_t* cu, int n_seq, int chunk, int32_t* order, hipStream_t st) {
+  hipLaunchKernelGGL(k_seq_order, dim3(1), dim3(kOrderBins), 0, st, cu, n_seq, chunk, order);
+  return hipGetLastError();
+}
+
+template <class In, int D>
+static hipError_t single_token_for(const ChunkArgs& a, float* o_pre) {
+  using T = typename In::T;
+  constexpr int NT1 = D == 128 ? 256 : 64, SPL = D == 128 ? 4 : 1;
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const int64_t nb1 = static_cast<int64_t>(a.n_seq) * a.h_v * SPL;
+  if (a.z)
+    hipLaunchKernelGGL((k_single_token<In, F32, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
+                       q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk,
+                       a.h_v, a.cu, a.n_seq, a.t_total, a.init, a.fin, a.slots, a.fresh, o_pre);
+  else if (a.o_dt == GDN_BF16)
+    hipLaunchKernelGGL((k_single_token<In, BF16, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
+                       q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk,
+                       a.h_v, a.cu, a.n_seq, a.t_total, a.init, a.fin, a.slots, a.fresh,
+                       static_cast<uint16_t*>(a.o));
+  else
+    hipLaunchKernelGGL((k_single_token<In, F32, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
+                       q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk,
+                       a.h_v, a.cu, a.n_seq, a.t_total, a.init, a.fin, a.slots, a.fresh, static_cast<float*>(a.o));
+  return hipGetLastError();
+}
+
+hipError_t launch_single_token(const ChunkArgs& a, float* o_pre) {
+  if (a.dt == GDN_BF16) return single_token_for<BF16, 128>(a, o_pre);
+  if (a.d == 128) return single_token_for<F32, 128>(a, o_pre);
+  return single_token_for<F32, 16>(a, o_pre);
 }
 
 template <class Pol, int D, int C>
@@ -1190,32 +1226,14 @@ static hipError_t run_chunk(const ChunkArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (ws.order) {
-    hipLaunchKernelGGL(k_seq_order, dim3(1), dim3(kOrderBins), 0, st, a.cu, a.n_seq, C, ws.order);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_seq_order(a.cu, a.n_seq, C, ws.order, st);
     if (e != hipSuccess) return e;
   }
   // One-token sequences: skipped only when a single sequence holds all of
   // several tokens (cu_seqlens ends at t_total, so it has no one-token
   // sequence); in a mixed call t_total is a capacity.
   if (a.n_seq > 1 || a.t_total == 1 || a.slots != nullptr) {
-    constexpr int NT1 = D == 128 ? 256 : 64, SPL = D == 128 ? 4 : 1;
-    using In = typename Pol::In;
-    const int64_t nb1 = static_cast<int64_t>(a.n_seq) * a.h_v * SPL;
-    float* const fin1 = a.fin;
-    if (a.z)
-      hipLaunchKernelGGL((k_single_token<In, F32, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
-                         q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk,
-                         a.h_v, a.cu, a.n_seq, a.t_total, a.init, fin1, a.slots, a.fresh, o_pre);
-    else if (a.o_dt == GDN_BF16)
-      hipLaunchKernelGGL((k_single_token<In, BF16, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0,
-                         st, q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps,
-                         a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total, a.init, fin1, a.slots, a.fresh,
-                         static_cast<uint16_t*>(a.o));
-    else
-      hipLaunchKernelGGL((k_single_token<In, F32, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
-                         q, k, v, a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk,
-                         a.h_v, a.cu, a.n_seq, a.t_total, a.init, fin1, a.slots, a.fresh, static_cast<float*>(a.o));
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_single_token(a, o_pre);
     if (e != hipSuccess) return e;
   }
   // One 16-wide d_v tile per workgroup: a single long sequence has only
@@ -1248,7 +1266,7 @@ static hipError_t run_chunk(const ChunkArgs& a) {
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {
   if (a.dt == GDN_BF16) {
-    if (a.d == 128 && a.chunk == 64) return run_chunk<PolBF16, 128, 64>(a);
+    if (a.d == 128 && a.chunk == 64) return run_chunk_bf16(a);
   } else {
     if (a.d == 128 && a.chunk == 64) return run_chunk<PolF32, 128, 64>(a);
     if (a.d == 16 && a.chunk == 16) return run_chunk<PolF32, 16, 16>(a);

@@ -198,30 +198,51 @@ struct GateSrc {
   const float* dt_bias;
 };
 
-// g and beta of token row t, v-head h.  softplus(x) is evaluated as
-// max(x, 0) + log1p(exp(-|x|)) and sigmoid(x) through exp(-|x|), so no
-// exponential overflows for any finite input.
-__device__ __forceinline__ void load_gate(const GateSrc& s, int64_t t, int h, int h_v, float& g, float& beta) {
+// The raw gate inputs of token row t, v-head h: the bits of g and beta, or of
+// the two gate projections (a bf16 value zero-extended).  Nothing here uses
+// the loaded values, so a caller can keep the loads in flight across other
+// work and convert later with gate_from_raw.
+__device__ __forceinline__ void gate_load_raw(const GateSrc& s, int64_t t, int h, int h_v, uint32_t& ra,
+                                              uint32_t& rb) {
   if (s.a == nullptr) {
     const int64_t i = t * h_v + h;
-    g = s.g[i];
-    beta = s.beta[i];
+    ra = __float_as_uint(s.g[i]);
+    rb = __float_as_uint(s.beta[i]);
+  } else if (s.ab_bf16) {
+    const int64_t i = t * s.ab_stride + h;
+    ra = static_cast<const uint16_t*>(s.a)[i];
+    rb = static_cast<const uint16_t*>(s.b)[i];
+  } else {
+    const int64_t i = t * s.ab_stride + h;
+    ra = __float_as_uint(static_cast<const float*>(s.a)[i]);
+    rb = __float_as_uint(static_cast<const float*>(s.b)[i]);
+  }
+}
+
+// g and beta from the raw inputs of v-head h.  softplus(x) is evaluated as
+// max(x, 0) + log1p(exp(-|x|)) and sigmoid(x) through exp(-|x|), so no
+// exponential overflows for any finite input.
+__device__ __forceinline__ void gate_from_raw(const GateSrc& s, int h, uint32_t ra, uint32_t rb, float& g,
+                                              float& beta) {
+  if (s.a == nullptr) {
+    g = __uint_as_float(ra);
+    beta = __uint_as_float(rb);
     return;
   }
-  const int64_t i = t * s.ab_stride + h;
-  float av, bv;
-  if (s.ab_bf16) {
-    av = bf16_bits_to_f32(static_cast<const uint16_t*>(s.a)[i]);
-    bv = bf16_bits_to_f32(static_cast<const uint16_t*>(s.b)[i]);
-  } else {
-    av = static_cast<const float*>(s.a)[i];
-    bv = static_cast<const float*>(s.b)[i];
-  }
+  const float av = s.ab_bf16 ? __uint_as_float(ra << 16) : __uint_as_float(ra);
+  const float bv = s.ab_bf16 ? __uint_as_float(rb << 16) : __uint_as_float(rb);
   const float x = av + (s.dt_bias ? s.dt_bias[h] : 0.f);
   const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
   g = -expf(s.a_log[h]) * sp;
   const float e = expf(-fabsf(bv));
   beta = bv >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+
+// g and beta of token row t, v-head h.
+__device__ __forceinline__ void load_gate(const GateSrc& s, int64_t t, int h, int h_v, float& g, float& beta) {
+  uint32_t ra, rb;
+  gate_load_raw(s, t, h, h_v, ra, rb);
+  gate_from_raw(s, h, ra, rb, g, beta);
 }
 
 // Sequence of a token-block slot.  Block j of sequence s (blocks of `blk`
