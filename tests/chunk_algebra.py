@@ -24,11 +24,12 @@ Form "gr" folds Tb into the two products that read U, so a chunk needs X only:
     O     = scale diag(b rq) Q S0^T + R X
     S_C^T = b_C S0^T + G X
 
-Form "pipe" is the bf16 scan kernel's form: the writes come pre-scaled for
-the state update, and a chunk's K S0^T is formed from the state one chunk
-back and the raw inter-chunk Gram matrix of K:
-    Tb'   = diag(exp(gamma_C - gamma) rk) Tb,   U2 = Tb' X
-    R     = P Tb,   O = scale diag(b rq) Q S0^T + R X
+Form "pipe" is the bf16 scan kernel's form: the writes W = Tb X serve the
+output through P, their decayed copy the state update, and a chunk's K S0^T
+is formed from the state one chunk back and the raw inter-chunk Gram matrix
+of K:
+    W     = Tb X,   U2 = diag(exp(gamma_C - gamma) rk) W
+    O     = scale diag(b rq) Q S0^T + P W
     S_C   = b_C S0 + U2^T K
     K_c S_c^T = b_C(c-1) K_c S_{c-1}^T + (K_c K_{c-1}^T) U2_{c-1}    (chunks after the first)
 """
@@ -169,10 +170,9 @@ def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_stat
                 O = scale * (b * rq)[:, :, None] * QS + P.mm(Rm, X, True, True, "hij,hjv->hiv")
                 S = P.store(b[:, -1][:, None, None] * S + P.mm(X, G, True, True, "hjv,hdj->hvd"))
             else:
-                Tb2 = P.store(dec[:, :, None] * Tb)
-                U2 = P.mm(Tb2, X, True, True, "hij,hjv->hiv")
-                Rm = P.store(np.einsum("hik,hkj->hij", Pm, Tb))   # formed in fp32 by the prep
-                O = scale * (b * rq)[:, :, None] * QS + P.mm(Rm, X, True, True, "hij,hjv->hiv")
+                W = P.mm(Tb, X, True, True, "hij,hjv->hiv")
+                U2 = P.store(W * dec[:, :, None])
+                O = scale * (b * rq)[:, :, None] * QS + P.mm(Pm, W, True, True, "hij,hjv->hiv")
                 prev = (K, S, U2, b[:, -1])
                 S = P.store(b[:, -1][:, None, None] * S + P.mm(U2, K, True, False, "hcv,hcd->hvd"))
             o[c0:c1] = O.transpose(1, 0, 2)

@@ -208,10 +208,10 @@ def test_chunk_workspace_size(lib):
         blk = 64 * 8 * 2   # one fragment block: 64 lanes x 8 bf16
         # per q/k head: K, Q and the chunk-to-previous-chunk Gram matrix (hi + lo)
         per_qk = al(slots * 16 * 16 * blk)
-        # per v-head: Tb' and R (hi + lo, six lower-triangular blocks each),
-        # and 132 fp32 scalars (c1, c2, the chunk decay)
+        # per v-head: Tb and P (hi + lo, six lower-triangular blocks each),
+        # and 196 fp32 scalars (c1, c2, c3, the chunk decay)
         per_v = al(slots * 32 * 12 * blk)
-        sc = al(slots * 32 * 132 * 4)
+        sc = al(slots * 32 * 196 * 4)
         order = al(4 * n_seq) if n_seq > 1 else 0
         return 3 * per_qk + 2 * per_v + sc + order
 
