@@ -35,6 +35,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -123,6 +124,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the gdn_chunk_bwd timing")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the varlen (8 packed sequences) and long-context (16 x 8192 + 256 decode) legs")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the speculative-verification and mixed prefill-plus-decode timings")
     ap.add_argument("--copy-probe", action="store_true",
@@ -385,27 +388,191 @@ def serving_leg(args, torch, np, ops, I):
                 state_bytes=state_bytes, lengths=lengths, ms_mixed=ms_mixed, t_live=int(sum(lengths)))
 
 
+def device_prefill_inputs(torch, I, lay, lengths, seed, *, state_std=None, tail_std=None):
+    """Seeded draws made on the device with the recipe of harness/inputs.py
+    (x, z ~ N(0,1) and conv w ~ N(0, 0.5) as bf16; beta = sigmoid(N(0,1));
+    g = -exp(A) softplus(N(0,1)) with A ~ U(0, ln 16) per v-head; norm w =
+    1 + 0.1 N(0,1); states N(0, state_std), tails N(0, tail_std) or zero), for
+    shapes whose host draws would take minutes.  Not the host stream's values:
+    timing only."""
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    T, n, ch = int(sum(lengths)), len(lengths), lay.channels
+
+    def rn(*shape, std=1.0):
+        return torch.randn(*shape, generator=gen, device=dev) * std
+
+    a_head = torch.rand(lay.h_v, generator=gen, device=dev) * math.log(16.0)
+    d = dict(x=rn(T, ch).to(torch.bfloat16), w=rn(ch, 4, std=0.5).to(torch.bfloat16),
+             beta=torch.sigmoid(rn(T, lay.h_v)),
+             g=-torch.exp(a_head)[None, :] * torch.nn.functional.softplus(rn(T, lay.h_v)),
+             z=rn(T, lay.h_v, lay.d_v).to(torch.bfloat16), nw=1.0 + 0.1 * rn(lay.d_v),
+             cu=torch.from_numpy(I.cu_from_lengths(lengths)).to(dev))
+    d["tail"] = (rn(n, 3, ch, std=tail_std) if tail_std is not None else torch.zeros(n, 3, ch, device=dev)
+                 ).to(torch.bfloat16)
+    d["state"] = (rn(n, lay.h_v, lay.d_v, lay.d_k, std=state_std) if state_std is not None
+                  else torch.zeros(n, lay.h_v, lay.d_v, lay.d_k, device=dev))
+    return d
+
+
+def varlen_leg(args, torch, ops, I):
+    """Varlen packed prefill: 8 sequences of log-uniform lengths in [512,
+    32768] (seed 3), nonzero initial states and conv tails carried in place;
+    conv, chunked rule with final states and the fused norm, bf16 outputs."""
+    lay = I.MODEL_LAYOUT
+    dev = "cuda:0"
+    lengths = I.c3_lengths()
+    T = int(sum(lengths))
+    d = device_prefill_inputs(torch, I, lay, lengths, 3, state_std=0.02, tail_std=1.0)
+    y_conv = torch.empty((T, lay.channels), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev)
+    q, k, v = ops.qkv_views(y_conv, lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+    ws = torch.empty(ops.gdn_chunk_fwd_workspace_size(lay.h_qk, lay.h_v, lay.d_k, lay.d_v, lay.chunk, len(lengths),
+                                                      T, torch.bfloat16, True), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        ops.gdn_conv1d_fwd(d["x"], d["w"], d["tail"], y_conv, cu_seqlens=d["cu"])
+        ops.gdn_chunk_fwd(q, k, v, d["g"], d["beta"], y, chunk=lay.chunk, cu_seqlens=d["cu"],
+                          initial_state=d["state"], final_state=d["state"], z=d["z"], norm_w=d["nw"], workspace=ws)
+
+    def chunk_only(i):
+        ops.gdn_chunk_fwd(q, k, v, d["g"], d["beta"], y, chunk=lay.chunk, cu_seqlens=d["cu"],
+                          initial_state=d["state"], final_state=d["state"], workspace=ws)
+
+    steps = max(2, args.steps // 4)
+    ms, _ = timed(step, steps, 2, torch)
+    ms_chunk, _ = timed(chunk_only, steps, 2, torch)
+    return dict(lengths=lengths, T=T, ms=ms, ms_chunk=ms_chunk)
+
+
+def long_context_leg(args, torch, ops, I):
+    """Long-context chunked prefill then decode, one sequence: 16 calls of
+    8192 tokens carrying the fp32 state and the conv history (fused norm, bf16
+    outputs), then 256 batch-1 decode steps (conv step, recurrent step with
+    the fused norm).  One run of the whole stream is one step."""
+    lay = I.MODEL_LAYOUT
+    dev = "cuda:0"
+    n_calls, call_len, n_dec = 16, 8192, 256
+    calls = [device_prefill_inputs(torch, I, lay, [call_len], 40 + i) for i in range(n_calls)]
+    dec = device_prefill_inputs(torch, I, lay, [n_dec], 60)
+    w, nw = calls[0]["w"], calls[0]["nw"]
+    tail = torch.zeros((1, 3, lay.channels), dtype=torch.bfloat16, device=dev)
+    state = torch.zeros((1, lay.h_v, lay.d_v, lay.d_k), device=dev)
+    y_conv = torch.empty((call_len, lay.channels), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((call_len, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev)
+    q, k, v = ops.qkv_views(y_conv, lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+    yc1 = torch.empty((1, lay.channels), dtype=torch.bfloat16, device=dev)
+    y1 = torch.empty((1, lay.h_v, lay.d_v), dtype=torch.bfloat16, device=dev)
+    q1, k1, v1 = ops.qkv_views(yc1, lay.h_qk, lay.d_k, lay.h_v, lay.d_v)
+    ws = torch.empty(ops.gdn_chunk_fwd_workspace_size(lay.h_qk, lay.h_v, lay.d_k, lay.d_v, lay.chunk, 1, call_len,
+                                                      torch.bfloat16, True), dtype=torch.uint8, device=dev)
+    cu = calls[0]["cu"]
+    stream = torch.cuda.current_stream()
+
+    def prefill():
+        for c in calls:
+            ops.gdn_conv1d_fwd(c["x"], w, tail, y_conv, cu_seqlens=cu)
+            ops.gdn_chunk_fwd(q, k, v, c["g"], c["beta"], y, chunk=lay.chunk, cu_seqlens=cu, initial_state=state,
+                              final_state=state, z=c["z"], norm_w=nw, workspace=ws)
+
+    def decode():
+        for t in range(n_dec):
+            ops.gdn_conv1d_fwd(dec["x"][t:t + 1], w, tail, yc1)
+            ops.gdn_recurrent_step(q1, k1, v1, dec["g"][t:t + 1], dec["beta"][t:t + 1], state, y1,
+                                   z=dec["z"][t:t + 1], norm_w=nw)
+
+    def chunk_call(i):
+        c = calls[i % n_calls]
+        ops.gdn_chunk_fwd(q, k, v, c["g"], c["beta"], y, chunk=lay.chunk, cu_seqlens=cu, initial_state=state,
+                          final_state=state, workspace=ws)
+
+    def rec_step(i):
+        t = i % n_dec
+        ops.gdn_recurrent_step(q1, k1, v1, dec["g"][t:t + 1], dec["beta"][t:t + 1], state, y1)
+
+    reps = 2
+    prefill()
+    decode()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    pre, dcd = [], []
+    for _ in range(reps):
+        state.zero_()
+        tail.zero_()
+        ev[0].record(stream)
+        prefill()
+        ev[1].record(stream)
+        decode()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        pre.append(ev[0].elapsed_time(ev[1]))
+        dcd.append(ev[1].elapsed_time(ev[2]))
+    ms_chunk, _ = timed(chunk_call, 16, 2, torch)
+    ms_rec, _ = timed(rec_step, 64, 4, torch)
+    return dict(n_calls=n_calls, call_len=call_len, n_dec=n_dec, ms_prefill=min(pre), ms_decode=min(dcd),
+                ms_chunk=ms_chunk, ms_rec=ms_rec)
+
+
 def cpu_baseline(np, I, R):
-    """Float64 oracle (conv -> gated delta rule -> gated norm) on the whole
-    prefill workload (4096 tokens, all 32 v-heads), single thread."""
+    """The float64 oracle timed on this host's cores on bounded samples of the
+    four workloads, all 32 v-heads, fewer tokens (the oracle walks tokens in
+    order at a cost per token that does not depend on sequence length, so a
+    rate in tokens/s carries over; decode steps scale with the request
+    count), once with one thread and once with every core the process may use:
+      C1  the whole 4096-token single-sequence prefill mixer (conv, recurrence, norm)
+      C2  16 of the 64 decode requests x 16 steps (steps/s scaled to 64 requests)
+      C3  the 8 packed sequences cut to 256 tokens each, nonzero states and tails
+      C4  4096 tokens of the long-context stream, and 32 batch-1 decode steps
+    Rates are for the whole workload: tokens/s, or steps/s for decode."""
+    import contextlib
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     lay = I.MODEL_LAYOUT
-    d = I.model_prefill_inputs()
-    n = 4096
-    import contextlib
-    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
-    with ctx:
+    affinity = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else list(range(os.cpu_count()))
+    kw = dict(h_qk=lay.h_qk, h_v=lay.h_v, d_k=lay.d_k, d_v=lay.d_v, bf16_boundary=True)
+
+    def prefill_rate(lengths, seed, state_std=None, tail_std=None):
+        d = I.prefill_inputs(seed, lay, lengths, state_std=state_std, tail_std=tail_std)
         t0 = time.perf_counter()
-        R.mixer_prefill(d["x"][:n], d["conv_w"], d["tail"], d["state"], d["beta"][:n], d["g"][:n], d["z"][:n],
-                        d["norm_w"], [0, n], h_qk=lay.h_qk, h_v=lay.h_v, d_k=lay.d_k, d_v=lay.d_v,
-                        bf16_boundary=True)
+        R.mixer_prefill(d["x"], d["conv_w"], d["tail"], d["state"], d["beta"], d["g"], d["z"], d["norm_w"],
+                        d["cu_seqlens"], **kw)
         dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"the whole B=1 T={n} prefill mixer (conv, recurrence, norm), all 32 v-heads, float64, 1 thread "
-                       f"({dt:.1f} s)")
+        return sum(lengths) / dt, dt
+
+    def decode_rate(n_req, n_steps, seed, full_req):
+        d = I.decode_inputs(seed, lay, n_req, n_steps)
+        tail, state = d["tail"].astype(np.float64), d["state"].copy()
+        t0 = time.perf_counter()
+        for t in range(n_steps):
+            R.mixer_decode_step(d["x"][t], d["conv_w"], tail, state, d["beta"][t], d["g"][t], d["z"][t],
+                                d["norm_w"], np.arange(n_req), **kw)
+        dt = time.perf_counter() - t0
+        return 1.0 / (dt / n_steps * full_req / n_req), dt
+
+    def run_all():
+        r, used = {}, 0.0
+        for key, fn in (("C1_tokens_per_s", lambda: prefill_rate([4096], 1)),
+                        ("C2_steps_per_s", lambda: decode_rate(16, 16, 2, 64)),
+                        ("C3_tokens_per_s", lambda: prefill_rate([256] * 8, 3, state_std=0.02, tail_std=1.0)),
+                        ("C4_prefill_tokens_per_s", lambda: prefill_rate([4096], 4)),
+                        ("C4_decode_steps_per_s", lambda: decode_rate(1, 32, 5, 1))):
+            r[key], t = fn()
+            used += t
+        return {k: round(v, 2) for k, v in r.items()}, used
+
+    limit = (lambda n: threadpool_limits(limits=n)) if threadpool_limits else (lambda n: contextlib.nullcontext())
+    with limit(1):
+        one, t_one = run_all()
+    with limit(len(affinity)):
+        allc, t_all = run_all()
+    return dict(value=allc["C1_tokens_per_s"], unit="tokens/s", cores=len(affinity), kind="oracle",
+                sample="C1: the whole B=1 T=4096 prefill mixer (conv, recurrence, norm), all 32 v-heads, float64, "
+                       "all cores the process may use (BLAS threads)",
+                cpu_count=os.cpu_count(), affinity=len(affinity), one_thread=one, all_cores=allc,
+                cpu_seconds_sampled={"one_thread": round(t_one, 1), "all_cores": round(t_all, 1)})
 
 
 def main():
@@ -523,6 +690,37 @@ def main():
                       "tokens_per_s": round(sv["t_live"] / (sv["ms_mixed"] * 1e-3), 1)},
             "buffer_sets": 1,
         }
+    if not args.no_workloads:
+        vl = varlen_leg(args, torch, ops, I)
+        vflop = FLOP_PER_TOKEN_HEAD * lay.h_v * vl["T"]
+        vtf = vflop / (vl["ms_chunk"] * 1e-3) / 1e12
+        out["varlen"] = {
+            "workload": f"8 packed sequences {vl['lengths']} ({vl['T']} tokens), nonzero states and conv tails, "
+                        "conv + chunked rule + fused norm, bf16 outputs, final states in place",
+            "tokens_per_s": round(vl["T"] / (vl["ms"] * 1e-3), 1), "ms_per_step": round(vl["ms"], 4),
+            "roofline": {"kernel": "gdn_chunk_fwd", "bound": "mfma", "achieved": round(vtf, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(vtf / PEAK_BF16_TFLOPS, 4),
+                         "avg_launch_ms": round(vl["ms_chunk"], 4), "algorithmic_flop_per_launch": vflop}}
+        lc = long_context_leg(args, torch, ops, I)
+        cflop = FLOP_PER_TOKEN_HEAD * lay.h_v * lc["call_len"]
+        ctf = cflop / (lc["ms_chunk"] * 1e-3) / 1e12
+        sb1 = lay.h_v * lay.d_v * lay.d_k * 4
+        rec_alg = 2 * sb1 + (2 * lay.h_qk * lay.d_k * 2 + lay.h_v * lay.d_v * 2 + 2 * lay.h_v * 4)
+        out["long_context"] = {
+            "workload": f"one sequence: {lc['n_calls']} chunked-prefill calls of {lc['call_len']} tokens carrying the "
+                        f"fp32 state and conv history (fused norm, bf16), then {lc['n_dec']} batch-1 decode steps",
+            "prefill_tokens_per_s": round(lc["n_calls"] * lc["call_len"] / (lc["ms_prefill"] * 1e-3), 1),
+            "prefill_ms": round(lc["ms_prefill"], 3),
+            "decode_steps_per_s": round(lc["n_dec"] / (lc["ms_decode"] * 1e-3), 1),
+            "decode_ms": round(lc["ms_decode"], 3),
+            "roofline": {"kernel": "gdn_chunk_fwd (one 8192-token call)", "bound": "mfma", "achieved": round(ctf, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ctf / PEAK_BF16_TFLOPS, 4),
+                         "avg_launch_ms": round(lc["ms_chunk"], 4), "algorithmic_flop_per_launch": cflop},
+            "decode_roofline": {"kernel": "gdn_recurrent_step (1 request)", "bound": "hbm",
+                                "achieved": round(rec_alg / (lc["ms_rec"] * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": round(rec_alg / (lc["ms_rec"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
+                                "avg_launch_ms": round(lc["ms_rec"], 4), "algorithmic_bytes_per_launch": rec_alg,
+                                "note": "2 MiB of state per step: launch-latency bound, far from the HBM roof"}}
     if not args.no_cpu_baseline:
         from oracle import gdn_ref as R
         out["cpu_baseline"] = cpu_baseline(np, I, R)

@@ -1154,7 +1154,7 @@ static size_t ws_bytes_for(int h_qk, int h_v, int n_seq, int64_t t_total, int wi
 
 size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_seq, int64_t t_total,
                       int with_norm) {
-  if (dt == GDN_BF16) return chunk_bf16_ws_bytes(h_qk, h_v, n_seq, t_total, with_norm);
+  if (dt == GDN_BF16) return ws_bytes_for<PolBF16, 128, 64>(h_qk, h_v, n_seq, t_total, with_norm);
   if (d == 128) return ws_bytes_for<PolF32, 128, 64>(h_qk, h_v, n_seq, t_total, with_norm);
   return ws_bytes_for<PolF32, 16, 16>(h_qk, h_v, n_seq, t_total, with_norm);
 }
@@ -1266,7 +1266,7 @@ static hipError_t run_chunk(const ChunkArgs& a) {
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {
   if (a.dt == GDN_BF16) {
-    if (a.d == 128 && a.chunk == 64) return run_chunk_bf16(a);
+    if (a.d == 128 && a.chunk == 64) return run_chunk<PolBF16, 128, 64>(a);
   } else {
     if (a.d == 128 && a.chunk == 64) return run_chunk<PolF32, 128, 64>(a);
     if (a.d == 16 && a.chunk == 16) return run_chunk<PolF32, 16, 16>(a);

@@ -125,10 +125,7 @@ int device_cu_count();
 
 size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_seq, int64_t t_total,
                       int with_norm);
-// The bf16, d = 128, chunk 64 path (csrc/chunk_bf16.hip) and the pieces of the
-// general chunk path it shares (csrc/chunk.hip).
-size_t chunk_bf16_ws_bytes(int h_qk, int h_v, int n_seq, int64_t t_total, int with_norm);
-hipError_t run_chunk_bf16(const ChunkArgs& a);
+// Pieces of the chunk path (csrc/chunk.hip).
 hipError_t launch_seq_order(const int32_t* cu, int n_seq, int chunk, int32_t* order, hipStream_t st);
 // The one-token sequences of a call (outputs to o_pre when a.z is set, else to a.o).
 hipError_t launch_single_token(const ChunkArgs& a, float* o_pre);

@@ -23,15 +23,6 @@ Form "gr" folds Tb into the two products that read U, so a chunk needs X only:
     G     = K^T diag(exp(gamma_C - gamma) rk) Tb   (dk x C)
     O     = scale diag(b rq) Q S0^T + R X
     S_C^T = b_C S0^T + G X
-
-Form "pipe" is the bf16 scan kernel's form: the writes W = Tb X serve the
-output through P, their decayed copy the state update, and a chunk's K S0^T
-is formed from the state one chunk back and the raw inter-chunk Gram matrix
-of K:
-    W     = Tb X,   U2 = diag(exp(gamma_C - gamma) rk) W
-    O     = scale diag(b rq) Q S0^T + P W
-    S_C   = b_C S0 + U2^T K
-    K_c S_c^T = b_C(c-1) K_c S_{c-1}^T + (K_c K_{c-1}^T) U2_{c-1}    (chunks after the first)
 """
 from __future__ import annotations
 
@@ -98,9 +89,8 @@ def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_stat
                              plan: str = "exact", form: str = "tx"):
     """Same contract as the oracle's gated_delta_rule, evaluated chunk by chunk.
     Chunks restart at every sequence start; the last chunk may be partial.
-    form "tx" forms U = Tb X; form "gr" uses R = P Tb and G = K^T diag(.) Tb;
-    form "pipe" the bf16 scan kernel's products (module docstring)."""
-    assert form in ("tx", "gr", "pipe")
+    form "tx" forms U = Tb X; form "gr" uses R = P Tb and G = K^T diag(.) Tb."""
+    assert form in ("tx", "gr")
     P = Plan(plan)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -118,7 +108,6 @@ def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_stat
     hq = np.arange(hv) // grp
     for s in range(n):
         S = P.store(S0[s].copy())                               # [Hv, dv, dk]
-        prev = None                                             # (K, S, U2, b_C) of the previous chunk
         for c0 in range(cu[s], cu[s + 1], chunk):
             c1 = min(c0 + chunk, cu[s + 1])
             C = c1 - c0
@@ -149,13 +138,7 @@ def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_stat
             T = P.store(T)
             Tb = P.store(T * bt[:, None, :])
             Pm = P.store(scale * gam_i * rq[:, :, None] * rk[:, None, :] * GQ)
-            if form == "pipe" and prev is not None:
-                Kp, Sp, U2p, bCp = prev
-                Gm = np.einsum("hid,hjd->hij", K, Kp)           # raw x raw, fp32 sums on the device
-                KS = P.store(bCp[:, None, None] * P.mm(K, Sp, False, True, "hcd,hvd->hcv")
-                             + P.mm(P.store(Gm), U2p, True, True, "hij,hjv->hiv"))
-            else:
-                KS = P.mm(K, S, False, True, "hcd,hvd->hcv")    # K S^T  [Hv, C, dv]
+            KS = P.mm(K, S, False, True, "hcd,hvd->hcv")        # K S^T  [Hv, C, dv]
             QS = P.mm(Q, S, False, True, "hcd,hvd->hcv")
             X = P.store(V - (b * rk)[:, :, None] * KS)
             dec = np.exp(gam[:, -1:] - gam) * rk                # [Hv, C]
@@ -164,17 +147,11 @@ def chunked_gated_delta_rule(q, k, v, g, beta, *, chunk, scale=1.0, initial_stat
                 O = scale * (b * rq)[:, :, None] * QS + P.mm(Pm, U, True, True, "hij,hjv->hiv")
                 Ud = P.store(U * dec[:, :, None])
                 S = P.store(b[:, -1][:, None, None] * S + P.mm(Ud, K, True, False, "hcv,hcd->hvd"))
-            elif form == "gr":
+            else:
                 Rm = P.mm(Pm, Tb, True, True, "hik,hkj->hij")
                 G = P.mm(K, P.store(dec[:, :, None] * Tb), False, True, "hcd,hcj->hdj")
                 O = scale * (b * rq)[:, :, None] * QS + P.mm(Rm, X, True, True, "hij,hjv->hiv")
                 S = P.store(b[:, -1][:, None, None] * S + P.mm(X, G, True, True, "hjv,hdj->hvd"))
-            else:
-                W = P.mm(Tb, X, True, True, "hij,hjv->hiv")
-                U2 = P.store(W * dec[:, :, None])
-                O = scale * (b * rq)[:, :, None] * QS + P.mm(Pm, W, True, True, "hij,hjv->hiv")
-                prev = (K, S, U2, b[:, -1])
-                S = P.store(b[:, -1][:, None, None] * S + P.mm(U2, K, True, False, "hcv,hcd->hvd"))
             o[c0:c1] = O.transpose(1, 0, 2)
         final[s] = S
     return o, final

@@ -202,26 +202,20 @@ def test_chunk_workspace_size(lib):
     out = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0
     slots = 4096 // 64 + 1
-
-    def layout(slots, n_seq):
-        al = lambda x: (x + 255) // 256 * 256
-        blk = 64 * 8 * 2   # one fragment block: 64 lanes x 8 bf16
-        # per q/k head: K, Q and the chunk-to-previous-chunk Gram matrix (hi + lo)
-        per_qk = al(slots * 16 * 16 * blk)
-        # per v-head: Tb and P (hi + lo, six lower-triangular blocks each),
-        # and 196 fp32 scalars (c1, c2, c3, the chunk decay)
-        per_v = al(slots * 32 * 12 * blk)
-        sc = al(slots * 32 * 196 * 4)
-        order = al(4 * n_seq) if n_seq > 1 else 0
-        return 3 * per_qk + 2 * per_v + sc + order
-
-    expect = layout(slots, 1)
+    # per q/k head: K and Q fragments (bf16); per v-head: Tb and P as bf16 hi+lo,
+    # fp32 scalars (the bf16 scan builds K^T from K in LDS)
+    expect = (slots * 16 * 2 * 64 * 128 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2 + slots * 32 * 4 * 64 * 4)
     assert out.value == expect
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 1, ctypes.byref(out)) == 0
     assert out.value == expect + 4096 * 32 * 128 * 4
     # several sequences: one slot more per sequence, and the longest-first order (int32 each)
     assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 8, 4096, L.GDN_BF16, 0, ctypes.byref(out)) == 0
-    assert out.value == layout(4096 // 64 + 8, 8)
+    slots = 4096 // 64 + 8
+    expect = (slots * 16 * 2 * 64 * 128 * 2 + 2 * slots * 32 * 2 * 64 * 64 * 2 + slots * 32 * 4 * 64 * 4 + 256)
+    assert out.value == expect
+    assert lib.gdn_chunk_fwd_workspace_size(16, 32, 128, 128, 64, 1, 4096, L.GDN_BF16, 0, None) == L.GDN_ERR_NULL
+    assert lib.gdn_chunk_fwd_workspace_size(16, 32, 64, 64, 64, 1, 4096, L.GDN_BF16, 0,
+                                            ctypes.byref(out)) == L.GDN_ERR_UNSUPPORTED
 
 
 def step(lib, **kw):

@@ -243,11 +243,7 @@ def test_long_context_16_calls_then_decode(ops):
     ops.gdn_chunk_fwd(q, k, v, g_all, b_all, y_one, chunk=64, cu_seqlens=cu_one, final_state=fin_one,
                       z=z_all, norm_w=nw)
     torch.cuda.synchronize()
-    e_y1 = max(rel_max(host(y_one[sl_].flatten(0, 1)), host(y_calls[sl_].flatten(0, 1)))
-               for sl_ in (slice(0, T // 2), slice(T // 2, T)))
-    e_f1 = rel_max(host(fin_one), host(state_prefill))
-    note(f"  16 calls against one call: y {e_y1:.2e} state {e_f1:.2e}")
-    assert e_y1 <= TOL_BF16 and e_f1 <= TOL_BF16
+    assert torch.equal(y_one, y_calls) and torch.equal(fin_one, state_prefill)
     del y_one
     # oracle: one run over the whole stream for the sampled heads
     note("  oracle, single shot over 131,328 tokens")
