@@ -214,24 +214,47 @@ __global__ __launch_bounds__(NT) void k_recurrent_verify(
     sb[p] = stream_load4(S + rr * D + cb);
   }
 
-  for (int t = 0; t < n_tok; ++t) {
-    const int64_t tr = static_cast<int64_t>(r) * n_tok + t;   // token row
+  // the token inputs are loaded one token ahead, so their latency falls under
+  // the previous token's work (the last token reloads its own: no branch)
+  struct TokIn {
     typename E::T vraw[PASSES];
+    typename E::T kr[8], qr[8];
+    uint32_t graw, braw;
+    typename E::T zraw;
+  };
+  auto load_tok = [&](int t, TokIn& ti) {
+    const int64_t tr = static_cast<int64_t>(r) * n_tok + t;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = rg + p * RPP;
-      vraw[p] = v[tr * v_stride + h * D + ((FULL || row < D) ? row : 0)];
+      ti.vraw[p] = v[tr * v_stride + h * D + ((FULL || row < D) ? row : 0)];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ti.kr[i] = k[tr * k_stride + hq * D + ca + i];
+      ti.kr[4 + i] = k[tr * k_stride + hq * D + cb + i];
+      ti.qr[i] = q[tr * q_stride + hq * D + ca + i];
+      ti.qr[4 + i] = q[tr * q_stride + hq * D + cb + i];
+    }
+    gate_load_raw(gates, tr, h, h_v, ti.graw, ti.braw);
+    ti.zraw = z ? z[(tr * h_v + h) * D + (tid < D ? tid : 0)] : typename E::T(0);
+  };
+  TokIn cur;
+  load_tok(0, cur);
+  for (int t = 0; t < n_tok; ++t) {
+    const int64_t tr = static_cast<int64_t>(r) * n_tok + t;   // token row
+    TokIn nxt;
+    load_tok(t + 1 < n_tok ? t + 1 : t, nxt);
     float kk[8], qq[8];
-    load4<E>(k + tr * k_stride + hq * D + ca, kk);
-    load4<E>(k + tr * k_stride + hq * D + cb, kk + 4);
-    load4<E>(q + tr * q_stride + hq * D + ca, qq);
-    load4<E>(q + tr * q_stride + hq * D + cb, qq + 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { kk[i] = E::cvt(cur.kr[i]); qq[i] = E::cvt(cur.qr[i]); }
     float gv, bt;
-    load_gate(gates, tr, h, h_v, gv, bt);
+    gate_from_raw(gates, h, cur.graw, cur.braw, gv, bt);
     const int64_t obase = (tr * h_v + h) * D;
-    typename E::T zraw = 0;
-    if (z) zraw = z[obase + (tid < D ? tid : 0)];
+    const typename E::T zraw = cur.zraw;
+    typename E::T vraw[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) vraw[p] = cur.vraw[p];
     float sk = 0.f, sq = 0.f, kq = 0.f;
     tok_sums8(kk, qq, sk, sq, kq);
     sk = group_sum<TPR>(sk);
@@ -275,6 +298,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_verify(
           if (FULL || row < D) EO::store(o, obase + row, orow[p]);
         }
       }
+      cur = nxt;
       continue;
     }
     // fused gated RMSNorm over the head's d_v outputs of this token
@@ -298,6 +322,7 @@ __global__ __launch_bounds__(NT) void k_recurrent_verify(
       EO::store(o, obase + tid, ov * rr * norm_w[tid] * silu(E::cvt(zraw)));
     }
     __syncthreads();   // so and sred are rewritten by the next token
+    cur = nxt;
   }
 }
 
@@ -311,8 +336,16 @@ static hipError_t run_verify(const VerifyArgs& a) {
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
   const T* z = static_cast<const T*>(a.z);
-  if (a.d == 128)
-    hipLaunchKernelGGL((k_recurrent_verify<E, EO, 128, 256>), dim3(blocks), dim3(256), 0, st, q, k, v, a.q_stride,
+  // d = 128: 1024 threads (two state rows each) measured fastest without the
+  // norm (133 against 148 us at 64 requests x 4 tokens); with the norm, whose
+  // three barriers per token weigh more in larger workgroups, 512 threads
+  // (146 against 152 us).
+  if (a.d == 128 && z == nullptr)
+    hipLaunchKernelGGL((k_recurrent_verify<E, EO, 128, 1024>), dim3(blocks), dim3(1024), 0, st, q, k, v, a.q_stride,
+                       a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.n_tok, a.state,
+                       a.slots, a.ckpt, a.n_cols, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
+  else if (a.d == 128)
+    hipLaunchKernelGGL((k_recurrent_verify<E, EO, 128, 512>), dim3(blocks), dim3(512), 0, st, q, k, v, a.q_stride,
                        a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.n_tok, a.state,
                        a.slots, a.ckpt, a.n_cols, static_cast<TO*>(a.o), z, a.norm_w, a.norm_eps);
   else
