@@ -7,11 +7,14 @@
 // paragraph and its prepared-interface list: raw projected QKV, dilation 1,
 // SiLU, caller-owned raw-input history, slot mapping, inactive lanes).
 //
-// Prefill: one workgroup per (block of 8 tokens of one sequence, 2048
-// channels); each thread owns 8 adjacent channels (one 16-byte vector per
+// Prefill: one workgroup per (block of 8 tokens of one sequence, 512
+// channels); each thread owns 2 adjacent channels (one 4-byte access per
 // token for bf16) and issues the loads of all 11 rows it reads (3 before the
 // block, 8 in it) before computing, so the whole input is in flight at
-// once (8-token blocks measured faster than 16 or 32).  Blocks are ordered so that consecutive token blocks of a channel
+// once.  Two channels per thread keep the register count low enough for
+// twice the resident workgroups of eight channels per thread, which measured
+// 27.5 against 32-33 us at 4096 tokens x 8192 channels (4-channel threads
+// 28-30 us; 8-token blocks faster than 4, 12 or 16).  Blocks are ordered so that consecutive token blocks of a channel
 // slice run on one XCD, where the 3-row halo a block re-reads from its
 // predecessor is an L2 hit.  Blocks never straddle sequences (slots from
 // common.hpp), which keeps the history reads inside the first block of each
@@ -25,7 +28,19 @@ namespace gdn {
 
 constexpr int kConvBT = 8;             // tokens per prefill block (>= 3)
 constexpr int kConvThreads = 256;
-constexpr int kConvCh = kConvThreads * 8;
+constexpr int kConvVec = 2;            // channels per prefill thread
+constexpr int kConvChP = kConvThreads * kConvVec;   // channels per prefill workgroup
+
+// kConvVec consecutive channels of one row, as raw elements (one access).
+template <class E>
+struct ConvRow {
+  typedef typename E::T V __attribute__((ext_vector_type(kConvVec)));
+  __device__ __forceinline__ static V ld(const typename E::T* p) { return *reinterpret_cast<const V*>(p); }
+  __device__ __forceinline__ static void st(typename E::T* p, V v) { *reinterpret_cast<V*>(p) = v; }
+  __device__ __forceinline__ static V zero() { return V{}; }
+};
+__device__ __forceinline__ uint16_t to_elem(float v, uint16_t) { return f32_to_bf16_bits(v); }
+__device__ __forceinline__ float to_elem(float v, float) { return v; }
 
 template <class E>
 __device__ __forceinline__ void load_taps(const typename E::T* w, int c0, float (&wt)[4][8]) {
@@ -54,10 +69,12 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
     const int32_t* __restrict__ slots, const int32_t* __restrict__ fresh, typename E::T* __restrict__ y,
     int64_t n_tblk, int n_slices) {
   using T = typename E::T;
+  using R = ConvRow<E>;
+  constexpr int NV = kConvVec;
   const int64_t lid = xcd_order(blockIdx.x, n_tblk * n_slices);
   const int slice = static_cast<int>(lid / n_tblk);
   const int64_t tblk = lid % n_tblk;
-  const int c0 = (slice * kConvThreads + threadIdx.x) * 8;
+  const int c0 = (slice * kConvThreads + threadIdx.x) * NV;
   if (c0 >= channels) return;
   int seq, len;
   int64_t t0;
@@ -69,7 +86,7 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
       if (es_slot >= 0 && fresh[es] != 0) {
         T* h = state + static_cast<int64_t>(es_slot) * 3 * channels + c0;
 #pragma unroll
-        for (int r = 0; r < 3; ++r) E::st_vec(h + r * static_cast<int64_t>(channels), E::zero_vec());
+        for (int r = 0; r < 3; ++r) R::st(h + r * static_cast<int64_t>(channels), R::zero());
       }
     }
     return;
@@ -85,32 +102,48 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
   // (history rows in the first block; zeros for a fresh sequence, whose
   // history is not read) and the block's own rows (rows past the block's end
   // re-read its last row and are not used)
-  typename E::Vec raw[3 + kConvBT];
+  typename R::V raw[3 + kConvBT];
   const bool zero_hist = p0 < 3 && fresh != nullptr && fresh[seq] != 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
     const int64_t lp = p0 - 3 + r;
-    if (lp < 0 && zero_hist) raw[r] = E::zero_vec();
-    else raw[r] = E::ld_vec(lp >= 0 ? x + (start + lp) * ld + c0 : hist + (3 + lp) * ld);
+    if (lp < 0 && zero_hist) raw[r] = R::zero();
+    else raw[r] = R::ld(lp >= 0 ? x + (start + lp) * ld + c0 : hist + (3 + lp) * ld);
   }
 #pragma unroll
-  for (int u = 0; u < kConvBT; ++u) raw[3 + u] = E::ld_vec(x + (t0 + (u < len ? u : len - 1)) * ld + c0);
-  float wt[4][8];
-  load_taps<E>(w, c0, wt);
+  for (int u = 0; u < kConvBT; ++u) raw[3 + u] = R::ld(x + (t0 + (u < len ? u : len - 1)) * ld + c0);
+  float wt[4][NV];
+  {
+    // taps of the thread's channels: w[c][0..3], channel-major
+    typedef T W8 __attribute__((ext_vector_type(4 * NV)));
+    const W8 wr = *reinterpret_cast<const W8*>(w + static_cast<int64_t>(c0) * 4);
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wt[i][c] = E::cvt(wr[4 * c + i]);
+  }
 
-  float h0[8], h1[8], h2[8];
-  E::unpack8(raw[0], h0);
-  E::unpack8(raw[1], h1);
-  E::unpack8(raw[2], h2);
+  float h0[NV], h1[NV], h2[NV];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    h0[c] = E::cvt(raw[0][c]);
+    h1[c] = E::cvt(raw[1][c]);
+    h2[c] = E::cvt(raw[2][c]);
+  }
 #pragma unroll
   for (int u = 0; u < kConvBT; ++u) {
     if (u < len) {
-      float cur[8], out[8];
-      E::unpack8(raw[3 + u], cur);
-      conv_out(wt, h0, h1, h2, cur, out);
-      E::store8(y + (t0 + u) * ld + c0, out);
+      typename R::V o;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) { h0[c] = h1[c]; h1[c] = h2[c]; h2[c] = cur[c]; }
+      for (int c = 0; c < NV; ++c) {
+        const float cur = E::cvt(raw[3 + u][c]);
+        const float acc = wt[0][c] * h0[c] + wt[1][c] * h1[c] + wt[2][c] * h2[c] + wt[3][c] * cur;
+        o[c] = to_elem(silu(acc), T{});
+        h0[c] = h1[c];
+        h1[c] = h2[c];
+        h2[c] = cur;
+      }
+      R::st(y + (t0 + u) * ld + c0, o);
     }
   }
 
@@ -121,10 +154,10 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
       const int64_t idx = L + r;
-      typename E::Vec row;
-      if (idx >= 3) row = E::ld_vec(x + (start + idx - 3) * ld + c0);
+      typename R::V row;
+      if (idx >= 3) row = R::ld(x + (start + idx - 3) * ld + c0);
       else row = idx == 0 ? raw[0] : (idx == 1 ? raw[1] : raw[2]);   // constant indices keep raw in registers
-      E::st_vec(hist + r * ld, row);
+      R::st(hist + r * ld, row);
     }
   }
 }
@@ -209,7 +242,7 @@ static hipError_t run_conv(const void* x, const void* w, int channels, const int
   using T = typename E::T;
   if (cu) {
     const int64_t ntblk = block_slots(t_total, n_seq, kConvBT);
-    const int nslices = (channels + kConvCh - 1) / kConvCh;
+    const int nslices = (channels + kConvChP - 1) / kConvChP;
     hipLaunchKernelGGL((k_conv1d_prefill<E>), dim3(static_cast<unsigned>(ntblk * nslices)), dim3(kConvThreads), 0, st,
                        static_cast<const T*>(x), static_cast<const T*>(w), channels, cu, n_seq, t_total,
                        static_cast<T*>(state), slots, fresh, static_cast<T*>(y), ntblk, nslices);
