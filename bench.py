@@ -54,10 +54,10 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (289_238_221, {"chunk.hip": "d4c6aa709200f2f4", "common.hpp": "c3ca3f5184368cb5",
-                                    "launch.hpp": "248bd9d12db4d7a8"}),
-    "gdn_recurrent_step": (274_537_268, {"recurrent.hip": "bd5d394eb0b8a939", "common.hpp": "c3ca3f5184368cb5",
-                                         "launch.hpp": "248bd9d12db4d7a8"}),
+    "gdn_chunk_fwd": (289_250_714, {"chunk.hip": "c8721f5ca44e879a", "common.hpp": "4e2cf7bb0de2ff2f",
+                                    "launch.hpp": "c3b849c7d316da8b"}),
+    "gdn_recurrent_step": (274_540_954, {"recurrent.hip": "feb115db1f28a22c", "common.hpp": "4e2cf7bb0de2ff2f",
+                                         "launch.hpp": "c3b849c7d316da8b"}),
 }
 
 
@@ -77,8 +77,8 @@ def measured_traffic(entry):
 # traffic above.
 MEASURED_MFMA = {
     "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
-                      {"chunk.hip": "d4c6aa709200f2f4", "common.hpp": "c3ca3f5184368cb5",
-                       "launch.hpp": "248bd9d12db4d7a8"}),
+                      {"chunk.hip": "c8721f5ca44e879a", "common.hpp": "4e2cf7bb0de2ff2f",
+                       "launch.hpp": "c3b849c7d316da8b"}),
 }
 
 
@@ -115,6 +115,45 @@ def environment(torch):
     return {"rocm_hip": torch.version.hip, "arch": getattr(props, "gcnArchName", None)}
 
 
+def streaming_probes(torch):
+    """What plain streaming kernels of the library reach on this GPU, per traffic shape (GB/s over the
+    bytes each moves), on buffers rotated so no pass finds its data in the 256 MB Infinity Cache."""
+    dev = "cuda:0"
+    n = 32 << 20                                    # 128 MiB of fp32
+    bufs = [torch.ones(n, device=dev) for _ in range(12)]
+
+    def rate(fn, nbytes, reps=20):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return round(nbytes / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    def fill(i):                                    # write 512 MiB
+        for j in range(4):
+            bufs[(4 * i + j) % 12].fill_(float(i))
+
+    def copy(i):                                    # read 128 MiB, write 128 MiB
+        bufs[(2 * i) % 12].copy_(bufs[(2 * i + 7) % 12])
+
+    def fan4(i):                                    # read 128 MiB once, write it four times
+        src = bufs[(5 * i) % 12]
+        for j in range(4):
+            bufs[(5 * i + 1 + j) % 12].copy_(src)
+
+    out = {"fill_512MiB_GB_per_s": rate(fill, 4 * n * 4), "copy_128MiB_GB_per_s": rate(copy, 2 * n * 4),
+           "read_once_write_4x_GB_per_s": rate(fan4, 8 * n * 4),
+           "note": "torch fill_ / copy_ kernels; the fan-out re-reads its source from cache for the last three "
+                   "copies, so it counts 4 reads + 4 writes"}
+    del bufs
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,7 +169,8 @@ def parse():
                     help="skip the speculative-verification and mixed prefill-plus-decode timings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="before the timed legs, copy 256 MiB device-to-device once (a plain copy of known "
-                         "size that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+                         "size that calibrates the FETCH_SIZE / WRITE_SIZE counters), then time plain streaming "
+                         "kernels of the library (fill, copy, one read fanned out to four writes) and report them")
     return ap.parse_args()
 
 
@@ -520,10 +560,10 @@ def cpu_baseline(np, I, R):
     order at a cost per token that does not depend on sequence length, so a
     rate in tokens/s carries over; decode steps scale with the request
     count), once with one thread and once with every core the process may use:
-      C1  the whole 4096-token single-sequence prefill mixer (conv, recurrence, norm)
-      C2  16 of the 64 decode requests x 16 steps (steps/s scaled to 64 requests)
-      C3  the 8 packed sequences cut to 256 tokens each, nonzero states and tails
-      C4  4096 tokens of the long-context stream, and 32 batch-1 decode steps
+      prefill 4096     the whole single-sequence prefill mixer (conv, recurrence, norm)
+      decode 64        16 of the 64 decode requests x 16 steps (steps/s scaled to 64 requests)
+      varlen 8         the 8 packed sequences cut to 256 tokens each, nonzero states and tails
+      long context     4096 tokens of the stream, and 32 batch-1 decode steps
     Rates are for the whole workload: tokens/s, or steps/s for decode."""
     import contextlib
     try:
@@ -554,11 +594,11 @@ def cpu_baseline(np, I, R):
 
     def run_all():
         r, used = {}, 0.0
-        for key, fn in (("C1_tokens_per_s", lambda: prefill_rate([4096], 1)),
-                        ("C2_steps_per_s", lambda: decode_rate(16, 16, 2, 64)),
-                        ("C3_tokens_per_s", lambda: prefill_rate([256] * 8, 3, state_std=0.02, tail_std=1.0)),
-                        ("C4_prefill_tokens_per_s", lambda: prefill_rate([4096], 4)),
-                        ("C4_decode_steps_per_s", lambda: decode_rate(1, 32, 5, 1))):
+        for key, fn in (("prefill_4096_tokens_per_s", lambda: prefill_rate([4096], 1)),
+                        ("decode_64_requests_steps_per_s", lambda: decode_rate(16, 16, 2, 64)),
+                        ("varlen_8_sequences_tokens_per_s", lambda: prefill_rate([256] * 8, 3, state_std=0.02, tail_std=1.0)),
+                        ("long_context_prefill_tokens_per_s", lambda: prefill_rate([4096], 4)),
+                        ("long_context_decode_steps_per_s", lambda: decode_rate(1, 32, 5, 1))):
             r[key], t = fn()
             used += t
         return {k: round(v, 2) for k, v in r.items()}, used
@@ -568,8 +608,8 @@ def cpu_baseline(np, I, R):
         one, t_one = run_all()
     with limit(len(affinity)):
         allc, t_all = run_all()
-    return dict(value=allc["C1_tokens_per_s"], unit="tokens/s", cores=len(affinity), kind="oracle",
-                sample="C1: the whole B=1 T=4096 prefill mixer (conv, recurrence, norm), all 32 v-heads, float64, "
+    return dict(value=allc["prefill_4096_tokens_per_s"], unit="tokens/s", cores=len(affinity), kind="oracle",
+                sample="the whole B=1 T=4096 prefill mixer (conv, recurrence, norm), all 32 v-heads, float64, "
                        "all cores the process may use (BLAS threads)",
                 cpu_count=os.cpu_count(), affinity=len(affinity), one_thread=one, all_cores=allc,
                 cpu_seconds_sampled={"one_thread": round(t_one, 1), "all_cores": round(t_all, 1)})
@@ -589,12 +629,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ops.L.load()
+    probes = None
     if args.copy_probe:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        probes = streaming_probes(torch)
     pf = prefill_leg(args, torch, np, ops, I)
     T = pf["T"]
     lay = pf["layout"]
@@ -721,6 +763,8 @@ def main():
                                 "unit": "GB/s", "frac": round(rec_alg / (lc["ms_rec"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 5),
                                 "avg_launch_ms": round(lc["ms_rec"], 4), "algorithmic_bytes_per_launch": rec_alg,
                                 "note": "2 MiB of state per step: launch-latency bound, far from the HBM roof"}}
+    if probes is not None:
+        out["streaming_probes"] = probes
     if not args.no_cpu_baseline:
         from oracle import gdn_ref as R
         out["cpu_baseline"] = cpu_baseline(np, I, R)
