@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = ["api.cpp", "conv1d.hip", "norm.hip", "recurrent.hip", "chunk.hip", "state_ops.hip", "backward.hip", "mixer_decode.hip"]
+SOURCES = ["api.cpp", "conv1d.hip", "norm.hip", "recurrent.hip", "chunk.hip", "chunk_bwd.hip", "state_ops.hip", "backward.hip", "mixer_decode.hip"]
 ARCH = "gfx950"
 
 

@@ -91,8 +91,11 @@ static size_t bwd_al(size_t x) { return (x + 255) & ~size_t(255); }
 size_t bwd_ws_bytes(int h_v, int d, int n_seq, int64_t t_total) {
   const int64_t slots = block_slots(t_total, n_seq, kBwdChunk);
   const int tiles = d / kBwdRows;
-  return bwd_al(sizeof(float) * slots * h_v * d * d) + 2 * bwd_al(sizeof(float) * t_total * h_v * tiles * d) +
-         2 * bwd_al(sizeof(float) * t_total * h_v * tiles);
+  const size_t b = bwd_al(sizeof(float) * slots * h_v * d * d) + 2 * bwd_al(sizeof(float) * t_total * h_v * tiles * d) +
+                   2 * bwd_al(sizeof(float) * t_total * h_v * tiles);
+  // bf16, d = 128 runs the chunked path (chunk_bwd.hip); h_qk <= h_v bounds its q/k regions
+  const size_t c = d == 128 ? bwd_chunked_ws_bytes(h_v, h_v, n_seq, t_total) : 0;
+  return b > c ? b : c;
 }
 
 static BwdWs bwd_carve(void* base, int h_v, int d, int n_seq, int64_t t_total) {
@@ -841,7 +844,7 @@ static hipError_t run_bwd(const BwdArgs& a) {
 
 hipError_t launch_chunk_bwd(const BwdArgs& a) {
   if (a.dt == GDN_BF16) {
-    if (a.d == 128) return run_bwd<BF16, 128>(a);
+    if (a.d == 128) return launch_chunk_bwd_chunked(a);
   } else {
     if (a.d == 128) return run_bwd<F32, 128>(a);
     if (a.d == 16) return run_bwd<F32, 16>(a);

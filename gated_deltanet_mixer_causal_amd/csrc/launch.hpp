@@ -132,6 +132,9 @@ hipError_t launch_single_token(const ChunkArgs& a, float* o_pre);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 size_t bwd_ws_bytes(int h_v, int d, int n_seq, int64_t t_total);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
+// The chunked backward on the matrix cores (csrc/chunk_bwd.hip): bf16, d = 128.
+size_t bwd_chunked_ws_bytes(int h_qk, int h_v, int n_seq, int64_t t_total);
+hipError_t launch_chunk_bwd_chunked(const BwdArgs& a);
 size_t conv_bwd_ws_bytes(int channels, int n_seq, int64_t t_total);
 hipError_t launch_conv1d_bwd(const ConvBwdArgs& a);
 hipError_t launch_recurrent_step(const StepArgs& a);

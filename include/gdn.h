@@ -430,10 +430,14 @@ gdn_status gdn_chunk_mixed(const void* q, const void* k, const void* v,
  * For L = sum(d_o * o) + sum(d_final * S_T), with o and S_T what gdn_chunk_fwd
  * returns for the same inputs (no norm epilogue), writes dL/dq, dL/dk (through
  * the L2 normalisation when use_qk_l2norm), dL/dv, dL/dg, dL/dbeta and
- * dL/d(initial_state).  The states entering every 16-token block are
- * computed into the workspace, then each sequence runs backwards through
- * its blocks, recomputing the states inside a block from its checkpoint.
- * All arithmetic is fp32; sums run in a fixed order (bitwise reproducible).
+ * dL/d(initial_state).  bf16 inputs with d_k = d_v = 128 run the chunked
+ * form on the matrix cores: a forward pass writes the state entering every
+ * 64-token chunk, a reverse pass over the chunks carries the state gradient
+ * (and writes dv), then one pass per (chunk, v-head) forms the other
+ * gradients from the chunk algebra; contractions take derived operands as
+ * bf16 hi+lo pairs with fp32 accumulation.  fp32 inputs run a token-by-token
+ * fp32 reverse chain from checkpoints every 16 tokens.  Sums run in a fixed
+ * order (bitwise reproducible).
  *
  *   q, k, v, strides, dt, g, beta, scale, use_qk_l2norm, l2_eps, h_qk, h_v,
  *   cu_seqlens, n_seq, t_total, initial_state: as gdn_chunk_fwd;

@@ -4,12 +4,16 @@ differences): packed sequences with ragged tails, a one-token and an empty
 sequence, nonzero initial states, a final-state gradient, scale != 1, and the
 L2 normalisation on and off.
 
-Tolerance: max|gpu - ref| / RMS(ref) <= 1e-4 per gradient tensor.  The kernels
-compute in fp32 on exact inputs; each gradient is a sum of a few thousand fp32
-products per token (two 128-long dot products per row, sums over 128 rows and
-over the later tokens through the state gradient), so a relative error of a
-few 1e-6 of the tensor's RMS is expected, and 1e-4 leaves room for the
-cancellation in dg (a difference of terms larger than itself).
+Tolerance: max|gpu - ref| / RMS(ref) per gradient tensor.
+- fp32 inputs (the per-token fp32 chain): 1e-4.  Each gradient is a sum of a
+  few thousand fp32 products per token, so a few 1e-6 of the tensor's RMS is
+  expected, and 1e-4 leaves room for the cancellation in dg.
+- bf16 inputs at d = 128 (the chunked matrix-core form): 1e-3.  Its
+  contractions take derived operands as bf16 hi+lo pairs (each within about
+  2^-17 of the fp32 value, the lo*lo term dropped), the scheme of the forward's
+  bf16 path, whose fp32 final state the suite bounds at 2e-3.  Products such as
+  Tb^T dU sum terms some ten to thirty times larger than the result, so errors
+  of 1e-4 to 3e-4 of the RMS are expected (measured: at most 2.3e-4, in dv).
 """
 import numpy as np
 import pytest
@@ -21,7 +25,12 @@ from oracle import gdn_grad_ref as G
 
 pytestmark = pytest.mark.gpu
 
-TOL = 1e-4
+TOL = 1e-4        # fp32 inputs
+TOL_BF16 = 1e-3   # bf16 inputs, chunked matrix-core form
+
+
+def _tol(lay):
+    return TOL_BF16 if lay.dtype == "bf16" else TOL
 SMALL = I.Layout(h_qk=2, h_v=4, d_k=128, d_v=128, chunk=64, dtype="bf16")
 
 
@@ -81,7 +90,7 @@ def test_chunk_bwd_against_oracle(ops, name, lay, lengths, scale, use_l2):
                                    cu_seqlens=d["cu_seqlens"], use_qk_l2norm=use_l2)
     errs = {key: rel_max(host(out[key]), ref[key]) for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial")}
     note("  " + ", ".join(f"{k_} {v_:.1e}" for k_, v_ in errs.items()))
-    assert all(e <= TOL for e in errs.values()), errs
+    assert all(e <= _tol(lay) for e in errs.values()), errs
 
     # reruns are bitwise identical; without d_final the final-state term drops out
     out2, _ = _run(ops, lay, d, do, dfin, scale, use_l2)
@@ -91,7 +100,7 @@ def test_chunk_bwd_against_oracle(ops, name, lay, lengths, scale, use_l2):
     ref3 = G.gated_delta_rule_grads(q, k, v, d["g"], d["beta"], do, None, scale=scale, initial_state=d["state"],
                                     cu_seqlens=d["cu_seqlens"], use_qk_l2norm=use_l2)
     for key in ("dq", "dk", "dv", "dg", "dbeta"):
-        assert rel_max(host(out3[key]), ref3[key]) <= TOL, key
+        assert rel_max(host(out3[key]), ref3[key]) <= _tol(lay), key
 
 
 def test_chunk_bwd_full_size_sampled_heads(ops):
@@ -120,7 +129,7 @@ def test_chunk_bwd_full_size_sampled_heads(ops):
                dg=host(out["dg"])[:, hs], dbeta=host(out["dbeta"])[:, hs], d_initial=host(out["d_initial"])[:, hs])
     errs = {key: rel_max(got[key], ref[key]) for key in got}
     note("  " + ", ".join(f"{k_} {v_:.1e}" for k_, v_ in errs.items()))
-    assert all(e <= TOL for e in errs.values()), errs
+    assert all(e <= TOL_BF16 for e in errs.values()), errs
 
 
 @pytest.mark.parametrize("name,lay,lengths", [("f32_tiny", I.TINY_LAYOUT, [40, 1, 2, 0, 23]),
@@ -158,23 +167,26 @@ def test_conv1d_bwd_against_oracle(ops, name, lay, lengths):
     assert torch.equal(dw, dw2)
 
 
-def test_chunk_bwd_single_sequence_without_cu(ops):
+@pytest.mark.parametrize("name,lay,T", [("f32_d16", I.TINY_LAYOUT, 37), ("bf16_d128", SMALL, 137)],
+                         ids=["f32_d16", "bf16_d128"])
+def test_chunk_bwd_single_sequence_without_cu(ops, name, lay, T):
     """One sequence with cu_seqlens NULL and no initial state: the same
     gradients as the packed form with cu_seqlens = [0, T]."""
-    lay = I.TINY_LAYOUT
-    note("chunk bwd: one sequence, no cu_seqlens")
-    d = I.prefill_inputs(55, lay, [37], g_mode="tiny")
+    note(f"chunk bwd {name}: one sequence of {T}, no cu_seqlens")
+    d = I.prefill_inputs(55, lay, [T], g_mode="tiny" if lay.dtype == "f32" else "model")
     rng = np.random.default_rng(56)
-    T = 37
+    tdt = torch.bfloat16 if lay.dtype == "bf16" else torch.float32
     do = rng.standard_normal((T, lay.h_v, lay.d_v)).astype(np.float32)
     q, k, v = I.split_qkv(d["x"], lay)
     outs = [torch.empty((T, lay.h_qk, lay.d_k), device=DEV), torch.empty((T, lay.h_qk, lay.d_k), device=DEV),
             torch.empty((T, lay.h_v, lay.d_v), device=DEV), torch.empty((T, lay.h_v), device=DEV),
             torch.empty((T, lay.h_v), device=DEV)]
     dinit = torch.empty((1, lay.h_v, lay.d_v, lay.d_k), device=DEV)
-    ops.gdn_chunk_bwd(dev(q), dev(k), dev(v), dev(d["g"]), dev(d["beta"]), dev(do), *outs, d_initial=dinit)
+    ops.gdn_chunk_bwd(dev(q, tdt), dev(k, tdt), dev(v, tdt), dev(d["g"]), dev(d["beta"]), dev(do), *outs,
+                      d_initial=dinit)
     torch.cuda.synchronize()
     ref = G.gated_delta_rule_grads(q, k, v, d["g"], d["beta"], do)
-    for name, got in zip(("dq", "dk", "dv", "dg", "dbeta"), outs):
-        assert rel_max(host(got), ref[name]) <= TOL, name
-    assert rel_max(host(dinit), ref["d_initial"]) <= TOL
+    errs = {nm: rel_max(host(got), ref[nm]) for nm, got in zip(("dq", "dk", "dv", "dg", "dbeta"), outs)}
+    errs["d_initial"] = rel_max(host(dinit), ref["d_initial"])
+    note("  " + ", ".join(f"{k_} {v_:.1e}" for k_, v_ in errs.items()))
+    assert all(e <= _tol(lay) for e in errs.values()), errs
