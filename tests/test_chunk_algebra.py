@@ -69,3 +69,33 @@ def test_split_bf16_plan_precision(form):
     err_o = np.max(np.abs(o - o_ref)) / np.sqrt(np.mean(o_ref ** 2))
     err_f = np.max(np.abs(f - f_ref)) / np.sqrt(np.mean(f_ref ** 2))
     assert err_o < 5e-4 and err_f < 5e-4, (err_o, err_f)
+
+
+@pytest.mark.parametrize("chunk,lengths,l2", [(1, [5], True), (4, [11, 1, 0, 9], True), (16, [40, 17], False),
+                                              (64, [150, 1, 64, 70], True), (200, [37], True)])
+def test_chunked_backward_equals_autograd(chunk, lengths, l2):
+    """The chunk-level gradient algebra of the chunked backward kernels
+    (chunk_algebra.chunked_gated_delta_rule_grads: dU, dX, the state-gradient
+    recurrence, dTb, dL = -T^T dT T^T, the decay terms and the suffix sum for
+    dg) against the gradient oracle's reverse-mode derivative of the
+    token-by-token rule, grouped heads, an initial state and a final-state
+    gradient, to 1e-11 of each tensor's largest entry."""
+    from chunk_algebra import chunked_gated_delta_rule_grads
+    from oracle import gdn_grad_ref as G
+    rng = np.random.default_rng(7 + chunk)
+    T, hqk, hv, d = sum(lengths), 2, 4, 8
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    q = rng.normal(size=(T, hqk, d))
+    k = rng.normal(size=(T, hqk, d))
+    v = rng.normal(size=(T, hv, d))
+    g = -rng.uniform(0.01, 0.6, size=(T, hv))
+    beta = rng.uniform(0.05, 0.95, size=(T, hv))
+    s0 = 0.3 * rng.normal(size=(len(lengths), hv, d, d))
+    do = rng.normal(size=(T, hv, d))
+    dfin = rng.normal(size=(len(lengths), hv, d, d))
+    kw = dict(scale=0.7, initial_state=s0, cu_seqlens=cu, use_qk_l2norm=l2)
+    ref = G.gated_delta_rule_grads(q, k, v, g, beta, do, dfin, **kw)
+    got = chunked_gated_delta_rule_grads(q, k, v, g, beta, do, dfin, chunk=chunk, **kw)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "d_initial"):
+        scale_ = max(float(np.abs(ref[key]).max()), 1e-300)
+        assert float(np.abs(got[key] - ref[key]).max()) <= 1e-11 * scale_, key
