@@ -335,8 +335,13 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_grad: one workgroup per (chunk slot, v-head)
+// k_bwd_grad: one workgroup of 8 waves per (chunk slot, v-head)
 // ---------------------------------------------------------------------------
+// Wave w works on token tile w % 4 (16 rows); the two waves of a tile split
+// the products: half 0 (w < 4) holds L's decayed Gram tiles and forms X, U,
+// dTb, then Z, dL and E; half 1 holds P and forms K dS^T, dU, dP and the
+// staging of dAq.  The sums over d_v into d_k columns (dO S, dX S, U dS) and
+// dQ^, dK^ are split by d_k: half h owns d_k tiles 4h .. 4h + 3.
 // LDS (bytes).  Rows: K, Q raw [64][LDK]; T, P hi|lo [64][L64]; then one
 // region reused by the solve (L, T fp32 [64][LDC]), the d_v parts (S, dS
 // [32][LDK], dO, X, beta X, U, dU [64][L32], hi|lo) and the C x C algebra
@@ -359,23 +364,26 @@ struct GradLds {
   static constexpr int kGam = kUEnd;                       // double[64]
   static constexpr int kB = kGam + 8 * BC, kD = kB + 4 * BC, kRk = kD + 4 * BC, kRq = kRk + 4 * BC,
                        kBeta = kRq + 4 * BC;
-  static constexpr int kRowG = kBeta + 4 * BC, kRowB = kRowG + 4 * BC;   // per-token sums of row terms
-  static constexpr int kColG = kRowB + 4 * BC, kColB = kColG + 16 * BC;  // [4 waves][64] column terms
-  static constexpr int kDd = kColB + 16 * BC;                             // per-token d_j k^_j . (U dS)_j
-  static constexpr int kRed = kDd + 4 * BC;                               // 16 floats
-  static constexpr int bytes = kRed + 64;
+  static constexpr int kRowG = kBeta + 4 * BC;   // [2 halves][64] row terms of dgamma
+  static constexpr int kRowB = kRowG + 8 * BC;   // [64] row terms of dbeta
+  static constexpr int kColG = kRowB + 4 * BC;   // [8 waves][64] column terms of dgamma
+  static constexpr int kColB = kColG + 32 * BC;  // [4 waves][64] column terms of dbeta
+  // 20 floats: b_C, <dS, S> per wave (4 ..), sum of d_j k^_j . (U dS)_j per wave (12 ..)
+  static constexpr int kRed = kColB + 16 * BC;
+  static constexpr int bytes = kRed + 80;
   static_assert(kTf + BC * LDC * 4 <= kUEnd, "solve fits the shared region");
+  static_assert(bytes <= 160 * 1024, "one workgroup per CU");
 };
 
 template <class In>
-__global__ __launch_bounds__(256) void k_bwd_grad(
+__global__ __launch_bounds__(512) void k_bwd_grad(
     const typename In::T* __restrict__ q, const typename In::T* __restrict__ k, const typename In::T* __restrict__ v,
     int64_t q_stride, int64_t k_stride, int64_t v_stride, GateSrc gates, float scale, int use_l2, float l2_eps,
     int h_qk, int h_v, const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const float* __restrict__ d_o,
     const float* __restrict__ dvx, const float* __restrict__ states, const float* __restrict__ dstates,
     float* __restrict__ dqh, float* __restrict__ dkh, float* __restrict__ dg, float* __restrict__ dbeta) {
   using LY = GradLds;
-  constexpr int D = BD, C = BC, LDK = LY::LDK, L64 = LY::L64, L32 = LY::L32, LDC = LY::LDC;
+  constexpr int D = BD, C = BC, LDK = LY::LDK, L64 = LY::L64, L32 = LY::L32, LDC = LY::LDC, NTH = 512;
   __shared__ __attribute__((aligned(16))) char lds[LY::bytes];
   __bf16* const sK = reinterpret_cast<__bf16*>(lds + LY::kK);
   __bf16* const sQ = reinterpret_cast<__bf16*>(lds + LY::kQ);
@@ -417,7 +425,6 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
   float* const s_rowb = reinterpret_cast<float*>(lds + LY::kRowB);
   float* const s_colg = reinterpret_cast<float*>(lds + LY::kColG);
   float* const s_colb = reinterpret_cast<float*>(lds + LY::kColB);
-  float* const s_dd = reinterpret_cast<float*>(lds + LY::kDd);
   float* const s_red = reinterpret_cast<float*>(lds + LY::kRed);
 
   const int64_t cs = blockIdx.x / h_v;
@@ -426,14 +433,18 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
   int64_t t0;
   if (!locate_block(cu, n_seq, t_total, C, cs, seq, t0, len)) return;
   const int hq = h / (h_v / h_qk);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tile = wv & 3;
+  const bool h0 = wv < 4;   // half 0 or half 1 (wave-uniform)
   const int r16 = lane & 15, g4 = lane >> 4;
   const int64_t vrow = static_cast<int64_t>(h_v) * D;
   const int64_t smat = (cs * h_v + h) * static_cast<int64_t>(D) * D;
+  const int i0 = 16 * tile + 4 * g4;   // this lane's first row in MFMA output tiles
+  const int ks0 = (16 * tile) / 32;
 
   // 1. raw K, Q rows (zero past len) and their L2 scales; gates and decays
   {
-    constexpr int TPR = D / 8, RPP = 256 / TPR;
+    constexpr int TPR = D / 8, RPP = NTH / TPR;
 #pragma unroll
     for (int it = 0; it < C / RPP; ++it) {
       const int row = it * RPP + tid / TPR, c8 = (tid % TPR) * 8;
@@ -454,9 +465,10 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
         s_rq[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sq + l2_eps) : 1.0f);
       }
     }
-    if (wave == 0) {
-      float gv = 0.f, bv = 0.f;
-      if (lane < len) load_gate(gates, t0 + lane, h, h_v, gv, bv);
+    if (wv == 0) {
+      float gv, bv;
+      load_gate(gates, t0 + (lane < len ? lane : len - 1), h, h_v, gv, bv);
+      if (lane >= len) gv = bv = 0.f;
       double gam = gv;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -473,42 +485,80 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
   }
   __syncthreads();
 
-  // 2. Gram tiles of row tile `wave`: (wave, tj), tj <= wave.  Lane (r, g)
-  //    holds element (i, j) = (16 wave + 4g + e, 16 tj + r).  LA = rk_i rk_j
-  //    (k_i . k_j) D_ij below the diagonal, P = scale D_ij rq_i rk_j (q_i . k_j)
-  //    on and below it; L = beta_i LA goes to LDS for the solve, P to LDS as
-  //    hi|lo rows (zero above the diagonal).
-  floatx4 Pt[4], LAt[4];
+  // Inputs of one 32-wide d_v part, fetched into registers a part ahead:
+  // S and dS rows (8 floats each per thread), dO (4 per thread), and this
+  // lane's V values (half 0, X tiles) or dV values (half 1, A operand).
+  // Rows past len re-read row len - 1 and are zeroed where they are used: a
+  // select right after a load would wait for it there.
+  struct PartIn {
+    float4 s[2], ds[2], o;
+  };
+  auto fetch_vv = [&](int p, float* vv) {   // V at this lane's X tile elements (half 0)
+    if (h0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e < len ? i0 + e : len - 1;
+          vv[4 * nt + e] = In::load(v, (t0 + i) * v_stride + (int64_t)h * D + 32 * p + 16 * nt + r16);
+        }
+    }
+  };
+  auto fetch_xv = [&](int p, float* xv) {   // dV as this lane's A operand values
+    const int xrow = 16 * tile + r16 < len ? 16 * tile + r16 : len - 1;
+    const float* src = dvx + (t0 + xrow) * vrow + h * D + 32 * p + 8 * g4;
+    const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+    xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+    xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+  };
+  auto fetch_part = [&](int p, PartIn& r) {
+    const int row = tid >> 4, c8 = (tid & 15) * 8;
+    const float* sp = states + smat + (int64_t)(32 * p + row) * D + c8;
+    const float* dp = dstates + smat + (int64_t)(32 * p + row) * D + c8;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      r.s[u] = reinterpret_cast<const float4*>(sp)[u];
+      r.ds[u] = reinterpret_cast<const float4*>(dp)[u];
+    }
+    const int tk = tid >> 3, c4 = (tid & 7) * 4;
+    r.o = *reinterpret_cast<const float4*>(d_o + (t0 + (tk < len ? tk : len - 1)) * vrow + h * D + 32 * p + c4);
+  };
+  PartIn nxt;
+
+  // 2. Gram tiles of row tile `tile`: (tile, tj), tj <= tile; lane (r, g)
+  //    holds element (i, j) = (16 tile + 4g + e, 16 tj + r).  Half 0: LA =
+  //    rk_i rk_j (k_i . k_j) D_ij below the diagonal (L = beta_i LA to LDS for
+  //    the solve); half 1: P = scale D_ij rq_i rk_j (q_i . k_j) on and below
+  //    it (hi|lo rows to LDS, zero above the diagonal).  Ct keeps LA (half 0)
+  //    or P (half 1).
   const float bC = s_red[0];
   {
+    const __bf16* aop = h0 ? sK : sQ;
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
-      Pt[tj] = LAt[tj] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (tj <= wave) {
-        floatx4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
+      if (tj <= tile) {
+        floatx4 gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const Frag kb = frag_rows(sK, LDK, 16 * tj, 32 * ks);
-          gk = mfma_bf16(frag_rows(sK, LDK, 16 * wave, 32 * ks), kb, gk);
-          gq = mfma_bf16(frag_rows(sQ, LDK, 16 * wave, 32 * ks), kb, gq);
-        }
+        for (int ks = 0; ks < D / 32; ++ks)
+          gm = mfma_bf16(frag_rows(aop, LDK, 16 * tile, 32 * ks), frag_rows(sK, LDK, 16 * tj, 32 * ks), gm);
         const int j = 16 * tj + r16;
         const double gj = s_gam[j];
         const float rkj = s_rk[j];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = 16 * wave + 4 * g4 + e;
+          const int i = i0 + e;
           const float dec = __expf(j <= i ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
-          const float la = j < i ? s_rk[i] * rkj * gk[e] * dec : 0.f;
-          const float pv = j <= i ? scale * dec * s_rq[i] * rkj * gq[e] : 0.f;
-          LAt[tj][e] = la;
-          Pt[tj][e] = pv;
-          sL[i * LDC + j] = s_beta[i] * la;
-          put_hl(sP, sP_lo, i * L64 + j, pv);
+          if (h0) {
+            const float la = j < i ? s_rk[i] * rkj * gm[e] * dec : 0.f;
+            sL[i * LDC + j] = s_beta[i] * la;
+          } else {
+            const float pv = j <= i ? scale * dec * s_rq[i] * rkj * gm[e] : 0.f;
+            put_hl(sP, sP_lo, i * L64 + j, pv);
+          }
         }
-      } else {
+      } else if (!h0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) put_hl(sP, sP_lo, (16 * wave + 4 * g4 + e) * L64 + 16 * tj + r16, 0.f);
+        for (int e = 0; e < 4; ++e) put_hl(sP, sP_lo, (i0 + e) * L64 + 16 * tj + r16, 0.f);
       }
     }
   }
@@ -516,223 +566,290 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
 
   // 3. T = (I + L)^-1 (fp32), then T as hi|lo rows (zero above the diagonal)
   unit_lower_inverse<C, LDC>(sL, sTf);
-  for (int f = tid; f < C * C; f += 256) {
+  // after the solve, whose forward substitution holds many registers
+  float vv[8], xv[8];
+  fetch_part(0, nxt);
+  fetch_vv(0, vv);
+  fetch_xv(0, xv);
+  for (int f = tid; f < C * C; f += NTH) {
     const int i = f / C, j = f % C;
     put_hl(sT, sT_lo, i * L64 + j, j <= i ? sTf[i * LDC + j] : 0.f);
   }
   __syncthreads();
 
-  // 4. the d_v parts: X, U, dU of 32 columns, then the sums over d_v
-  floatx4 dOS[8], dXS[8], UdS[8], dPt[4], dTbt[4];
+  // 4. the d_v parts: X, U, dU of 32 columns, then the sums over d_v:
+  //    dOS, dXS, UdS on this half's d_k tiles nb .. nb + 3, and T4 = dTb
+  //    (half 0) or dP (half 1).
+  const int nb = h0 ? 0 : 4;
+  floatx4 dOS[4], dXS[4], UdS[4], T4[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) dOS[n] = dXS[n] = UdS[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 4; ++n) dOS[n] = dXS[n] = UdS[n] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int tj = 0; tj < 4; ++tj) dPt[tj] = dTbt[tj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int tj = 0; tj < 4; ++tj) T4[tj] = floatx4{0.f, 0.f, 0.f, 0.f};
   float sds = 0.f;   // this thread's part of <dS, S>
-  const int ks0 = (16 * wave) / 32;
-  const int i0 = 16 * wave + 4 * g4;   // this lane's first row in MFMA output tiles
+#pragma unroll 1
   for (int p = 0; p < 4; ++p) {
-    // a. stage S and dS rows 32p .. 32p + 31 (d_v) and dO columns 32p .. (tokens)
+    // a. stage S and dS rows 32p .. 32p + 31 (d_v) and dO columns 32p .. from
+    //    the registers fetched a part ahead, then fetch the next part
     {
-      const int row = tid >> 3, c16 = (tid & 7) * 16;
-      const float* sp = states + smat + (int64_t)(32 * p + row) * D + c16;
-      const float* dp = dstates + smat + (int64_t)(32 * p + row) * D + c16;
+      const int row = tid >> 4, c8 = (tid & 15) * 8;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 a = reinterpret_cast<const float4*>(sp)[u];
-        const float4 b = reinterpret_cast<const float4*>(dp)[u];
+      for (int u = 0; u < 2; ++u) {
+        const float4 a = nxt.s[u], b = nxt.ds[u];
         sds += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-        put4_hl(sS, sS_lo, row * LDK + c16 + 4 * u, a);
-        put4_hl(sdS, sdS_lo, row * LDK + c16 + 4 * u, b);
+        put4_hl(sS, sS_lo, row * LDK + c8 + 4 * u, a);
+        put4_hl(sdS, sdS_lo, row * LDK + c8 + 4 * u, b);
       }
-      const int tk = tid >> 2, c8 = (tid & 3) * 8;
-      float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-      if (tk < len) {
-        const float* src = d_o + (t0 + tk) * vrow + h * D + 32 * p + c8;
-        x0 = reinterpret_cast<const float4*>(src)[0];
-        x1 = reinterpret_cast<const float4*>(src)[1];
-      }
-      put4_hl(sDO, sDO_lo, tk * L32 + c8, x0);
-      put4_hl(sDO, sDO_lo, tk * L32 + c8 + 4, x1);
+      const int tk = tid >> 3, c4 = (tid & 7) * 4;
+      put4_hl(sDO, sDO_lo, tk * L32 + c4, tk < len ? nxt.o : make_float4(0.f, 0.f, 0.f, 0.f));
     }
+    if (p < 3) fetch_part(p + 1, nxt);
     __syncthreads();
-    // b. X = V - diag(b rk) K S^T and K dS^T for this wave's 16 tokens
+    // b. half 0: X = V - diag(b rk) K S^T (and beta X); half 1: K dS^T
     floatx4 kds[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      floatx4 ks_ = {0.f, 0.f, 0.f, 0.f}, kd = ks_;
+      const __bf16* bh = h0 ? sS : sdS;
+      const __bf16* bl = h0 ? sS_lo : sdS_lo;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        const Frag a = frag_rows(sK, LDK, 16 * wave, 32 * ks);
-        ks_ = mfma_bf16(a, frag_rows(sS, LDK, 16 * nt, 32 * ks), ks_);
-        ks_ = mfma_bf16(a, frag_rows(sS_lo, LDK, 16 * nt, 32 * ks), ks_);
-        kd = mfma_bf16(a, frag_rows(sdS, LDK, 16 * nt, 32 * ks), kd);
-        kd = mfma_bf16(a, frag_rows(sdS_lo, LDK, 16 * nt, 32 * ks), kd);
+        const Frag a = frag_rows(sK, LDK, 16 * tile, 32 * ks);
+        acc = mfma_bf16(a, frag_rows(bh, LDK, 16 * nt, 32 * ks), acc);
+        acc = mfma_bf16(a, frag_rows(bl, LDK, 16 * nt, 32 * ks), acc);
       }
-      kds[nt] = kd;
-      const int c = 16 * nt + r16;
+      kds[nt] = acc;
+      if (h0) {
+        const int c = 16 * nt + r16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        const float vv = i < len ? In::load(v, (t0 + i) * v_stride + (int64_t)h * D + 32 * p + c) : 0.f;
-        const float x = vv - s_b[i] * s_rk[i] * ks_[e];
-        put_hl(sX, sX_lo, i * L32 + c, x);
-        put_hl(sXb, sXb_lo, i * L32 + c, s_beta[i] * x);
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          const float x = (i < len ? vv[4 * nt + e] : 0.f) - s_b[i] * s_rk[i] * acc[e];
+          put_hl(sX, sX_lo, i * L32 + c, x);
+          put_hl(sXb, sXb_lo, i * L32 + c, s_beta[i] * x);
+        }
       }
     }
+    if (p < 3) fetch_vv(p + 1, vv);
     __syncthreads();
-    // c. U = T (beta X) and dU = P^T dO + diag(d rk) K dS^T
+    // c. half 0: U = T (beta X); half 1: dU = P^T dO + diag(d rk) K dS^T
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      floatx4 u = {0.f, 0.f, 0.f, 0.f}, du;
+      floatx4 u = {0.f, 0.f, 0.f, 0.f};
+      if (h0) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (32 * ks <= 16 * wave + 15)
-          u = mma3(u, frag_rows(sT, L64, 16 * wave, 32 * ks), frag_rows(sT_lo, L64, 16 * wave, 32 * ks),
-                   frag_cols(sXb, L32, 32 * ks, 16 * nt), frag_cols(sXb_lo, L32, 32 * ks, 16 * nt));
+        for (int ks = 0; ks < 2; ++ks) {
+          if (32 * ks <= 16 * tile + 15)
+            u = mma3(u, frag_rows(sT, L64, 16 * tile, 32 * ks), frag_rows(sT_lo, L64, 16 * tile, 32 * ks),
+                     frag_cols(sXb, L32, 32 * ks, 16 * nt), frag_cols(sXb_lo, L32, 32 * ks, 16 * nt));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = s_d[i0 + e] * s_rk[i0 + e] * kds[nt][e];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks >= ks0)
+            u = mma3(u, frag_cols(sP, L64, 32 * ks, 16 * tile), frag_cols(sP_lo, L64, 32 * ks, 16 * tile),
+                     frag_cols(sDO, L32, 32 * ks, 16 * nt), frag_cols(sDO_lo, L32, 32 * ks, 16 * nt));
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) du[e] = s_d[i0 + e] * s_rk[i0 + e] * kds[nt][e];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (ks >= ks0)
-          du = mma3(du, frag_cols(sP, L64, 32 * ks, 16 * wave), frag_cols(sP_lo, L64, 32 * ks, 16 * wave),
-                    frag_cols(sDO, L32, 32 * ks, 16 * nt), frag_cols(sDO_lo, L32, 32 * ks, 16 * nt));
-      }
+      __bf16* oh = h0 ? sU : sDU;
+      __bf16* ol = h0 ? sU_lo : sDU_lo;
       const int c = 16 * nt + r16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        put_hl(sU, sU_lo, (i0 + e) * L32 + c, u[e]);
-        put_hl(sDU, sDU_lo, (i0 + e) * L32 + c, du[e]);
-      }
+      for (int e = 0; e < 4; ++e) put_hl(oh, ol, (i0 + e) * L32 + c, u[e]);
     }
     __syncthreads();
     // d. sums over this part's 32 d_v columns
     {
-      const Frag aoh = frag_rows(sDO, L32, 16 * wave, 0), aol = frag_rows(sDO_lo, L32, 16 * wave, 0);
-      const Frag auh = frag_rows(sU, L32, 16 * wave, 0), aul = frag_rows(sU_lo, L32, 16 * wave, 0);
-      const Frag adh = frag_rows(sDU, L32, 16 * wave, 0), adl = frag_rows(sDU_lo, L32, 16 * wave, 0);
+      const Frag aoh = frag_rows(sDO, L32, 16 * tile, 0), aol = frag_rows(sDO_lo, L32, 16 * tile, 0);
+      const Frag auh = frag_rows(sU, L32, 16 * tile, 0), aul = frag_rows(sU_lo, L32, 16 * tile, 0);
       Frag axh, axl;
       {
-        const int row = 16 * wave + r16;
-        float xv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (row < len) {
-          const float* src = dvx + (t0 + row) * vrow + h * D + 32 * p + 8 * g4;
-          const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
-          xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
-          xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
-        }
-        split8(xv, axh, axl);
-      }
+        float xm[8];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const Frag bsh = frag_cols(sS, LDK, 0, 16 * n), bsl = frag_cols(sS_lo, LDK, 0, 16 * n);
-        const Frag bdh = frag_cols(sdS, LDK, 0, 16 * n), bdl = frag_cols(sdS_lo, LDK, 0, 16 * n);
+        for (int e = 0; e < 8; ++e) xm[e] = 16 * tile + r16 < len ? xv[e] : 0.f;
+        split8(xm, axh, axl);
+      }
+      if (p < 3) fetch_xv(p + 1, xv);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int c0 = 16 * (nb + n);
+        const Frag bsh = frag_cols(sS, LDK, 0, c0), bsl = frag_cols(sS_lo, LDK, 0, c0);
         dOS[n] = mma3(dOS[n], aoh, aol, bsh, bsl);
         dXS[n] = mma3(dXS[n], axh, axl, bsh, bsl);
-        UdS[n] = mma3(UdS[n], auh, aul, bdh, bdl);
+        UdS[n] = mma3(UdS[n], auh, aul, frag_cols(sdS, LDK, 0, c0), frag_cols(sdS_lo, LDK, 0, c0));
       }
+      const Frag ath = h0 ? frag_rows(sDU, L32, 16 * tile, 0) : aoh;
+      const Frag atl = h0 ? frag_rows(sDU_lo, L32, 16 * tile, 0) : aol;
+      const __bf16* bt = h0 ? sX : sU;
+      const __bf16* btl = h0 ? sX_lo : sU_lo;
 #pragma unroll
-      for (int tj = 0; tj < 4; ++tj) {
-        if (tj <= wave) {
-          dPt[tj] = mma3(dPt[tj], aoh, aol, frag_rows(sU, L32, 16 * tj, 0), frag_rows(sU_lo, L32, 16 * tj, 0));
-          dTbt[tj] = mma3(dTbt[tj], adh, adl, frag_rows(sX, L32, 16 * tj, 0), frag_rows(sX_lo, L32, 16 * tj, 0));
-        }
-      }
+      for (int tj = 0; tj < 4; ++tj)
+        if (tj <= tile)
+          T4[tj] = mma3(T4[tj], ath, atl, frag_rows(bt, L32, 16 * tj, 0), frag_rows(btl, L32, 16 * tj, 0));
     }
     __syncthreads();
   }
 
   // 5. the C x C algebra.  Row sums of a wave's tiles belong to its own rows;
   //    column sums are left per wave and added in a fixed order.
+  //    Half 1: dP (masked) with P: its dgamma terms and dAq (two scalings);
+  //    half 0: dTb (masked) with T: dbeta's column terms and dT.
   {
-    float rowg[4] = {0.f, 0.f, 0.f, 0.f}, colg[4] = {0.f, 0.f, 0.f, 0.f}, colb[4] = {0.f, 0.f, 0.f, 0.f};
+    float rowa[4] = {0.f, 0.f, 0.f, 0.f}, cola[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
       const int j = 16 * tj + r16;
-      if (tj <= wave) {
+      if (tj <= tile) {
         const double gj = s_gam[j];
         const float rkj = s_rk[j], bj = s_beta[j];
-        float cg = 0.f, cb = 0.f;
+        float ca = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = i0 + e;
           const bool on = j <= i;
-          const float dp = on ? dPt[tj][e] : 0.f;
-          const float m1 = dp * Pt[tj][e];
-          rowg[e] += m1;
-          cg += m1;
-          const float dec = __expf(on ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
-          const float aq = on ? scale * dp * dec : 0.f;
-          put_hl(sAqk, sAqk_lo, i * L64 + j, aq * rkj);
-          put_hl(sAqq, sAqq_lo, i * L64 + j, s_rq[i] * aq);
-          const float dtb = on ? dTbt[tj][e] : 0.f;
-          const float tij = static_cast<float>(sT[i * L64 + j]) + static_cast<float>(sT_lo[i * L64 + j]);
-          cb += dtb * tij;
-          put_hl(sDT, sDT_lo, i * L64 + j, dtb * bj);
+          const float x = on ? T4[tj][e] : 0.f;
+          if (!h0) {
+            const float m1 = x * (static_cast<float>(sP[i * L64 + j]) + static_cast<float>(sP_lo[i * L64 + j]));
+            rowa[e] += m1;
+            ca += m1;
+            const float dec = __expf(on ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
+            const float aq = on ? scale * x * dec : 0.f;
+            put_hl(sAqk, sAqk_lo, i * L64 + j, aq * rkj);
+            put_hl(sAqq, sAqq_lo, i * L64 + j, s_rq[i] * aq);
+          } else {
+            const float tij = static_cast<float>(sT[i * L64 + j]) + static_cast<float>(sT_lo[i * L64 + j]);
+            ca += x * tij;
+            put_hl(sDT, sDT_lo, i * L64 + j, x * bj);
+          }
         }
-        colg[tj] = cg;
-        colb[tj] = cb;
+        cola[tj] = ca;
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int idx = (i0 + e) * L64 + j;
-          put_hl(sAqk, sAqk_lo, idx, 0.f);
-          put_hl(sAqq, sAqq_lo, idx, 0.f);
-          put_hl(sDT, sDT_lo, idx, 0.f);
+          if (!h0) {
+            put_hl(sAqk, sAqk_lo, idx, 0.f);
+            put_hl(sAqq, sAqq_lo, idx, 0.f);
+          } else {
+            put_hl(sDT, sDT_lo, idx, 0.f);
+          }
         }
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rowg[e] = sum16(rowg[e]);
-#pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
-      const float cg = sum_groups(colg[tj]), cb = sum_groups(colb[tj]);
+      const float c_ = sum_groups(cola[tj]);
       if (g4 == 0) {
-        s_colg[wave * C + 16 * tj + r16] = cg;
-        s_colb[wave * C + 16 * tj + r16] = cb;
+        if (h0) s_colb[tile * C + 16 * tj + r16] = c_;
+        else s_colg[wv * C + 16 * tj + r16] = c_;
       }
+    }
+    if (!h0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rowa[e] = sum16(rowa[e]);
+      if (r16 == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_rowg[C + i0 + e] = rowa[e];
+      }
+    }
+  }
+  // <dS, S> over the workgroup
+  {
+    float x = sds;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+    if (lane == 0) s_red[4 + wv] = x;
+  }
+  __syncthreads();
+
+  // 6. dQ^ = scale diag(b) dO S + dAq diag(rk) K and dK^ = diag(d) U dS -
+  //    diag(b) dX S + (diag(rq) dAq)^T Q + E K on this half's d_k tiles, the
+  //    row dots of their dgamma terms taken before the products are added;
+  //    meanwhile half 0 forms Z = dT T^T, then dL = -T^T Z and E.
+  floatx4 dq4[4], dk4[4];
+  {
+    float t_row[4] = {0.f, 0.f, 0.f, 0.f}, dd_row[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int c = 16 * (nb + n) + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        const float qv = static_cast<float>(sQ[i * LDK + c]), kv = static_cast<float>(sK[i * LDK + c]);
+        const float bi = s_b[i], qs = scale * bi * dOS[n][e], ud = s_d[i] * UdS[n][e];
+        t_row[e] += s_rq[i] * qv * qs - bi * s_rk[i] * kv * dXS[n][e];
+        dd_row[e] += s_rk[i] * kv * ud;
+        dq4[n][e] = qs;
+        dk4[n][e] = ud - bi * dXS[n][e];
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const Frag kb = frag_cols(sK, LDK, 32 * ks, 16 * (nb + n));
+        dq4[n] = mma2(dq4[n], frag_rows(sAqk, L64, 16 * tile, 32 * ks), frag_rows(sAqk_lo, L64, 16 * tile, 32 * ks),
+                      kb);
+        dk4[n] = mma2(dk4[n], frag_cols(sAqq, L64, 32 * ks, 16 * tile), frag_cols(sAqq_lo, L64, 32 * ks, 16 * tile),
+                      frag_cols(sQ, LDK, 32 * ks, 16 * (nb + n)));
+      }
+      // one tile's operand reads at a time (registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t_row[e] = sum16(t_row[e]);
+      dd_row[e] = sum16(dd_row[e]);
     }
     if (r16 == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s_rowg[i0 + e] = rowg[e];
+      for (int e = 0; e < 4; ++e) {
+        if (h0) s_rowg[i0 + e] = t_row[e] - dd_row[e];
+        else s_rowg[C + i0 + e] += t_row[e] - dd_row[e];
+      }
+    }
+    const float ddw = sum_groups(((dd_row[0] + dd_row[1]) + dd_row[2]) + dd_row[3]);
+    if (lane == 0) s_red[12 + wv] = ddw;
+  }
+  if (h0) {
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      if (tj <= tile) {
+        floatx4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          z = mma3(z, frag_rows(sDT, L64, 16 * tile, 32 * ks), frag_rows(sDT_lo, L64, 16 * tile, 32 * ks),
+                   frag_rows(sT, L64, 16 * tj, 32 * ks), frag_rows(sT_lo, L64, 16 * tj, 32 * ks));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put_hl(sZ, sZ_lo, (i0 + e) * L64 + 16 * tj + r16, z[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put_hl(sZ, sZ_lo, (i0 + e) * L64 + 16 * tj + r16, 0.f);
+      }
     }
   }
   __syncthreads();
-  // Z = dT T^T on the tiles (wave, tj <= wave), zero above the diagonal
-#pragma unroll
-  for (int tj = 0; tj < 4; ++tj) {
-    if (tj <= wave) {
-      floatx4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        z = mma3(z, frag_rows(sDT, L64, 16 * wave, 32 * ks), frag_rows(sDT_lo, L64, 16 * wave, 32 * ks),
-                 frag_rows(sT, L64, 16 * tj, 32 * ks), frag_rows(sT_lo, L64, 16 * tj, 32 * ks));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) put_hl(sZ, sZ_lo, (i0 + e) * L64 + 16 * tj + r16, z[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) put_hl(sZ, sZ_lo, (i0 + e) * L64 + 16 * tj + r16, 0.f);
-    }
-  }
-  __syncthreads();
-  // dL = -T^T Z (strictly lower); its dgamma and dbeta terms; E = (dA + dA^T) diag(rk)
-  {
+  if (h0) {
+    // dL = -T^T Z (strictly lower); its dgamma and dbeta terms; E = (dA + dA^T) diag(rk)
     float rowg[4] = {0.f, 0.f, 0.f, 0.f}, rowb[4] = {0.f, 0.f, 0.f, 0.f}, colg[4] = {0.f, 0.f, 0.f, 0.f};
     floatx4 dAt[4];
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
       dAt[tj] = floatx4{0.f, 0.f, 0.f, 0.f};
-      if (tj <= wave) {
-        floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      if (tj <= tile) {
+        floatx4 z = {0.f, 0.f, 0.f, 0.f}, gk = z;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (ks >= ks0)
-            z = mma3(z, frag_cols(sT, L64, 32 * ks, 16 * wave), frag_cols(sT_lo, L64, 32 * ks, 16 * wave),
+            z = mma3(z, frag_cols(sT, L64, 32 * ks, 16 * tile), frag_cols(sT_lo, L64, 32 * ks, 16 * tile),
                      frag_cols(sZ, L64, 32 * ks, 16 * tj), frag_cols(sZ_lo, L64, 32 * ks, 16 * tj));
         }
+        // the K K^T tile again (raw operands, exact products)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+          gk = mfma_bf16(frag_rows(sK, LDK, 16 * tile, 32 * ks), frag_rows(sK, LDK, 16 * tj, 32 * ks), gk);
         const int j = 16 * tj + r16;
         const double gj = s_gam[j];
+        const float rkj = s_rk[j];
         float cg = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -740,11 +857,12 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
           const bool on = j < i;
           const float dl = on ? -z[e] : 0.f;
           const float bi = s_beta[i];
-          const float m2 = dl * bi * LAt[tj][e];
+          const float dec = __expf(on ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
+          const float la = on ? s_rk[i] * rkj * gk[e] * dec : 0.f;
+          const float m2 = dl * bi * la;
           rowg[e] += m2;
           cg += m2;
-          rowb[e] += dl * LAt[tj][e];
-          const float dec = __expf(on ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
+          rowb[e] += dl * la;
           dAt[tj][e] = on ? bi * dec * dl : 0.f;
         }
         colg[tj] = cg;
@@ -753,7 +871,7 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
     // E overwrites dT, which no wave reads after the Z product
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
-      if (tj <= wave) {
+      if (tj <= tile) {
         const int j = 16 * tj + r16;
         const float rkj = s_rk[j];
 #pragma unroll
@@ -774,7 +892,7 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
       const float cg = sum_groups(colg[tj]);
-      if (g4 == 0) s_colg[wave * C + 16 * tj + r16] += cg;
+      if (g4 == 0) s_colg[wv * C + 16 * tj + r16] = cg;
     }
     if (r16 == 0) {
 #pragma unroll
@@ -784,78 +902,44 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
       }
     }
   }
-  // <dS, S> over the workgroup
-  {
-    float x = sds;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-    if (lane == 0) s_red[4 + wave] = x;
-  }
   __syncthreads();
-
-  // 6. dQ^ = scale diag(b) dO S + dAq diag(rk) K and dK^ = diag(d) U dS -
-  //    diag(b) dX S + (diag(rq) dAq)^T Q + E K, for this wave's 16 rows; the
-  //    row dots of the dgamma terms are taken before the products are added.
   {
-    float t_row[4] = {0.f, 0.f, 0.f, 0.f}, dd_row[4] = {0.f, 0.f, 0.f, 0.f};
-    float* qo = dqh + (t0 * h_v + h) * static_cast<int64_t>(D);
-    float* ko = dkh + (t0 * h_v + h) * static_cast<int64_t>(D);
+    float* oq = dqh + (t0 * h_v + h) * static_cast<int64_t>(D);
+    float* ok = dkh + (t0 * h_v + h) * static_cast<int64_t>(D);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int c = 16 * n + r16;
-      floatx4 aq, ak;
+    for (int n = 0; n < 4; ++n) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        const float qv = static_cast<float>(sQ[i * LDK + c]), kv = static_cast<float>(sK[i * LDK + c]);
-        const float bi = s_b[i];
-        const float qs = scale * bi * dOS[n][e];
-        t_row[e] += s_rq[i] * qv * qs - bi * s_rk[i] * kv * dXS[n][e];
-        dd_row[e] += s_d[i] * s_rk[i] * kv * UdS[n][e];
-        aq[e] = qs;
-        ak[e] = s_d[i] * UdS[n][e] - bi * dXS[n][e];
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const Frag kb = frag_cols(sK, LDK, 32 * ks, 16 * n);
-        aq = mma2(aq, frag_rows(sAqk, L64, 16 * wave, 32 * ks), frag_rows(sAqk_lo, L64, 16 * wave, 32 * ks), kb);
-        ak = mma2(ak, frag_cols(sAqq, L64, 32 * ks, 16 * wave), frag_cols(sAqq_lo, L64, 32 * ks, 16 * wave),
-                  frag_cols(sQ, LDK, 32 * ks, 16 * n));
-        ak = mma2(ak, frag_rows(sDT, L64, 16 * wave, 32 * ks), frag_rows(sDT_lo, L64, 16 * wave, 32 * ks), kb);
-      }
+      for (int ks = 0; ks < 2; ++ks)
+        dk4[n] = mma2(dk4[n], frag_rows(sDT, L64, 16 * tile, 32 * ks), frag_rows(sDT_lo, L64, 16 * tile, 32 * ks),
+                      frag_cols(sK, LDK, 32 * ks, 16 * (nb + n)));
+      const int c = 16 * (nb + n) + r16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        if (i < len) {
-          qo[(int64_t)i * vrow + c] = aq[e];
-          ko[(int64_t)i * vrow + c] = ak[e];
+        if (i0 + e < len) {
+          oq[(int64_t)(i0 + e) * vrow + c] = dq4[n][e];
+          ok[(int64_t)(i0 + e) * vrow + c] = dk4[n][e];
         }
       }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t_row[e] = sum16(t_row[e]);
-      dd_row[e] = sum16(dd_row[e]);
-    }
-    if (r16 == 0) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s_rowg[i0 + e] += t_row[e] - dd_row[e];
-        s_dd[i0 + e] = dd_row[e];
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   __syncthreads();
 
   // 7. per token: dgamma, then dg = its suffix sum over the chunk, and dbeta
-  if (wave == 0) {
+  if (wv == 0) {
     const int t = lane;
-    float x = s_rowg[t] - (((s_colg[t] + s_colg[C + t]) + s_colg[2 * C + t]) + s_colg[3 * C + t]);
-    const float db = s_rowb[t] + (((s_colb[t] + s_colb[C + t]) + s_colb[2 * C + t]) + s_colb[3 * C + t]);
-    float dd = s_dd[t];
+    float cg = 0.f;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) dd += __shfl_xor(dd, m, 64);
-    if (t == C - 1) x += dd + bC * (((s_red[4] + s_red[5]) + s_red[6]) + s_red[7]);
+    for (int w = 0; w < 8; ++w) cg += s_colg[w * C + t];
+    float x = (s_rowg[t] + s_rowg[C + t]) - cg;
+    const float db = s_rowb[t] + (((s_colb[t] + s_colb[C + t]) + s_colb[2 * C + t]) + s_colb[3 * C + t]);
+    float dd = 0.f, sd = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      dd += s_red[12 + w];
+      sd += s_red[4 + w];
+    }
+    if (t == C - 1) x += dd + bC * sd;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float y = __shfl_down(x, off, 64);
@@ -869,51 +953,76 @@ __global__ __launch_bounds__(256) void k_bwd_grad(
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_dqk: per (token, q/k head), dq^ and dk^ summed over the v-heads that
-// read the q/k head (in head order), then dx = rx (dx^ - x^ (x^ . dx^)) with
-// x^ = rx x, rx = 1 / sqrt(|x|^2 + eps) (or dx = dx^ without the L2 norm).
-// 128 threads, one d_k element each.
+// k_bwd_dqk: per (token, q/k head) row, dq^ and dk^ summed over the v-heads
+// that read the q/k head (in head order), then dx = rx (dx^ - x^ (x^ . dx^))
+// with x^ = rx x, rx = 1 / sqrt(|x|^2 + eps) (or dx = dx^ without the L2
+// norm).  16 lanes per row, 8 consecutive elements each; 16 rows per
+// workgroup.
 // ---------------------------------------------------------------------------
-template <class In>
-__global__ __launch_bounds__(128) void k_bwd_dqk(const typename In::T* __restrict__ q,
-                                                 const typename In::T* __restrict__ k, int64_t q_stride,
-                                                 int64_t k_stride, int use_l2, float l2_eps, int h_qk, int h_v,
-                                                 const float* __restrict__ dqh, const float* __restrict__ dkh,
-                                                 float* __restrict__ dq, float* __restrict__ dk) {
-  __shared__ float red[2][4];
-  const int64_t t = blockIdx.x / h_qk;
-  const int hq = static_cast<int>(blockIdx.x % h_qk);
-  const int c = threadIdx.x, lane = c & 63, wv = c >> 6;
+__global__ __launch_bounds__(256) void k_bwd_dqk(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                 int64_t q_stride, int64_t k_stride, int use_l2, float l2_eps,
+                                                 int h_qk, int h_v, int64_t t_total, const float* __restrict__ dqh,
+                                                 const float* __restrict__ dkh, float* __restrict__ dq,
+                                                 float* __restrict__ dk) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  if (row >= t_total * h_qk) return;   // whole 16-lane groups leave together
+  const int64_t t = row / h_qk;
+  const int hq = static_cast<int>(row % h_qk);
+  const int c8 = (threadIdx.x & 15) * 8;
   const int grp = h_v / h_qk;
-  float gq = 0.f, gk = 0.f;
+  float gq[8], gk[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) gq[e] = gk[e] = 0.f;
   for (int i = 0; i < grp; ++i) {
-    const int64_t row = (t * h_v + hq * grp + i) * BD + c;
-    gq += dqh[row];
-    gk += dkh[row];
+    const int64_t off = (t * h_v + hq * grp + i) * BD + c8;
+    const float4 a0 = *reinterpret_cast<const float4*>(dqh + off), a1 = *reinterpret_cast<const float4*>(dqh + off + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(dkh + off), b1 = *reinterpret_cast<const float4*>(dkh + off + 4);
+    gq[0] += a0.x; gq[1] += a0.y; gq[2] += a0.z; gq[3] += a0.w;
+    gq[4] += a1.x; gq[5] += a1.y; gq[6] += a1.z; gq[7] += a1.w;
+    gk[0] += b0.x; gk[1] += b0.y; gk[2] += b0.z; gk[3] += b0.w;
+    gk[4] += b1.x; gk[5] += b1.y; gk[6] += b1.z; gk[7] += b1.w;
   }
-  float outq = gq, outk = gk;
   if (use_l2) {
-    const float xq = In::load(q, t * q_stride + (int64_t)hq * BD + c);
-    const float xk = In::load(k, t * k_stride + (int64_t)hq * BD + c);
-    float v[4] = {xq * xq, xk * xk, xq * gq, xk * gk};
+    const uint4 rq = *reinterpret_cast<const uint4*>(q + t * q_stride + (int64_t)hq * BD + c8);
+    const uint4 rk = *reinterpret_cast<const uint4*>(k + t * k_stride + (int64_t)hq * BD + c8);
+    const uint32_t wq[4] = {rq.x, rq.y, rq.z, rq.w}, wk[4] = {rk.x, rk.y, rk.z, rk.w};
+    float xq[8], xk[8];
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] += __shfl_xor(v[u], m, 64);
-    if (lane == 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) red[wv][u] = v[u];
+    for (int u = 0; u < 4; ++u) {
+      xq[2 * u] = __uint_as_float(wq[u] << 16);
+      xq[2 * u + 1] = __uint_as_float(wq[u] & 0xffff0000u);
+      xk[2 * u] = __uint_as_float(wk[u] << 16);
+      xk[2 * u + 1] = __uint_as_float(wk[u] & 0xffff0000u);
     }
-    __syncthreads();
-    const float sqq = red[0][0] + red[1][0], skk = red[0][1] + red[1][1];
-    const float dq_ = red[0][2] + red[1][2], dk_ = red[0][3] + red[1][3];
-    const float rq = 1.0f / sqrtf(sqq + l2_eps), rk = 1.0f / sqrtf(skk + l2_eps);
+    float sqq = 0.f, skk = 0.f, sqg = 0.f, skg = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sqq += xq[e] * xq[e];
+      skk += xk[e] * xk[e];
+      sqg += xq[e] * gq[e];
+      skg += xk[e] * gk[e];
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      sqq += __shfl_xor(sqq, m, 64);
+      skk += __shfl_xor(skk, m, 64);
+      sqg += __shfl_xor(sqg, m, 64);
+      skg += __shfl_xor(skg, m, 64);
+    }
+    const float rqn = 1.0f / sqrtf(sqq + l2_eps), rkn = 1.0f / sqrtf(skk + l2_eps);
     // x^ . dx^ = rx (x . dx^)
-    outq = rq * (gq - (rq * xq) * (rq * dq_));
-    outk = rk * (gk - (rk * xk) * (rk * dk_));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gq[e] = rqn * (gq[e] - (rqn * xq[e]) * (rqn * sqg));
+      gk[e] = rkn * (gk[e] - (rkn * xk[e]) * (rkn * skg));
+    }
   }
-  dq[(t * h_qk + hq) * BD + c] = outq;
-  dk[(t * h_qk + hq) * BD + c] = outk;
+  float* oq = dq + row * BD + c8;
+  float* ok = dk + row * BD + c8;
+  *reinterpret_cast<float4*>(oq) = make_float4(gq[0], gq[1], gq[2], gq[3]);
+  *reinterpret_cast<float4*>(oq + 4) = make_float4(gq[4], gq[5], gq[6], gq[7]);
+  *reinterpret_cast<float4*>(ok) = make_float4(gk[0], gk[1], gk[2], gk[3]);
+  *reinterpret_cast<float4*>(ok + 4) = make_float4(gk[4], gk[5], gk[6], gk[7]);
 }
 
 // Workspace of the chunked backward: the forward prep's regions (with Tb^T),
@@ -998,15 +1107,17 @@ hipError_t launch_chunk_bwd_chunked(const BwdArgs& a) {
     if (e != hipSuccess) return e;
   }
   if (slots > 0) {
-    hipLaunchKernelGGL(k_bwd_grad<BF16>, dim3(static_cast<unsigned>(slots * a.h_v)), dim3(256), 0, st, q, k, v,
+    hipLaunchKernelGGL(k_bwd_grad<BF16>, dim3(static_cast<unsigned>(slots * a.h_v)), dim3(512), 0, st, q, k, v,
                        a.q_stride, a.k_stride, a.v_stride, a.gate, a.scale, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.cu,
                        a.n_seq, a.t_total, a.d_o, a.dv, w.w.states, w.dstates, w.dqh, w.dkh, a.dg, a.dbeta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.t_total > 0) {
-    hipLaunchKernelGGL(k_bwd_dqk<BF16>, dim3(static_cast<unsigned>(a.t_total * a.h_qk)), dim3(128), 0, st, q, k,
-                       a.q_stride, a.k_stride, a.use_l2, a.l2_eps, a.h_qk, a.h_v, w.dqh, w.dkh, a.dq, a.dk);
+    const int64_t rows = a.t_total * a.h_qk;
+    hipLaunchKernelGGL(k_bwd_dqk, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, st, q, k,
+                       a.q_stride, a.k_stride, a.use_l2, a.l2_eps, a.h_qk, a.h_v, a.t_total, w.dqh, w.dkh, a.dq,
+                       a.dk);
     return hipGetLastError();
   }
   return hipSuccess;
