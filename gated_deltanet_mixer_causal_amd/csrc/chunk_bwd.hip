@@ -165,63 +165,90 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int
   const int ks0 = (16 * wave) / KS;       // first k-step of this tile's rows of P^T and Tb^T
   const int64_t vrow = static_cast<int64_t>(h_v) * D;
 
-  // operands of one chunk (registers), loaded one chunk ahead
+  // Operands of one chunk (registers).  Each set is reloaded for the next
+  // (earlier) chunk right after its last use in this one, so the loads are
+  // spread over the three phases and every load has about a chunk step of
+  // latency: K, Q, P^T and c3 after phase A, Tb^T and c1 after phase B, b_C
+  // and dO (two chunks ahead) in phase C.
   Frag kf[NKS_D], qf[NKS_D], ph[NKS_C], pl[NKS_C], th[NKS_C], tl[NKS_C];
-  float4 c1v, c3v, dov;
-  float bcv, c2t;
-  auto load_chunk = [&](int64_t jj, Frag* kf_, Frag* qf_, Frag* ph_, Frag* pl_, Frag* th_, Frag* tl_, float4& c1_,
-                        float4& c3_, float& bc_, float4& do_, float& c2_) {
-    const int64_t t0_ = start + jj * C;
-    const int len_ = static_cast<int>(end - t0_ < C ? end - t0_ : C);
+  float4 c1v, c3v;
+  float bcv;
+  auto unit_of = [&](int64_t jj) { return (slot0 + jj) * h_v + h; };
+  auto load_kqp = [&](int64_t jj) {
     const __bf16* kq_ = static_cast<const __bf16*>(ws.kq) + ((slot0 + jj) * h_qk + hq) * BW::kq_elems + lane * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS_D; ++ks) {
-      kf_[ks] = PB::ld(kq_ + BW::kq_block(0, wave, ks));
-      qf_[ks] = PB::ld(kq_ + BW::kq_block(1, wave, ks));
+      kf[ks] = PB::ld(kq_ + BW::kq_block(0, wave, ks));
+      qf[ks] = PB::ld(kq_ + BW::kq_block(1, wave, ks));
     }
-    const int64_t u_ = (slot0 + jj) * h_v + h;
-    const __bf16* p_ = static_cast<const __bf16*>(ws.p) + u_ * BW::op_elems + lane * 8;
-    const __bf16* t_ = static_cast<const __bf16*>(ws.tbt) + u_ * BW::op_elems + lane * 8;
+    const __bf16* p_ = static_cast<const __bf16*>(ws.p) + unit_of(jj) * BW::op_elems + lane * 8;
 #pragma unroll
     for (int ks = 0; ks < NKS_C; ++ks) {
       if (ks >= ks0) {
-        ph_[ks] = PB::ld(p_ + BW::op_block(wave, ks, 0));
-        pl_[ks] = PB::ld(p_ + BW::op_block(wave, ks, 1));
-        th_[ks] = PB::ld(t_ + BW::op_block(wave, ks, 0));
-        tl_[ks] = PB::ld(t_ + BW::op_block(wave, ks, 1));
+        ph[ks] = PB::ld(p_ + BW::op_block(wave, ks, 0));
+        pl[ks] = PB::ld(p_ + BW::op_block(wave, ks, 1));
       }
     }
-    const float* sc_ = ws.sc + u_ * (4 * C);
-    c1_ = *reinterpret_cast<const float4*>(sc_ + orow0);
-    c3_ = *reinterpret_cast<const float4*>(sc_ + 2 * C + orow0);
-    bc_ = sc_[3 * C];
-    // dO staging: token tid / 4, d_v columns 4 (tid % 4) .. + 3
-    const int tk = tid >> 2;
-    c2_ = sc_[C + tk];
-    do_ = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tk < len_) do_ = *reinterpret_cast<const float4*>(d_o + (t0_ + tk) * vrow + h * D + dv0 + 4 * (tid & 3));
+    c3v = *reinterpret_cast<const float4*>(ws.sc + unit_of(jj) * (4 * C) + 2 * C + orow0);
   };
-  auto stage_do = [&](int buf, float4 v4, float c2) {
-    const int tk = tid >> 2, c0 = 4 * (tid & 3);
-    const float v[4] = {v4.x, v4.y, v4.z, v4.w};
+  auto load_tbt = [&](int64_t jj) {
+    const __bf16* t_ = static_cast<const __bf16*>(ws.tbt) + unit_of(jj) * BW::op_elems + lane * 8;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = swz_off<LDT>(c0 + e, tk >> 3) + (tk & 7);
-      put_hl(sDO[buf], sDO[buf] + 16 * LDT, idx, v[e]);
-      put_hl(sDOc[buf], sDOc[buf] + 16 * LDT, idx, c2 * v[e]);
+    for (int ks = 0; ks < NKS_C; ++ks) {
+      if (ks >= ks0) {
+        th[ks] = PB::ld(t_ + BW::op_block(wave, ks, 0));
+        tl[ks] = PB::ld(t_ + BW::op_block(wave, ks, 1));
+      }
     }
+    c1v = *reinterpret_cast<const float4*>(ws.sc + unit_of(jj) * (4 * C) + orow0);
+  };
+  // dO of chunk jj for the staging, in the layout of the MFMA outputs: this
+  // lane's tokens orow0 .. orow0 + 3 at d_v column dv0 + r16 (one 8-byte LDS
+  // run per array), and c2 of those tokens; rows past the end re-read the
+  // last row and are zeroed at the staging
+  auto load_do = [&](int64_t jj, float4& do_, float4& c2_) {
+    const int64_t t0_ = start + jj * C;
+    const int len_ = static_cast<int>(end - t0_ < C ? end - t0_ : C);
+    c2_ = *reinterpret_cast<const float4*>(ws.sc + unit_of(jj) * (4 * C) + C + orow0);
+    float t4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = orow0 + i < len_ ? orow0 + i : len_ - 1;
+      t4[i] = d_o[(t0_ + r) * vrow + h * D + dv0 + r16];
+    }
+    do_ = make_float4(t4[0], t4[1], t4[2], t4[3]);
+  };
+  auto stage_do = [&](int buf, int64_t jj, float4 v4, float4 c2) {
+    const int64_t t0_ = start + jj * C;
+    const float v[4] = {v4.x, v4.y, v4.z, v4.w}, c[4] = {c2.x, c2.y, c2.z, c2.w};
+    float a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = t0_ + orow0 + i < end ? v[i] : 0.f;
+      b[i] = c[i] * a[i];
+    }
+    const int idx = swz_off<LDT>(r16, orow0 >> 3) + (orow0 & 7);
+    PB::put4(sDO[buf], sDO[buf] + 16 * LDT, idx, a);
+    PB::put4(sDOc[buf], sDOc[buf] + 16 * LDT, idx, b);
   };
 
   int buf = 0;
+  float4 don, c2n;   // dO of the next chunk down, loaded a chunk before its staging
   if (nchunks > 0) {
-    load_chunk(nchunks - 1, kf, qf, ph, pl, th, tl, c1v, c3v, bcv, dov, c2t);
-    stage_do(0, dov, c2t);
+    load_kqp(nchunks - 1);
+    load_tbt(nchunks - 1);
+    bcv = ws.sc[unit_of(nchunks - 1) * (4 * C) + 3 * C];
+    float4 d0, c0;
+    load_do(nchunks - 1, d0, c0);
+    stage_do(0, nchunks - 1, d0, c0);
+    load_do(nchunks > 1 ? nchunks - 2 : 0, don, c2n);
   }
   __syncthreads();
 
   for (int64_t j = nchunks - 1; j >= 0; --j) {
     const int64_t t0 = start + j * C;
     const int len = static_cast<int>(end - t0 < C ? end - t0 : C);
+    const int64_t jn = j > 0 ? j - 1 : j;   // the next chunk down (the last step reloads its own)
     // the gradient of the state leaving this chunk
     {
       float* o = dstates + (((slot0 + j) * h_v + h) * D + dv0 + r16) * D;
@@ -229,12 +256,6 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int
       for (int jj = 0; jj < 2; ++jj)
         *reinterpret_cast<float4*>(o + 16 * (wave + 4 * jj) + 4 * g4) = make_float4(G[jj][0], G[jj][1], G[jj][2], G[jj][3]);
     }
-    // next (earlier) chunk's operands, in flight during this one
-    const int64_t jn = j > 0 ? j - 1 : j;
-    Frag kfn[NKS_D], qfn[NKS_D], phn[NKS_C], pln[NKS_C], thn[NKS_C], tln[NKS_C];
-    float4 c1n, c3n, don;
-    float bcn, c2n;
-    load_chunk(jn, kfn, qfn, phn, pln, thn, tln, c1n, c3n, bcn, don, c2n);
 
     // ---- A: dU = P^T dO + diag(c3) K dS^T for token tile `wave` ----
     {
@@ -262,6 +283,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int
       PB::put4(sDU, sDU_lo, swz_off<LDT>(r16, orow0 >> 3) + (orow0 & 7), t4);
     }
     __syncthreads();
+    load_kqp(jn);   // K, Q, P^T and c3 of this chunk are consumed
 
     // ---- B: dX = Tb^T dU (= dV); -c1 dX for the state update ----
     {
@@ -283,6 +305,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int
       PB::put4(sDX, sDX_lo, swz_off<LDT>(r16, orow0 >> 3) + (orow0 & 7), t4);
     }
     __syncthreads();
+    load_tbt(jn);   // Tb^T and c1 of this chunk are consumed
 
     // ---- C: dS <- b_C dS + Q^T (c2 dO) - K^T (c1 dX) ----
     {
@@ -305,23 +328,10 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int
         const float t4[4] = {acc[0], acc[1], acc[2], acc[3]};
         PB::put4(sG, sG_lo, swz_off<LDK>(r16, (16 * mt + 4 * g4) >> 3) + ((4 * g4) & 7), t4);
       }
-      stage_do(buf ^ 1, don, c2n);
+      stage_do(buf ^ 1, jn, don, c2n);
+      bcv = ws.sc[unit_of(jn) * (4 * C) + 3 * C];
+      load_do(j > 1 ? j - 2 : 0, don, c2n);
     }
-#pragma unroll
-    for (int ks = 0; ks < NKS_D; ++ks) {
-      kf[ks] = kfn[ks];
-      qf[ks] = qfn[ks];
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS_C; ++ks) {
-      ph[ks] = phn[ks];
-      pl[ks] = pln[ks];
-      th[ks] = thn[ks];
-      tl[ks] = tln[ks];
-    }
-    c1v = c1n;
-    c3v = c3n;
-    bcv = bcn;
     buf ^= 1;
     __syncthreads();
   }
