@@ -705,7 +705,7 @@ def main():
         out["fused_gates"]["recurrent_step_vs_plain"] = round(dc["ms_rec_gated"] / dc["ms_rec"], 4)
     if pf["ms_bwd"] is not None:
         out["backward"] = {
-            "what": "gdn_chunk_bwd: dq, dk, dv, dg, dbeta, d_initial of the same 4096-token call (fp32)",
+            "what": "gdn_chunk_bwd: dq, dk, dv, dg, dbeta, d_initial of the same 4096-token call (fp32 outputs; the chunked matrix-core form for these bf16 inputs)",
             "ms_per_call": round(pf["ms_bwd"], 4),
             "tokens_per_s": round(T / (pf["ms_bwd"] * 1e-3), 1),
             "vs_forward_chunk_fwd": round(pf["ms_bwd"] / pf["ms_chunk"], 2),

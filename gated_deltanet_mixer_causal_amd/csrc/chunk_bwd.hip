@@ -543,32 +543,47 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
   //    or P (half 1).
   const float bC = s_red[0];
   {
-    const __bf16* aop = h0 ? sK : sQ;
+    auto gram = [&](const __bf16* aop, int tj) {
+      floatx4 gm = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      if (tj <= tile) {
-        floatx4 gm = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < D / 32; ++ks)
+        gm = mfma_bf16(frag_rows(aop, LDK, 16 * tile, 32 * ks), frag_rows(sK, LDK, 16 * tj, 32 * ks), gm);
+      return gm;
+    };
+    if (h0) {
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-          gm = mfma_bf16(frag_rows(aop, LDK, 16 * tile, 32 * ks), frag_rows(sK, LDK, 16 * tj, 32 * ks), gm);
-        const int j = 16 * tj + r16;
-        const double gj = s_gam[j];
-        const float rkj = s_rk[j];
+      for (int tj = 0; tj < 4; ++tj) {
+        if (tj <= tile) {
+          const floatx4 gm = gram(sK, tj);
+          const int j = 16 * tj + r16;
+          const double gj = s_gam[j];
+          const float rkj = s_rk[j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
-          const float dec = __expf(j <= i ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
-          if (h0) {
-            const float la = j < i ? s_rk[i] * rkj * gm[e] * dec : 0.f;
-            sL[i * LDC + j] = s_beta[i] * la;
-          } else {
-            const float pv = j <= i ? scale * dec * s_rq[i] * rkj * gm[e] : 0.f;
-            put_hl(sP, sP_lo, i * L64 + j, pv);
+          for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            const float dec = __expf(j < i ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
+            sL[i * LDC + j] = s_beta[i] * s_rk[i] * rkj * gm[e] * dec;
           }
         }
-      } else if (!h0) {
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) put_hl(sP, sP_lo, (i0 + e) * L64 + 16 * tj + r16, 0.f);
+      for (int tj = 0; tj < 4; ++tj) {
+        float pv[4] = {0.f, 0.f, 0.f, 0.f};
+        const int j = 16 * tj + r16;
+        if (tj <= tile) {
+          const floatx4 gm = gram(sQ, tj);
+          const double gj = s_gam[j];
+          const float rkj = s_rk[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            const float dec = __expf(j <= i ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
+            pv[e] = scale * dec * s_rq[i] * rkj * gm[e];
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put_hl(sP, sP_lo, (i0 + e) * L64 + j, pv[e]);
       }
     }
   }
@@ -708,44 +723,55 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
   //    half 0: dTb (masked) with T: dbeta's column terms and dT.
   {
     float rowa[4] = {0.f, 0.f, 0.f, 0.f}, cola[4] = {0.f, 0.f, 0.f, 0.f};
+    if (!h0) {
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      const int j = 16 * tj + r16;
-      if (tj <= tile) {
-        const double gj = s_gam[j];
-        const float rkj = s_rk[j], bj = s_beta[j];
-        float ca = 0.f;
+      for (int tj = 0; tj < 4; ++tj) {
+        const int j = 16 * tj + r16;
+        float ak[4] = {0.f, 0.f, 0.f, 0.f}, aqq[4] = {0.f, 0.f, 0.f, 0.f};
+        if (tj <= tile) {
+          const double gj = s_gam[j];
+          const float rkj = s_rk[j];
+          float ca = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
-          const bool on = j <= i;
-          const float x = on ? T4[tj][e] : 0.f;
-          if (!h0) {
+          for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            const bool on = j <= i;
+            const float x = on ? T4[tj][e] : 0.f;
             const float m1 = x * (static_cast<float>(sP[i * L64 + j]) + static_cast<float>(sP_lo[i * L64 + j]));
             rowa[e] += m1;
             ca += m1;
-            const float dec = __expf(on ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
-            const float aq = on ? scale * x * dec : 0.f;
-            put_hl(sAqk, sAqk_lo, i * L64 + j, aq * rkj);
-            put_hl(sAqq, sAqq_lo, i * L64 + j, s_rq[i] * aq);
-          } else {
-            const float tij = static_cast<float>(sT[i * L64 + j]) + static_cast<float>(sT_lo[i * L64 + j]);
-            ca += x * tij;
-            put_hl(sDT, sDT_lo, i * L64 + j, x * bj);
+            const float aq = scale * x * __expf(on ? static_cast<float>(s_gam[i] - gj) : -INFINITY);
+            ak[e] = aq * rkj;
+            aqq[e] = s_rq[i] * aq;
           }
+          cola[tj] = ca;
         }
-        cola[tj] = ca;
-      } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int idx = (i0 + e) * L64 + j;
-          if (!h0) {
-            put_hl(sAqk, sAqk_lo, idx, 0.f);
-            put_hl(sAqq, sAqq_lo, idx, 0.f);
-          } else {
-            put_hl(sDT, sDT_lo, idx, 0.f);
-          }
+          put_hl(sAqk, sAqk_lo, (i0 + e) * L64 + j, ak[e]);
+          put_hl(sAqq, sAqq_lo, (i0 + e) * L64 + j, aqq[e]);
         }
+      }
+    } else {
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        const int j = 16 * tj + r16;
+        float dt[4] = {0.f, 0.f, 0.f, 0.f};
+        if (tj <= tile) {
+          const float bj = s_beta[j];
+          float ca = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            const float x = j <= i ? T4[tj][e] : 0.f;
+            const float tij = static_cast<float>(sT[i * L64 + j]) + static_cast<float>(sT_lo[i * L64 + j]);
+            ca += x * tij;
+            dt[e] = x * bj;
+          }
+          cola[tj] = ca;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put_hl(sDT, sDT_lo, (i0 + e) * L64 + j, dt[e]);
       }
     }
 #pragma unroll
