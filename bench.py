@@ -53,11 +53,12 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # with these hashes (sha256, first 16 hex digits).  A kernel changed since the
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
+CHUNK_SOURCES = {"chunk.hip": "2b43fae7d023f74f", "chunk_impl.hpp": "22356f8569e384af",
+                 "common.hpp": "4e2cf7bb0de2ff2f", "launch.hpp": "1c8e7c7cfb0f4bb1"}
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (289_250_714, {"chunk.hip": "c8721f5ca44e879a", "common.hpp": "4e2cf7bb0de2ff2f",
-                                    "launch.hpp": "c3b849c7d316da8b"}),
-    "gdn_recurrent_step": (274_540_954, {"recurrent.hip": "feb115db1f28a22c", "common.hpp": "4e2cf7bb0de2ff2f",
-                                         "launch.hpp": "c3b849c7d316da8b"}),
+    "gdn_chunk_fwd": (289_265_179, CHUNK_SOURCES),
+    "gdn_recurrent_step": (274_540_367, {"recurrent.hip": "feb115db1f28a22c", "common.hpp": "4e2cf7bb0de2ff2f",
+                                         "launch.hpp": "1c8e7c7cfb0f4bb1"}),
 }
 
 
@@ -76,9 +77,7 @@ def measured_traffic(entry):
 # (512 FLOP per op) summed over the prep and scan kernels; hash-gated like the
 # traffic above.
 MEASURED_MFMA = {
-    "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512,
-                      {"chunk.hip": "c8721f5ca44e879a", "common.hpp": "4e2cf7bb0de2ff2f",
-                       "launch.hpp": "c3b849c7d316da8b"}),
+    "gdn_chunk_fwd": ((2_621_440 + 69_206_016) * 512, 524_288 * 512, CHUNK_SOURCES),
 }
 
 
