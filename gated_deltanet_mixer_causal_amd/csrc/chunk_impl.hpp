@@ -228,6 +228,33 @@ struct WsLayout {
   }
 };
 
+// Sum of squares of 8 values, in a fixed order of fused multiply-adds.
+__device__ __forceinline__ float sumsq8(const float* v) {
+  float s = v[0] * v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) s = __builtin_fmaf(v[i], v[i], s);
+  return s;
+}
+
+// Sum over each row of 16 lanes (every lane of the wave active), on the DPP
+// row rotations 8, 4, 2, 1.  The result equals group_sum<16> bit for bit:
+// after the step of offset m the partial sums repeat with period m in the
+// row, so lane i's rotated partner (i - m) mod 16 holds the same value as its
+// xor partner i ^ m, and each addition takes the same two operands in the
+// same order.  A rotation is a modifier on the add instead of an LDS
+// crossbar round trip.
+template <int M>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + M, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return v;
+}
+
 // N consecutive values from LDS, as 16-byte reads when they fill them
 template <int N, class T>
 __device__ __forceinline__ void lds_row(const T* p, T* out) {
@@ -260,7 +287,12 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sL, float* sT) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
   if (wave == 0 && lane < 16 * NT) {
-    const int b = lane >> 4, c = lane & 15, base = 16 * b;
+    int c = lane & 15;
+    // opaque per call: the kernels call this inside their unit loops, and the
+    // 16 selects (i == c) below would otherwise be hoisted into 16 registers
+    // held across every unit
+    asm volatile("" : "+v"(c));
+    const int b = lane >> 4, base = 16 * b;
     float tcol[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -304,7 +336,7 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sL, float* sT) {
 // blocks: block (mt, ks), lane l holds M^T[16 mt + l%16][ks*KSTEP + (l/16)*FE
 // + e] = M[ks*KSTEP + (l/16)*FE + e][16 mt + l%16] (zero above M's diagonal).
 template <class Pol, int D, int C, bool kBwd = false>
-__global__ __launch_bounds__(256) void k_chunk_prep(
+__global__ __launch_bounds__(256, 2) void k_chunk_prep(
     const typename Pol::In::T* __restrict__ q, const typename Pol::In::T* __restrict__ k,
     int64_t q_stride, int64_t k_stride, GateSrc gates, float scale, int use_l2, float l2_eps, int h_qk, int h_v,
     const int32_t* __restrict__ cu, int n_seq, int64_t t_total, const int32_t* __restrict__ seq_slots, ChunkWs ws,
@@ -395,11 +427,14 @@ __global__ __launch_bounds__(256) void k_chunk_prep(
           Pol::commit8(sK + row * LDK + c8, kr[it], row < len, kv);
           Pol::commit8(sQ + row * LDK + c8, qr[it], row < len, qv);
         }
-        float sk = 0.f, sq = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { sk += kv[i] * kv[i]; sq += qv[i] * qv[i]; }
-        sk = group_sum<TPR>(sk);
-        sq = group_sum<TPR>(sq);
+        float sk = sumsq8(kv), sq = sumsq8(qv);
+        if constexpr (TPR == 16) {
+          sk = row16_sum(sk);
+          sq = row16_sum(sq);
+        } else {
+          sk = group_sum<TPR>(sk);
+          sq = group_sum<TPR>(sq);
+        }
         if ((RPP <= C || row < C) && tid % TPR == 0) {
           const bool valid = row < len;
           s_rk[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f);

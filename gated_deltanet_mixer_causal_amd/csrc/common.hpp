@@ -109,7 +109,26 @@ struct F32 {
   }
 };
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU with the hardware reciprocal (1 ulp) in place of an IEEE divide: the
+// conv kernels, the norms and the fused prefill form it for every output, and
+// the divide's ten-instruction sequence dominated the fused prefill's conv.
+// Every kernel uses this one definition, so entry points that promise
+// bit-identical results stay so.
+__device__ __forceinline__ float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// One output of the width-4 causal conv with SiLU: taps w0..w3 against the
+// three previous raw inputs h0 (oldest) .. h2 and the current one x.  The
+// products are accumulated in this order with explicit fused multiply-adds,
+// so every kernel that forms a conv output (the conv kernels, the one-launch
+// decode mixer and the fused prefill) rounds it alike.
+__device__ __forceinline__ float conv4_silu(float w0, float w1, float w2, float w3, float h0, float h1, float h2,
+                                            float x) {
+  float acc = w0 * h0;
+  acc = __builtin_fmaf(w1, h1, acc);
+  acc = __builtin_fmaf(w2, h2, acc);
+  acc = __builtin_fmaf(w3, x, acc);
+  return silu(acc);
+}
 
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64).
 template <int width>

@@ -57,8 +57,7 @@ __device__ __forceinline__ void conv_out(const float (&wt)[4][8], const float (&
                                          const float (&w2)[8], const float (&cur)[8], float (&out)[8]) {
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const float acc = wt[0][c] * w0[c] + wt[1][c] * w1[c] + wt[2][c] * w2[c] + wt[3][c] * cur[c];
-    out[c] = silu(acc);
+    out[c] = conv4_silu(wt[0][c], wt[1][c], wt[2][c], wt[3][c], w0[c], w1[c], w2[c], cur[c]);
   }
 }
 
@@ -137,8 +136,7 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
         const float cur = E::cvt(raw[3 + u][c]);
-        const float acc = wt[0][c] * h0[c] + wt[1][c] * h1[c] + wt[2][c] * h2[c] + wt[3][c] * cur;
-        o[c] = to_elem(silu(acc), T{});
+        o[c] = to_elem(conv4_silu(wt[0][c], wt[1][c], wt[2][c], wt[3][c], h0[c], h1[c], h2[c], cur), T{});
         h0[c] = h1[c];
         h1[c] = h2[c];
         h2[c] = cur;

@@ -37,13 +37,6 @@ __device__ __forceinline__ void md_stream_store4(float* p, float4 v) {
   __builtin_nontemporal_store(md_f4{v.x, v.y, v.z, v.w}, reinterpret_cast<md_f4*>(p));
 }
 
-// conv output of one channel from its history h0 (oldest) .. h2 and the token
-// x, with the taps of that channel; the expression is the unfused conv's
-__device__ __forceinline__ float md_conv(float w0, float w1, float w2, float w3, float h0, float h1, float h2,
-                                         float x) {
-  const float acc = w0 * h0 + w1 * h1 + w2 * h2 + w3 * x;
-  return silu(acc);
-}
 
 template <class E, class EO, int D, int NT, int GMAX, int PAR>
 __global__ __launch_bounds__(NT * PAR) void k_mixer_decode(
@@ -93,7 +86,7 @@ __global__ __launch_bounds__(NT * PAR) void k_mixer_decode(
     const float h0 = E::load(hp, 0), h1 = E::load(hp, ld), h2 = E::load(hp, 2 * ld);
     const typename E::T xraw = x[static_cast<int64_t>(r) * ld + c];
     const float xc = E::cvt(xraw);
-    const float y = md_conv(E::load(w, 4 * static_cast<int64_t>(c)), E::load(w, 4 * static_cast<int64_t>(c) + 1),
+    const float y = conv4_silu(E::load(w, 4 * static_cast<int64_t>(c)), E::load(w, 4 * static_cast<int64_t>(c) + 1),
                             E::load(w, 4 * static_cast<int64_t>(c) + 2), E::load(w, 4 * static_cast<int64_t>(c) + 3),
                             h0, h1, h2, xc);
     // the unfused path stores the conv output in the input dtype
