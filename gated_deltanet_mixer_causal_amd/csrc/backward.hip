@@ -621,20 +621,34 @@ __global__ __launch_bounds__(kCbThreads) void k_conv_bwd_dx(
 #pragma unroll
       for (int i = 0; i < 4; ++i) wt[i][c] = tmp[4 * c + i];
   }
+  // Every load below is unconditional, from a clamped row, and rows outside
+  // the sequence are zeroed after their load: loads under a branch made the
+  // compiler wait for each at the join, one memory round trip per row.
   // padded rows u0 .. u0 + kCbBT + 5 (zeros past the sequence)
   float pr[kCbBT + 6][8];
 #pragma unroll
   for (int r = 0; r < kCbBT + 6; ++r) {
     const int64_t j = u0 + r;   // padded index
+    const int64_t jx = j - 3 < L ? (j - 3 < 0 ? 0 : j - 3) : L - 1;   // a row of x_s (L >= 1 here)
+    const typename E::T* src =
+        (j < 3 && hist) ? hist + (static_cast<int64_t>(seq) * 3 + j) * ld + c0 : x + (start + jx) * ld + c0;
+    E::load8(src, pr[r]);
+  }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) pr[r][c] = 0.f;
-    if (j < 3) {
-      if (hist) E::load8(hist + (static_cast<int64_t>(seq) * 3 + j) * ld + c0, pr[r]);
-    } else if (j - 3 < L) {
-      E::load8(x + (start + j - 3) * ld + c0, pr[r]);
-    }
+  for (int r = 0; r < kCbBT + 6; ++r) {
+    const int64_t j = u0 + r;
+    const bool valid = j < 3 ? hist != nullptr : j - 3 < L;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) pr[r][c] = valid ? pr[r][c] : 0.f;
   }
   // dpre for tokens u0 .. u0 + kCbBT + 2 (zero outside [0, L))
+  float4 gy[kCbBT + 3][2];
+#pragma unroll
+  for (int r = 0; r < kCbBT + 3; ++r) {
+    const int64_t t = u0 + r < L ? u0 + r : L - 1;
+    gy[r][0] = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0);
+    gy[r][1] = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0 + 4);
+  }
   float dp[kCbBT + 3][8];
   float dwa[4][8] = {};
 #pragma unroll
@@ -644,8 +658,7 @@ __global__ __launch_bounds__(kCbThreads) void k_conv_bwd_dx(
     for (int c = 0; c < 8; ++c) dp[r][c] = 0.f;
     if (t < L) {
       float g[8];
-      const float4 a4 = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0);
-      const float4 b4 = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0 + 4);
+      const float4 a4 = gy[r][0], b4 = gy[r][1];
       g[0] = a4.x; g[1] = a4.y; g[2] = a4.z; g[3] = a4.w; g[4] = b4.x; g[5] = b4.y; g[6] = b4.z; g[7] = b4.w;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {

@@ -236,25 +236,6 @@ __device__ __forceinline__ float sumsq8(const float* v) {
   return s;
 }
 
-// Sum over each row of 16 lanes (every lane of the wave active), on the DPP
-// row rotations 8, 4, 2, 1.  The result equals group_sum<16> bit for bit:
-// after the step of offset m the partial sums repeat with period m in the
-// row, so lane i's rotated partner (i - m) mod 16 holds the same value as its
-// xor partner i ^ m, and each addition takes the same two operands in the
-// same order.  A rotation is a modifier on the add instead of an LDS
-// crossbar round trip.
-template <int M>
-__device__ __forceinline__ float row_ror(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + M, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += row_ror<8>(v);
-  v += row_ror<4>(v);
-  v += row_ror<2>(v);
-  v += row_ror<1>(v);
-  return v;
-}
-
 // N consecutive values from LDS, as 16-byte reads when they fill them
 template <int N, class T>
 __device__ __forceinline__ void lds_row(const T* p, T* out) {
@@ -428,13 +409,8 @@ __global__ __launch_bounds__(256, 2) void k_chunk_prep(
           Pol::commit8(sQ + row * LDK + c8, qr[it], row < len, qv);
         }
         float sk = sumsq8(kv), sq = sumsq8(qv);
-        if constexpr (TPR == 16) {
-          sk = row16_sum(sk);
-          sq = row16_sum(sq);
-        } else {
-          sk = group_sum<TPR>(sk);
-          sq = group_sum<TPR>(sq);
-        }
+        sk = group_sum<TPR>(sk);
+        sq = group_sum<TPR>(sq);
         if ((RPP <= C || row < C) && tid % TPR == 0) {
           const bool valid = row < len;
           s_rk[row] = !valid ? 0.f : (use_l2 ? 1.0f / sqrtf(sk + l2_eps) : 1.0f);

@@ -130,12 +130,33 @@ __device__ __forceinline__ float conv4_silu(float w0, float w1, float w2, float 
   return silu(acc);
 }
 
-// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+// DPP row rotation: lane i of each row of 16 lanes reads lane (i - M) mod 16.
+template <int M>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + M, 0xf, 0xf, false));
+}
+
+// Sum over groups of `width` consecutive lanes (width a power of two <= 64),
+// every lane of each group active: the xor butterfly v += v[lane ^ m] for
+// m = width/2 .. 1.  For width 16 (the rows of 16 lanes of the d = 128
+// kernels) it runs on DPP row rotations by m instead of LDS crossbar
+// shuffles, with the same result bit for bit: after the step of offset m the
+// partial sums repeat with period m in the row, so the rotated partner
+// (i - m) mod 16 holds the value of the xor partner i ^ m, and each addition
+// takes the same two operands in the same order.
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (width == 16) {
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    v += row_ror<1>(v);
+    return v;
+  } else {
 #pragma unroll
-  for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
-  return v;
+    for (int off = width / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, width);
+    return v;
+  }
 }
 
 // ---- arithmetic of one recurrent token --------------------------------------

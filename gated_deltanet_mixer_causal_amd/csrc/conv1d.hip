@@ -101,16 +101,23 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
   // (history rows in the first block; zeros for a fresh sequence, whose
   // history is not read) and the block's own rows (rows past the block's end
   // re-read its last row and are not used)
+  // All 11 loads are unconditional (the source of a row before the block is
+  // a pointer select) and a fresh sequence's history rows are zeroed after
+  // their load: a load under a branch made the compiler wait for it at the
+  // join, which serialised the three rows before the block and the block's
+  // own rows into four memory round trips per workgroup.
   typename R::V raw[3 + kConvBT];
   const bool zero_hist = p0 < 3 && fresh != nullptr && fresh[seq] != 0;
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
     const int64_t lp = p0 - 3 + r;
-    if (lp < 0 && zero_hist) raw[r] = R::zero();
-    else raw[r] = R::ld(lp >= 0 ? x + (start + lp) * ld + c0 : hist + (3 + lp) * ld);
+    raw[r] = R::ld(lp >= 0 ? x + (start + lp) * ld + c0 : hist + (3 + lp) * ld);
   }
 #pragma unroll
   for (int u = 0; u < kConvBT; ++u) raw[3 + u] = R::ld(x + (t0 + (u < len ? u : len - 1)) * ld + c0);
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+    if (p0 - 3 + r < 0 && zero_hist) raw[r] = R::zero();
   float wt[4][NV];
   {
     // taps of the thread's channels: w[c][0..3], channel-major
@@ -141,6 +148,9 @@ __global__ __launch_bounds__(kConvThreads) void k_conv1d_prefill(
         h1[c] = h2[c];
         h2[c] = cur;
       }
+      // plain stores: the chunk kernels read y right after, from cache
+      // (non-temporal stores made this kernel 1.2 us faster and the scan,
+      // which reads v from y a step ahead, 5 us slower)
       R::st(y + (t0 + u) * ld + c0, o);
     }
   }
