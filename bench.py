@@ -53,7 +53,7 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # with these hashes (sha256, first 16 hex digits).  A kernel changed since the
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
-CHUNK_SOURCES = {"chunk.hip": "2b43fae7d023f74f", "chunk_impl.hpp": "f3f7a2d2d0da033e",
+CHUNK_SOURCES = {"chunk.hip": "2b43fae7d023f74f", "chunk_impl.hpp": "00117838d6369ddb",
                  "common.hpp": "48a2a30823c83686", "launch.hpp": "1c8e7c7cfb0f4bb1"}
 MEASURED_TRAFFIC = {
     "gdn_chunk_fwd": (289_238_644, CHUNK_SOURCES),

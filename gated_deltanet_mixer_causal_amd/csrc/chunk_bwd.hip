@@ -26,11 +26,12 @@
 //
 // Launches (after the forward prep, written in its backward mode with P^T and
 // Tb^T fragments, and the forward scan writing the state entering every chunk):
-//   k_bwd_dstate  one workgroup per (sequence, v-head, 16-wide d_v slice),
-//                 chunks last to first, the slice of dS in fp32 registers:
-//                 writes dS leaving each chunk, dV and dS_initial.  Three
-//                 products per chunk with a barrier after each, like the
-//                 forward scan.
+//   dstate_body   the reverse scan, run as the prefix of that forward scan
+//                 in the same launch: one workgroup per (sequence, v-head,
+//                 16-wide d_v slice), chunks last to first, the slice of dS
+//                 in fp32 registers: writes dS leaving each chunk, dV and
+//                 dS_initial.  Three products per chunk with a barrier after
+//                 each, like the forward scan.
 //   k_bwd_grad    one workgroup per (chunk, v-head): recomputes the chunk's
 //                 Gram tiles, L, P and T, streams S, dS, dO over four 32-wide
 //                 d_v parts to form X, U, dU and the sums over d_v (dO S,
@@ -108,28 +109,40 @@ __device__ __forceinline__ float sum_groups(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_dstate: the gradient of the state, chunks last to first
+// dstate_body: the gradient of the state, chunks last to first.  It runs in
+// one launch with the forward scan that writes the state entering every
+// chunk (k_bwd_scans below): the two read only the prep's workspace and
+// write disjoint buffers.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int32_t* __restrict__ cu, int n_seq,
-                                                    int64_t t_total, const float* __restrict__ d_o,
-                                                    const float* __restrict__ d_final, float* __restrict__ dv,
-                                                    float* __restrict__ d_init, float* __restrict__ dstates,
-                                                    ChunkWs ws) {
+// LDS (bf16 elements): dS rows (d_v) hi | lo; dO rows, double-buffered; c2 dO,
+// double-buffered; dU rows; -c1 dX rows; the chunk's K rows; its Q rows.
+struct DstateLds {
+  static constexpr int LDT = BC, LDK = BD, LDKT = BD + 8;
+  static constexpr int G = 0, DO = G + 2 * 16 * LDK, DOC = DO + 2 * 2 * 16 * LDT, DU = DOC + 2 * 2 * 16 * LDT,
+                       DX = DU + 2 * 16 * LDT, KT = DX + 2 * 16 * LDT, QT = KT + BC * LDKT, end = QT + BC * LDKT;
+  static constexpr size_t bytes = sizeof(__bf16) * end;
+};
+
+__device__ __forceinline__ void dstate_body(int64_t bidx, char* lds, int h_qk, int h_v,
+                                            const int32_t* __restrict__ cu, int n_seq, int64_t t_total,
+                                            const float* __restrict__ d_o, const float* __restrict__ d_final,
+                                            float* __restrict__ dv, float* __restrict__ d_init,
+                                            float* __restrict__ dstates, ChunkWs ws) {
   constexpr int D = BD, C = BC, KS = 32, NKS_D = D / KS, NKS_C = C / KS, NTILE = D / 16;
-  constexpr int LDT = C, LDK = D, LDKT = D + 8;
-  __shared__ __attribute__((aligned(16))) __bf16 sG[2 * 16 * LDK];         // dS rows (d_v), hi | lo
-  __shared__ __attribute__((aligned(16))) __bf16 sDO[2][2 * 16 * LDT];     // dO rows (d_v), double-buffered
-  __shared__ __attribute__((aligned(16))) __bf16 sDOc[2][2 * 16 * LDT];    // c2 dO
-  __shared__ __attribute__((aligned(16))) __bf16 sDU[2 * 16 * LDT];        // dU rows (d_v)
-  __shared__ __attribute__((aligned(16))) __bf16 sDX[2 * 16 * LDT];        // -c1 dX rows (d_v)
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[C * LDKT];            // the chunk's K rows
-  __shared__ __attribute__((aligned(16))) __bf16 sQt[C * LDKT];            // the chunk's Q rows
+  constexpr int LDT = DstateLds::LDT, LDK = DstateLds::LDK, LDKT = DstateLds::LDKT;
+  __bf16* const base = reinterpret_cast<__bf16*>(lds);
+  __bf16* const sG = base + DstateLds::G;
+  __bf16(*const sDO)[2 * 16 * LDT] = reinterpret_cast<__bf16(*)[2 * 16 * LDT]>(base + DstateLds::DO);
+  __bf16(*const sDOc)[2 * 16 * LDT] = reinterpret_cast<__bf16(*)[2 * 16 * LDT]>(base + DstateLds::DOC);
+  __bf16* const sDU = base + DstateLds::DU;
+  __bf16* const sDX = base + DstateLds::DX;
+  __bf16* const sKt = base + DstateLds::KT;
+  __bf16* const sQt = base + DstateLds::QT;
   __bf16* const sG_lo = sG + 16 * LDK;
   __bf16* const sDU_lo = sDU + 16 * LDT;
   __bf16* const sDX_lo = sDX + 16 * LDT;
 
   const int64_t per_seq = static_cast<int64_t>(h_v) * NTILE;
-  const int64_t bidx = blockIdx.x;
   const int64_t rank = bidx / per_seq;
   if (rank >= n_seq) return;
   const int s = ws.order ? ws.order[rank] : static_cast<int>(rank);
@@ -343,6 +356,26 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(int h_qk, int h_v, const int
           make_float4(G[jj][0], G[jj][1], G[jj][2], G[jj][3]);
   }
 }
+
+// The reverse scan as the prefix of the forward scan that writes the state
+// entering every chunk (k_chunk_scan's Pre argument): blocks [0, nblk) run
+// it, and the forward scan takes the blocks after them.  The two read only
+// the prep's workspace and write disjoint buffers; the reverse scan, the
+// longer chain, takes the first blocks.  nblk is a multiple of 8, so both
+// halves keep their XCD-aware block mapping.
+struct DstatePrefix {
+  static constexpr size_t kLdsBytes = DstateLds::bytes;
+  int64_t nblk;
+  const float* d_o;
+  const float* d_final;
+  float* dv;
+  float* d_init;
+  float* dstates;
+  __device__ __forceinline__ void run(int64_t b, char* lds, int h_qk, int h_v, const int32_t* cu, int n_seq,
+                                      int64_t t_total, const ChunkWs& ws) const {
+    dstate_body(b, lds, h_qk, h_v, cu, n_seq, t_total, d_o, d_final, dv, d_init, dstates, ws);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // k_bwd_grad: one workgroup of 8 waves per (chunk slot, v-head)
@@ -1132,14 +1165,11 @@ hipError_t launch_chunk_bwd_chunked(const BwdArgs& a) {
   }
   const int64_t nblk = static_cast<int64_t>(a.n_seq) * a.h_v * (BD / 16);
   if (nblk > 0) {
-    hipLaunchKernelGGL((k_chunk_scan<PB, F32, BD, BC, 1, true>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
-                       q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total, a.init,
-                       nullptr, nullptr, nullptr, static_cast<float*>(nullptr), w.w);
+    hipLaunchKernelGGL((k_chunk_scan<PB, F32, BD, BC, 1, true, DstatePrefix>), dim3(static_cast<unsigned>(2 * nblk)),
+                       dim3(256), 0, st, q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq,
+                       a.t_total, a.init, nullptr, nullptr, nullptr, static_cast<float*>(nullptr), w.w,
+                       DstatePrefix{nblk, a.d_o, a.d_final, a.dv, a.d_init, w.dstates});
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwd_dstate, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st, a.h_qk, a.h_v, a.cu,
-                       a.n_seq, a.t_total, a.d_o, a.d_final, a.dv, a.d_init, w.dstates, w.w);
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (slots > 0) {
