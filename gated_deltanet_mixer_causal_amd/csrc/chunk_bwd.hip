@@ -536,16 +536,17 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
   struct PartIn {
     float4 s[2], ds[2], o;
   };
-  auto fetch_vv = [&](int p, float* vv) {   // V at this lane's X tile elements (half 0)
-    if (h0) {
+  // V at this lane's X tile elements (used by half 0), kept as raw bits and
+  // converted where it is used: loaded under a branch, or converted on
+  // arrival, it made the wave wait for the load right there
+  auto fetch_vv = [&](int p, uint32_t* vv) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e < len ? i0 + e : len - 1;
-          vv[4 * nt + e] = In::load(v, (t0 + i) * v_stride + (int64_t)h * D + 32 * p + 16 * nt + r16);
-        }
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e < len ? i0 + e : len - 1;
+        vv[4 * nt + e] = to_u32(v[(t0 + i) * v_stride + (int64_t)h * D + 32 * p + 16 * nt + r16]);
+      }
   };
   auto fetch_xv = [&](int p, float* xv) {   // dV as this lane's A operand values
     const int xrow = 16 * tile + r16 < len ? 16 * tile + r16 : len - 1;
@@ -625,13 +626,24 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
   // 3. T = (I + L)^-1 (fp32), then T as hi|lo rows (zero above the diagonal)
   unit_lower_inverse<C, LDC>(sL, sTf);
   // after the solve, whose forward substitution holds many registers
-  float vv[8], xv[8];
+  uint32_t vv[8];
+  float xv[8];
   fetch_part(0, nxt);
   fetch_vv(0, vv);
   fetch_xv(0, xv);
-  for (int f = tid; f < C * C; f += NTH) {
-    const int i = f / C, j = f % C;
-    put_hl(sT, sT_lo, i * L64 + j, j <= i ? sTf[i * LDC + j] : 0.f);
+  {
+    // eight consecutive columns per thread: two 16-byte reads, 16-byte stores
+    static_assert(C * C == 8 * NTH, "one pass of eight columns per thread");
+    const int i = tid >> 3, j0 = (tid & 7) * 8;
+    const float4 t0 = *reinterpret_cast<const float4*>(sTf + i * LDC + j0);
+    const float4 t1 = *reinterpret_cast<const float4*>(sTf + i * LDC + j0 + 4);
+    float tv[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tv[e] = j0 + e <= i ? tv[e] : 0.f;   // T above the diagonal is not written
+    Frag th, tl;
+    split8(tv, th, tl);
+    *reinterpret_cast<Frag*>(sT + i * L64 + j0) = th;
+    *reinterpret_cast<Frag*>(sT_lo + i * L64 + j0) = tl;
   }
   __syncthreads();
 
@@ -647,6 +659,9 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
   float sds = 0.f;   // this thread's part of <dS, S>
 #pragma unroll 1
   for (int p = 0; p < 4; ++p) {
+    // the part whose inputs are fetched during this one (the last part
+    // re-reads its own: a load under a branch is waited for at the join)
+    const int pn = p < 3 ? p + 1 : 3;
     // a. stage S and dS rows 32p .. 32p + 31 (d_v) and dO columns 32p .. from
     //    the registers fetched a part ahead, then fetch the next part
     {
@@ -661,7 +676,7 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
       const int tk = tid >> 3, c4 = (tid & 7) * 4;
       put4_hl(sDO, sDO_lo, tk * L32 + c4, tk < len ? nxt.o : make_float4(0.f, 0.f, 0.f, 0.f));
     }
-    if (p < 3) fetch_part(p + 1, nxt);
+    fetch_part(pn, nxt);
     __syncthreads();
     // b. half 0: X = V - diag(b rk) K S^T (and beta X); half 1: K dS^T
     floatx4 kds[2];
@@ -682,13 +697,13 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = i0 + e;
-          const float x = (i < len ? vv[4 * nt + e] : 0.f) - s_b[i] * s_rk[i] * acc[e];
+          const float x = (i < len ? from_u32<In>(vv[4 * nt + e]) : 0.f) - s_b[i] * s_rk[i] * acc[e];
           put_hl(sX, sX_lo, i * L32 + c, x);
           put_hl(sXb, sXb_lo, i * L32 + c, s_beta[i] * x);
         }
       }
     }
-    if (p < 3) fetch_vv(p + 1, vv);
+    fetch_vv(pn, vv);
     __syncthreads();
     // c. half 0: U = T (beta X); half 1: dU = P^T dO + diag(d rk) K dS^T
 #pragma unroll
@@ -729,7 +744,7 @@ __global__ __launch_bounds__(512) void k_bwd_grad(
         for (int e = 0; e < 8; ++e) xm[e] = 16 * tile + r16 < len ? xv[e] : 0.f;
         split8(xm, axh, axl);
       }
-      if (p < 3) fetch_xv(p + 1, xv);
+      fetch_xv(pn, xv);
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int c0 = 16 * (nb + n);
