@@ -579,17 +579,23 @@ __global__ __launch_bounds__(NT) void k_bwd_reduce(
 //     dw[i]  = sum over all sequences and t of dpre[t] p[t + i]
 // The rounding of y to the input dtype is not differentiated.
 // ---------------------------------------------------------------------------
-constexpr int kCbBT = 8;            // tokens per block
+constexpr int kCbBT = 32;           // tokens per strip
 constexpr int kCbThreads = 256;     // 8 channels per thread
+constexpr int kCbPF = 4;            // rows fetched ahead
 
 __device__ __forceinline__ float silu_grad(float x) {
   const float s = 1.0f / (1.0f + __expf(-x));
   return s * (1.0f + x * (1.0f - s));
 }
 
-// Block (kCbBT tokens of one sequence, kCbThreads * 8 channels): dx of its
+// Strip (kCbBT tokens of one sequence, kCbThreads * 8 channels): dx of its
 // rows and its share of dw (the products of its own rows), written as one
-// partial per block.  Empty block slots write zero partials.
+// partial per strip.  Empty strip slots write zero partials.  Each thread
+// walks its 8 channels down the strip with a window of four input rows and
+// four dpre values, so a strip reads its kCbBT rows of x plus 6 and of dy plus
+// 3.  The rows of x and dy come kCbPF steps ahead into a ring of raw registers
+// (unconditional loads from clamped rows, converted and zeroed at use: a load
+// under a branch, or converted on arrival, is waited for right there).
 template <class E>
 __global__ __launch_bounds__(kCbThreads) void k_conv_bwd_dx(
     const typename E::T* __restrict__ x, const typename E::T* __restrict__ w, int channels,
@@ -610,7 +616,7 @@ __global__ __launch_bounds__(kCbThreads) void k_conv_bwd_dx(
     return;
   }
   const int64_t start = seq_start(cu, seq, t_total), L = seq_start(cu, seq + 1, t_total) - start;
-  const int64_t u0 = t0 - start;   // local index of the block's first token
+  const int64_t u0 = t0 - start;   // local index of the strip's first token
   float wt[4][8];
   {
     float tmp[32];
@@ -621,86 +627,114 @@ __global__ __launch_bounds__(kCbThreads) void k_conv_bwd_dx(
 #pragma unroll
       for (int i = 0; i < 4; ++i) wt[i][c] = tmp[4 * c + i];
   }
-  // Every load below is unconditional, from a clamped row, and rows outside
-  // the sequence are zeroed after their load: loads under a branch made the
-  // compiler wait for each at the join, one memory round trip per row.
-  // padded rows u0 .. u0 + kCbBT + 5 (zeros past the sequence)
-  float pr[kCbBT + 6][8];
-#pragma unroll
-  for (int r = 0; r < kCbBT + 6; ++r) {
-    const int64_t j = u0 + r;   // padded index
+  // raw row of the padded input p at padded index j (history rows for j < 3
+  // with a history, else a clamped row of x_s), and whether it is nonzero
+  auto p_src = [&](int64_t j) -> const typename E::T* {
     const int64_t jx = j - 3 < L ? (j - 3 < 0 ? 0 : j - 3) : L - 1;   // a row of x_s (L >= 1 here)
-    const typename E::T* src =
-        (j < 3 && hist) ? hist + (static_cast<int64_t>(seq) * 3 + j) * ld + c0 : x + (start + jx) * ld + c0;
-    E::load8(src, pr[r]);
-  }
-#pragma unroll
-  for (int r = 0; r < kCbBT + 6; ++r) {
-    const int64_t j = u0 + r;
-    const bool valid = j < 3 ? hist != nullptr : j - 3 < L;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) pr[r][c] = valid ? pr[r][c] : 0.f;
-  }
-  // dpre for tokens u0 .. u0 + kCbBT + 2 (zero outside [0, L))
-  float4 gy[kCbBT + 3][2];
-#pragma unroll
-  for (int r = 0; r < kCbBT + 3; ++r) {
-    const int64_t t = u0 + r < L ? u0 + r : L - 1;
-    gy[r][0] = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0);
-    gy[r][1] = *reinterpret_cast<const float4*>(dy + (start + t) * ld + c0 + 4);
-  }
-  float dp[kCbBT + 3][8];
+    return (j < 3 && hist) ? hist + (static_cast<int64_t>(seq) * 3 + j) * ld + c0 : x + (start + jx) * ld + c0;
+  };
+  auto p_valid = [&](int64_t j) { return j < 3 ? hist != nullptr : j - 3 < L; };
+  auto dy_src = [&](int64_t t) { return dy + (start + (t < L ? t : L - 1)) * ld + c0; };
+
+  // window: padded rows u + 0 .. u + 3 of the dpre token u being formed (the
+  // first three enter before the walk), and dpre of the four tokens before it
+  float pw[4][8], dw4[4][8];
   float dwa[4][8] = {};
 #pragma unroll
-  for (int r = 0; r < kCbBT + 3; ++r) {
-    const int64_t t = u0 + r;
+  for (int r = 0; r < 3; ++r) {
+    const int64_t j = u0 + r;
+    E::unpack8(E::ld_vec(p_src(j)), pw[r + 1]);
+    const bool ok = p_valid(j);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) dp[r][c] = 0.f;
-    if (t < L) {
-      float g[8];
-      const float4 a4 = gy[r][0], b4 = gy[r][1];
-      g[0] = a4.x; g[1] = a4.y; g[2] = a4.z; g[3] = a4.w; g[4] = b4.x; g[5] = b4.y; g[6] = b4.z; g[7] = b4.w;
+    for (int c = 0; c < 8; ++c) pw[r + 1][c] = ok ? pw[r + 1][c] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dw4[k][c] = 0.f;
+  // ring of rows fetched ahead: step r needs padded row u0 + r + 3 and dy of token u0 + r
+  typename E::Vec pring[kCbPF];
+  float4 gring[kCbPF][2];
+#pragma unroll
+  for (int k = 0; k < kCbPF; ++k) {
+    pring[k] = E::ld_vec(p_src(u0 + k + 3));
+    const float* g = dy_src(u0 + k);
+    gring[k][0] = reinterpret_cast<const float4*>(g)[0];
+    gring[k][1] = reinterpret_cast<const float4*>(g)[1];
+  }
+  // steps r = 0 .. kCbBT + 3: dpre of token u0 + r, and dx of token u0 + r - 3
+  // (tokens from u0 + 3 on need dpre up to u0 + kCbBT + 2)
+  constexpr int kSteps = kCbBT + 4;
+  static_assert(kSteps % kCbPF == 0, "whole ring turns");
+#pragma unroll 1
+  for (int r0 = 0; r0 < kSteps; r0 += kCbPF) {
+#pragma unroll
+    for (int k = 0; k < kCbPF; ++k) {
+      const int r = r0 + k;
+      const int64_t t = u0 + r;
+      // shift in padded row t + 3
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pw[i][c] = pw[i + 1][c];
+      {
+        float nr[8];
+        E::unpack8(pring[k], nr);
+        const bool ok = p_valid(t + 3);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) pw[3][c] = ok ? nr[c] : 0.f;
+      }
+      const float4 ga = gring[k][0], gb = gring[k][1];
+      // fetch the step kCbPF ahead into this slot (past the walk: a clamped re-read)
+      {
+        const int64_t tn = t + kCbPF;
+        pring[k] = E::ld_vec(p_src(tn + 3));
+        const float* g = dy_src(tn);
+        gring[k][0] = reinterpret_cast<const float4*>(g)[0];
+        gring[k][1] = reinterpret_cast<const float4*>(g)[1];
+      }
+      // dpre of token t (zero outside [0, L)), shifted into the dpre window
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dw4[i][c] = dw4[i + 1][c];
+      const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float pre = wt[0][c] * pr[r][c] + wt[1][c] * pr[r + 1][c] + wt[2][c] * pr[r + 2][c] +
-                          wt[3][c] * pr[r + 3][c];
-        dp[r][c] = g[c] * silu_grad(pre);
+        const float pre = wt[0][c] * pw[0][c] + wt[1][c] * pw[1][c] + wt[2][c] * pw[2][c] + wt[3][c] * pw[3][c];
+        dw4[3][c] = t < L ? g[c] * silu_grad(pre) : 0.f;
       }
-      if (r < kCbBT) {   // the block's own tokens contribute to dw
+      if (r < len) {   // the strip's own tokens contribute to dw
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int c = 0; c < 8; ++c) dwa[i][c] += dp[r][c] * pr[r + i][c];
+          for (int c = 0; c < 8; ++c) dwa[i][c] += dw4[3][c] * pw[i][c];
+      }
+      // dx[u] = dp_pad[u + 3] = sum_i w[i] dpre[u + 3 - i] (+ d_hist_out[u + 3 - L]), u = t - 3
+      if (r >= 3 && r - 3 < len) {
+        const int64_t u = t - 3;
+        float o[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          o[c] = wt[3][c] * dw4[0][c] + wt[2][c] * dw4[1][c] + wt[1][c] * dw4[2][c] + wt[0][c] * dw4[3][c];
+        const int64_t jo = u + 3 - L;
+        if (dhist_out && jo >= 0 && jo < 3) {
+          const float* src = dhist_out + (static_cast<int64_t>(seq) * 3 + jo) * ld + c0;
+          const float4 a4 = *reinterpret_cast<const float4*>(src);
+          const float4 b4 = *reinterpret_cast<const float4*>(src + 4);
+          const float e[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+          for (int c = 0; c < 8; ++c) o[c] += e[c];
+        }
+        float* dst = dx + (start + u) * ld + c0;
+        *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
       }
     }
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     *reinterpret_cast<float4*>(part + 4 * c) = make_float4(dwa[0][c], dwa[1][c], dwa[2][c], dwa[3][c]);
-  // dx[u] = dp_pad[u + 3] = sum_i w[i] dpre[u + 3 - i] (+ d_hist_out[u + 3 - L])
-#pragma unroll
-  for (int r = 0; r < kCbBT; ++r) {
-    if (r < len) {
-      const int64_t u = u0 + r;
-      float o[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        o[c] = wt[3][c] * dp[r][c] + wt[2][c] * dp[r + 1][c] + wt[1][c] * dp[r + 2][c] + wt[0][c] * dp[r + 3][c];
-      const int64_t jo = u + 3 - L;
-      if (dhist_out && jo >= 0 && jo < 3) {
-        float e[8];
-        const float* src = dhist_out + (static_cast<int64_t>(seq) * 3 + jo) * ld + c0;
-        const float4 a4 = *reinterpret_cast<const float4*>(src);
-        const float4 b4 = *reinterpret_cast<const float4*>(src + 4);
-        e[0] = a4.x; e[1] = a4.y; e[2] = a4.z; e[3] = a4.w; e[4] = b4.x; e[5] = b4.y; e[6] = b4.z; e[7] = b4.w;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] += e[c];
-      }
-      float* dst = dx + (start + u) * ld + c0;
-      *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    }
-  }
 }
 
 // d_hist_in of each sequence: dp_pad[j] for j < 3, one thread per (sequence,

@@ -195,7 +195,7 @@ def test_conv1d_bwd_validation(lib):
     assert call(dx=_addr(3)) == L.GDN_ERR_ALIAS                 # dx over dy
     out = ctypes.c_size_t(0)
     assert lib.gdn_conv1d_bwd_workspace_size(8192, 1, 4096, ctypes.byref(out)) == 0
-    assert out.value == (4096 // 8 + 1) * 8192 * 4 * 4
+    assert out.value == (4096 // 32 + 1) * 8192 * 4 * 4   # one dw partial per 32-token strip
 
 
 def test_chunk_workspace_size(lib):
