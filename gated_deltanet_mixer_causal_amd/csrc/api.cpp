@@ -276,7 +276,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, int64_t q
                           float* final_state, void* o, gdn_dtype o_dt, const void* z, const float* norm_w,
                           float norm_eps, void* workspace, size_t ws_bytes, void* stream,
                           const int32_t* state_slots = nullptr, const int32_t* fresh = nullptr,
-                          int32_t n_slots = 0) {
+                          int32_t n_slots = 0, bool side_ok = true) {
   // With state_slots (the mixed prefill + decode form) initial_state and
   // final_state are the same state pool of n_slots rows, read and written at
   // the slot of each sequence.
@@ -330,6 +330,7 @@ gdn_status chunk_fwd_impl(const void* q, const void* k, const void* v, int64_t q
   a.slots = state_slots; a.fresh = fresh;
   a.o = o; a.o_dt = o_dt; a.z = z; a.norm_w = norm_w; a.norm_eps = norm_eps;
   a.workspace = workspace; a.stream = stream;
+  a.side_ok = side_ok;
   return finish(gdn::launch_chunk_fwd(a));
 }
 
@@ -405,9 +406,11 @@ gdn_status gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, in
   if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
   void* ws = device_scratch();
   if (!ws) return GDN_ERR_HIP;
+  // no side stream: this entry creates nothing
   return chunk_fwd_impl(q, k, v, q_stride, k_stride, v_stride, dt, plain_gates(g, beta), scale, use_qk_l2norm,
                         l2_eps, h_qk, h_v, d_k, d_v, chunk, cu_seqlens, n_seq, t_total, initial_state,
-                        final_state, o, o_dt, z, norm_w, norm_eps, ws, GDN_NOALLOC_SCRATCH_BYTES, stream);
+                        final_state, o, o_dt, z, norm_w, norm_eps, ws, GDN_NOALLOC_SCRATCH_BYTES, stream,
+                        nullptr, nullptr, 0, false);
 }
 
 gdn_status gdn_chunk_fwd_gated(const void* q, const void* k, const void* v, int64_t q_stride, int64_t k_stride,

@@ -53,6 +53,8 @@
 // product uses hi*hi + hi*lo + lo*hi (or hi*raw + lo*raw), accumulated in fp32
 // (the multi-term bf16 technique of Henry, Tang and Heinecke, ARITH 2019).
 // Policy PolF32 uses the fp32 matrix-core instruction for fp32 inputs.
+#include <mutex>
+
 #include "chunk_impl.hpp"
 
 namespace gdn {
@@ -211,13 +213,12 @@ hipError_t launch_seq_order(const int32_t* cu, int n_seq, int chunk, int32_t* or
 }
 
 template <class In, int D>
-static hipError_t single_token_for(const ChunkArgs& a, float* o_pre) {
+static hipError_t single_token_for(const ChunkArgs& a, float* o_pre, hipStream_t st) {
   using T = typename In::T;
   constexpr int NT1 = D == 128 ? 256 : 64, SPL = D == 128 ? 4 : 1;
   const T* q = static_cast<const T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   const T* v = static_cast<const T*>(a.v);
-  hipStream_t st = static_cast<hipStream_t>(a.stream);
   const int64_t nb1 = static_cast<int64_t>(a.n_seq) * a.h_v * SPL;
   if (a.z)
     hipLaunchKernelGGL((k_single_token<In, F32, D, NT1, SPL>), dim3(static_cast<unsigned>(nb1)), dim3(NT1), 0, st,
@@ -235,11 +236,69 @@ static hipError_t single_token_for(const ChunkArgs& a, float* o_pre) {
   return hipGetLastError();
 }
 
-hipError_t launch_single_token(const ChunkArgs& a, float* o_pre) {
-  if (a.dt == GDN_BF16) return single_token_for<BF16, 128>(a, o_pre);
-  if (a.d == 128) return single_token_for<F32, 128>(a, o_pre);
-  return single_token_for<F32, 16>(a, o_pre);
+hipError_t launch_single_token(const ChunkArgs& a, float* o_pre, hipStream_t st) {
+  if (a.dt == GDN_BF16) return single_token_for<BF16, 128>(a, o_pre, st);
+  if (a.d == 128) return single_token_for<F32, 128>(a, o_pre, st);
+  return single_token_for<F32, 16>(a, o_pre, st);
 }
+
+// A second stream per device for the one-token sequences of a call, which
+// then run beside the scan instead of after it (they read no prep output and
+// write other sequences' rows and states).  Created on first use with the
+// default priority and held until the process ends; the fork and the join
+// are events, so a captured call captures both branches.  Calls from several
+// host threads on one device share it (each fork, launch and join record is
+// made under a lock, and a join waits at least for its own launch).
+namespace {
+struct SideStream {
+  hipStream_t st = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// Launches one-token work on the side stream after everything already on st;
+// *forked tells whether st must wait for it (side_join).  Falls back to st
+// itself while st is being captured (a capture must not pull a stream that
+// other threads use into the graph) or where no side stream can be had.
+hipError_t side_fork(const ChunkArgs& a, float* o_pre, hipStream_t st, bool* forked) {
+  *forked = false;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  int dev = 0;
+  if (!a.side_ok || hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone ||
+      hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices)
+    return launch_single_token(a, o_pre, st);
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& sd = g_side[dev];
+  hipError_t e = hipSuccess;
+  if (!sd.st) {
+    hipStream_t s2 = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    if ((e = hipStreamCreateWithFlags(&s2, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&f, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&j, hipEventDisableTiming)) != hipSuccess) return e;
+    sd.st = s2;
+    sd.fork = f;
+    sd.join = j;
+  }
+  if ((e = hipEventRecord(sd.fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(sd.st, sd.fork, 0)) != hipSuccess) return e;
+  if ((e = launch_single_token(a, o_pre, sd.st)) != hipSuccess) return e;
+  if ((e = hipEventRecord(sd.join, sd.st)) != hipSuccess) return e;
+  *forked = true;
+  return hipSuccess;
+}
+
+// st waits for the side stream's work so far (at least the last fork's launch).
+hipError_t side_join(hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  return hipStreamWaitEvent(st, g_side[dev].join, 0);
+}
+}  // namespace
 
 template <class Pol, int D, int C>
 static hipError_t run_chunk(const ChunkArgs& a) {
@@ -278,8 +337,9 @@ static hipError_t run_chunk(const ChunkArgs& a) {
   // One-token sequences: skipped only when a single sequence holds all of
   // several tokens (cu_seqlens ends at t_total, so it has no one-token
   // sequence); in a mixed call t_total is a capacity.
+  bool forked = false;
   if (a.n_seq > 1 || a.t_total == 1 || a.slots != nullptr) {
-    hipError_t e = launch_single_token(a, o_pre);
+    hipError_t e = side_fork(a, o_pre, st, &forked);
     if (e != hipSuccess) return e;
   }
   // One 16-wide d_v tile per workgroup: a single long sequence has only
@@ -294,6 +354,7 @@ static hipError_t run_chunk(const ChunkArgs& a) {
                        a.init, a.fin, a.slots, a.fresh, o_pre, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (forked && (e = side_join(st)) != hipSuccess) return e;
     if (a.t_total > 0)
       return launch_gated_rmsnorm(o_pre, GDN_F32, a.z, a.dt, a.norm_w, a.norm_eps, a.t_total * a.h_v, D,
                                   a.o, a.o_dt, a.stream, a.slots ? a.cu : nullptr, a.n_seq, a.slots, a.h_v);
@@ -307,7 +368,9 @@ static hipError_t run_chunk(const ChunkArgs& a) {
     hipLaunchKernelGGL((k_chunk_scan<Pol, F32, D, C, NV>), dim3(static_cast<unsigned>(nblk)), dim3(256), 0, st,
                        q, k, v, a.q_stride, a.k_stride, a.v_stride, a.h_qk, a.h_v, a.cu, a.n_seq, a.t_total,
                        a.init, a.fin, a.slots, a.fresh, static_cast<float*>(a.o), ws);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return forked ? side_join(st) : hipSuccess;
 }
 
 hipError_t launch_chunk_fwd(const ChunkArgs& a) {

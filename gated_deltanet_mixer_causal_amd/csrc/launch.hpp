@@ -34,6 +34,7 @@ struct ChunkArgs {
   float norm_eps;
   void* workspace;
   void* stream;
+  bool side_ok = true;   // the one-token sequences may run on the library's side stream (not for the no-alloc entry)
 };
 
 struct StepArgs {
@@ -128,7 +129,7 @@ size_t chunk_ws_bytes(gdn_dtype dt, int h_qk, int h_v, int d, int chunk, int n_s
 // Pieces of the chunk path (csrc/chunk.hip).
 hipError_t launch_seq_order(const int32_t* cu, int n_seq, int chunk, int32_t* order, hipStream_t st);
 // The one-token sequences of a call (outputs to o_pre when a.z is set, else to a.o).
-hipError_t launch_single_token(const ChunkArgs& a, float* o_pre);
+hipError_t launch_single_token(const ChunkArgs& a, float* o_pre, hipStream_t st);
 hipError_t launch_chunk_fwd(const ChunkArgs& a);
 size_t bwd_ws_bytes(int h_v, int d, int n_seq, int64_t t_total);
 hipError_t launch_chunk_bwd(const BwdArgs& a);

@@ -34,9 +34,14 @@
  *   - The library is thread-safe across streams.  Its host-side state is a
  *     thread-local last HIP error and caches filled on first use: the compute
  *     unit count of each device, the resident workgroups per compute unit of
- *     one kernel, and the device address of the scratch array of
+ *     one kernel, the device address of the scratch array of
  *     gdn_chunk_fwd_noalloc on each device (which that entry point, and only
- *     it, shares between calls).
+ *     it, shares between calls), and one side stream with two events per
+ *     device, on which the chunk entry points run the one-token sequences of
+ *     a multi-sequence or pooled call beside the scan (forked from and joined
+ *     back into the caller's stream before the call's last kernel; not while
+ *     the caller's stream is being captured, and never for
+ *     gdn_chunk_fwd_noalloc).  They are held until the process ends.
  *
  * Layouts (row-major, last index fastest)
  *   conv input/output x, y   [t_total, channels], channels ordered q | k | v
