@@ -53,12 +53,12 @@ FLOP_PER_TOKEN_HEAD = 139_648  # chunked gated delta rule, C=64, d=128 (algorith
 # with these hashes (sha256, first 16 hex digits).  A kernel changed since the
 # counters were taken reports null.
 CSRC = os.path.join(ROOT, "gated_deltanet_mixer_causal_amd", "csrc")
-CHUNK_SOURCES = {"chunk.hip": "2b43fae7d023f74f", "chunk_impl.hpp": "00117838d6369ddb",
-                 "common.hpp": "48a2a30823c83686", "launch.hpp": "1c8e7c7cfb0f4bb1"}
+CHUNK_SOURCES = {"chunk.hip": "34a28395d94d9929", "chunk_impl.hpp": "00117838d6369ddb",
+                 "common.hpp": "48a2a30823c83686", "launch.hpp": "3c7351067da3f401"}
 MEASURED_TRAFFIC = {
-    "gdn_chunk_fwd": (289_238_644, CHUNK_SOURCES),
-    "gdn_recurrent_step": (274_532_843, {"recurrent.hip": "feb115db1f28a22c", "common.hpp": "48a2a30823c83686",
-                                         "launch.hpp": "1c8e7c7cfb0f4bb1"}),
+    "gdn_chunk_fwd": (289_238_630, CHUNK_SOURCES),
+    "gdn_recurrent_step": (274_533_171, {"recurrent.hip": "feb115db1f28a22c", "common.hpp": "48a2a30823c83686",
+                                         "launch.hpp": "3c7351067da3f401"}),
 }
 
 
